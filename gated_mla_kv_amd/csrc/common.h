@@ -1,0 +1,107 @@
+// Device helpers shared by the gfx950 kernels: vector types, bf16 conversion, MFMA wrappers,
+// the LDS transpose read, wave reductions, and the compile-time layer shapes.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gmla {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#define GMLA_LDS __attribute__((address_space(3)))
+
+// ---------------------------------------------------------------------------------------
+// bf16 <-> f32. Rounding is to nearest, ties to even (no NaN inputs on this path).
+// ---------------------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+  return __uint_as_float(((uint32_t)b) << 16);
+}
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+// two floats -> packed bf16 pair (lo in bits 0..15)
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
+}
+__device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// ---------------------------------------------------------------------------------------
+// MFMA (CDNA4 bf16, fp32 accumulate). Lane layouts (checked on the hardware):
+//   32x32x16: A lane l holds row l%32, k = 8*(l/32)+i; B lane l holds col l%32, same k;
+//             C lane l holds col l%32, rows (j/4)*8 + (l/32)*4 + j%4, j = 0..15.
+//   16x16x32: A lane l holds row l%16, k = 8*(l/16)+i; B col l%16, same k;
+//             C lane l holds col l%16, rows 4*(l/16) + j, j = 0..3.
+// ---------------------------------------------------------------------------------------
+__device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------------------------------
+// LDS transpose read (ds_read_b64_tr_b16). Within each group of 16 lanes, with chunk_j the
+// four 16-bit values at lane j's address, lane i receives
+//   out[r] = chunk_{(i>>2) + 4r}[i & 3],  r = 0..3.
+// To read an MFMA operand whose k index runs down the rows of a row-major [k][n] LDS tile
+// (lane needs column n, four consecutive k), lane j of the group points at
+//   &tile[k0 + (j>>2)][n0 + 4*(j&3)]
+// and lane i then holds tile[k0 + r][n0 + i] for r = 0..3.
+// ---------------------------------------------------------------------------------------
+__device__ __forceinline__ u32x2 lds_read_tr16(const void* p) {
+  i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((GMLA_LDS i16x4*)(p));
+  return __builtin_bit_cast(u32x2, v);
+}
+
+// ---------------------------------------------------------------------------------------
+// Loads / stores
+// ---------------------------------------------------------------------------------------
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *(const u32x4*)p; }
+__device__ __forceinline__ void st16(void* p, u32x4 v) { *(u32x4*)p = v; }
+__device__ __forceinline__ u32x4 zero16() { return u32x4{0u, 0u, 0u, 0u}; }
+
+// ---------------------------------------------------------------------------------------
+// Wave reductions (wave64)
+// ---------------------------------------------------------------------------------------
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + __expf(-x)); }
+
+// ---------------------------------------------------------------------------------------
+// Compile-time layer shapes (the dims a kernel is instantiated for)
+// ---------------------------------------------------------------------------------------
+struct ShapeK3 {
+  static constexpr int H = 96, DN = 128, DS = 64, DV = 128, L = 512, QL = 1536, HID = 7168;
+  static constexpr int NIH = 32, DI = 128;
+};
+struct ShapeTiny {
+  static constexpr int H = 4, DN = 16, DS = 8, DV = 16, L = 32, QL = 64, HID = 256;
+  static constexpr int NIH = 0, DI = 0;
+};
+
+__host__ __device__ constexpr int cdiv(int a, int b) { return (a + b - 1) / b; }
+__host__ __device__ constexpr int round_up(int a, int b) { return cdiv(a, b) * b; }
+
+}  // namespace gmla

@@ -1,0 +1,377 @@
+// Decode attention in the latent space (absorbed MLA) and its sparse (Gated DSA) variant.
+//
+// With latent absorption (K3.1 Gated DSA blog, the note after eq. (10)) the score of head h
+// against cached position j is q~_h . [c_j ; r_j] * scale, where q~_h = [W^K_h^T q_nope_h ;
+// q_shared_h], and the head output is recovered as z_h = W^V_h sum_j p_j c_j. Each cached
+// position is read once, as one 576-value latent row, for all 96 heads at once: 1,152 bytes
+// instead of the expanded cache's 61,440 (KV cache card: 30,720 values per position).
+//
+// decode_attn_kernel: one workgroup per (sequence, split of the positions), 4 waves.
+// * The latent rows of a 32-position tile are staged in LDS (double-buffered, via registers,
+//   16-byte loads, each HBM byte read once).
+// * Waves 0..HP/32-1 each own 32 heads: their q~ rows sit in VGPRs as the B operand of
+//   S^T = Lat Q~^T (v_mfma_f32_32x32x16_bf16, k over the 576 latent features), so lane l holds
+//   head l%32; max/sum need one xor-32 shuffle. P^T (bf16) and the rescale factors go to LDS.
+// * All four waves then accumulate O^T = Lat^T P^T for a quarter of the 512 latent output
+//   features, taking Lat^T straight from the row-major tile with ds_read_b64_tr_b16.
+// * Each split writes unnormalised O and (max, sum) per head; decode_merge combines splits.
+// GATHER (sparse DSA): positions come from the selected list instead of a contiguous range.
+#include "common.h"
+#include "kernels.h"
+
+namespace gmla {
+
+template <class S>
+struct DecodeCfg {
+  static constexpr int H = S::H, L = S::L, DS = S::DS, DL = S::L + S::DS;
+  static constexpr int HP = round_up(H, 32);     // heads padded to 32-wide MFMA blocks
+  static constexpr int DLP = round_up(DL, 32);   // score k dimension, padded
+  static constexpr int LP = round_up(L, 32);     // output features, padded
+  static constexpr int NSW = HP / 32;            // waves that compute scores
+  static constexpr int KSD = DLP / 16;           // score k-steps
+  static constexpr int NDT = LP / 32;            // 32-wide output feature tiles
+  static constexpr int DTW = cdiv(NDT, 4);       // feature tiles per wave
+  static constexpr int BT = 32;                  // positions per tile
+  static constexpr int LROW = DLP + 8;           // LDS row stride of the latent tile (bf16)
+  static constexpr int PROW = BT + 8;            // LDS row stride of P^T [head][pos]
+  static constexpr int CH = DLP / 8;             // 16-byte chunks per padded row
+  static constexpr int NCH = cdiv(BT * CH, 256); // chunks per thread per tile
+  static_assert(NSW <= 4, "at most four score waves");
+};
+
+__device__ __forceinline__ int perm_row_d(int m) {
+  const int a = m >> 3, g = (m >> 2) & 1, b = m & 3;
+  return 16 * (a >> 1) + 8 * g + 4 * (a & 1) + b;
+}
+
+template <class S, bool GATHER>
+__global__ __launch_bounds__(256) void decode_attn_kernel(DecodeAttnArgs a) {
+  using C = DecodeCfg<S>;
+  __shared__ __attribute__((aligned(16))) uint16_t Ls[2][C::BT * C::LROW];
+  __shared__ __attribute__((aligned(16))) uint16_t Ps[C::HP * C::PROW];
+  __shared__ float alpha_s[C::HP];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g2 = lane >> 5, l32 = lane & 31;
+  const int b = blockIdx.x / a.n_splits, split = blockIdx.x % a.n_splits;
+  const int n_vis = GATHER ? min(a.sel_cnt[b], a.sel_stride) : min(a.n_vis[b] + a.vis_offset, a.T_cap);
+  const int p0 = split * a.chunk;
+  const int p1 = min(p0 + a.chunk, n_vis);
+  const int n_pos = max(p1 - p0, 0);
+  const int n_tiles = cdiv(n_pos, C::BT);
+  const uint16_t* lat = a.latent + (size_t)b * a.T_cap * C::DL;
+  const int32_t* sel = GATHER ? a.sel_idx + (size_t)b * a.sel_stride : nullptr;
+
+  // ---- score waves: q~ for heads wave*32 + l32 ----
+  const bool is_sw = wave < C::NSW;
+  const int head = wave * 32 + l32;
+  u32x4 qf[C::KSD];
+  if (is_sw) {
+    const uint16_t* qrow = a.q_tilde + ((size_t)b * C::H + head) * C::DL;
+#pragma unroll
+    for (int s = 0; s < C::KSD; ++s) {
+      const int d = s * 16 + g2 * 8;
+      qf[s] = (head < C::H && d < C::DL) ? ld16(qrow + d) : zero16();
+    }
+  }
+
+  u32x4 rl[C::NCH];
+  auto load_tile = [&](int t) {
+    const int j0 = p0 + t * C::BT;
+#pragma unroll
+    for (int i = 0; i < C::NCH; ++i) {
+      const int c = tid + 256 * i;
+      const int row = c / C::CH, col = (c % C::CH) * 8;
+      const int j = j0 + row;
+      bool ok = c < C::BT * C::CH && j < p1 && col < C::DL;
+      int pos = j;
+      if (GATHER && ok) {
+        pos = sel[j];
+        ok = pos >= 0 && pos < a.T_cap;
+      }
+      rl[i] = ok ? ld16(lat + (size_t)pos * C::DL + col) : zero16();
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < C::NCH; ++i) {
+      const int c = tid + 256 * i;
+      if (c < C::BT * C::CH) st16(&Ls[buf][(c / C::CH) * C::LROW + (c % C::CH) * 8], rl[i]);
+    }
+  };
+
+  const float sl2 = a.scale * 1.4426950408889634f;
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x16 o[C::DTW][C::NSW];
+#pragma unroll
+  for (int i = 0; i < C::DTW; ++i)
+#pragma unroll
+    for (int j = 0; j < C::NSW; ++j) o[i][j] = f32x16{};
+
+  const int krow_a = perm_row_d(l32);
+  if (n_tiles > 0) {
+    load_tile(0);
+    store_tile(0);
+  }
+  __syncthreads();
+  for (int t = 0; t < n_tiles; ++t) {
+    const int cur = t & 1;
+    const int j0 = p0 + t * C::BT;
+    if (t + 1 < n_tiles) load_tile(t + 1);
+    if (is_sw) {
+      // S^T [32 positions x 32 heads]
+      f32x16 sacc = f32x16{};
+      const uint16_t* lr = &Ls[cur][krow_a * C::LROW + g2 * 8];
+#pragma unroll
+      for (int s = 0; s < C::KSD; ++s) sacc = mfma32(ld16(lr + s * 16), qf[s], sacc);
+      float mt = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int j = j0 + 16 * (r >> 3) + 8 * g2 + (r & 7);
+        const float x = (j < p1) ? sacc[r] * sl2 : -INFINITY;
+        sacc[r] = x;
+        mt = fmaxf(mt, x);
+      }
+      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+      const float m_new = fmaxf(m_run, mt);
+      const float alpha = fast_exp2(m_run - m_new);
+      m_run = m_new;
+      float ls = 0.f;
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        float p[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          p[i] = fast_exp2(sacc[hh * 8 + i] - m_new);
+          ls += p[i];
+        }
+        st16(&Ps[head * C::PROW + hh * 16 + g2 * 8],
+             u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
+                   pack_bf16x2(p[6], p[7])});
+      }
+      l_run = l_run * alpha + ls;
+      if (g2 == 0) alpha_s[head] = alpha;
+    }
+    __syncthreads();
+    // ---- O^T [features x heads] += Lat^T P^T for this wave's feature tiles ----
+    {
+      const int G = lane >> 4, jj = lane & 15;
+      float al[C::NSW];
+#pragma unroll
+      for (int hs = 0; hs < C::NSW; ++hs) al[hs] = alpha_s[hs * 32 + l32];
+      u32x4 pb[C::NSW][2];
+#pragma unroll
+      for (int hs = 0; hs < C::NSW; ++hs)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) pb[hs][ks] = ld16(&Ps[(hs * 32 + l32) * C::PROW + ks * 16 + g2 * 8]);
+#pragma unroll
+      for (int dt = 0; dt < C::DTW; ++dt) {
+        const int ft = wave + 4 * dt;  // feature tile
+        if (ft >= C::NDT) break;
+#pragma unroll
+        for (int hs = 0; hs < C::NSW; ++hs)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[dt][hs][r] *= al[hs];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const uint16_t* lp =
+              &Ls[cur][(ks * 16 + 8 * (G >> 1) + (jj >> 2)) * C::LROW + ft * 32 + 16 * (G & 1) + 4 * (jj & 3)];
+          const u32x2 lo = lds_read_tr16(lp);
+          const u32x2 hi = lds_read_tr16(lp + 4 * C::LROW);
+          const u32x4 af = u32x4{lo.x, lo.y, hi.x, hi.y};
+#pragma unroll
+          for (int hs = 0; hs < C::NSW; ++hs) o[dt][hs] = mfma32(af, pb[hs][ks], o[dt][hs]);
+        }
+      }
+    }
+    if (t + 1 < n_tiles) store_tile(cur ^ 1);
+    __syncthreads();
+  }
+
+  // ---- write this split's partial results ----
+  const size_t part = (size_t)b * a.n_splits + split;
+  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  if (is_sw && head < C::H && g2 == 0) {
+    a.part_ml[(part * C::H + head) * 2 + 0] = m_run;  // base-2 scaled logits
+    a.part_ml[(part * C::H + head) * 2 + 1] = l_tot;
+  }
+#pragma unroll
+  for (int dt = 0; dt < C::DTW; ++dt) {
+    const int ft = wave + 4 * dt;
+    if (ft >= C::NDT) break;
+#pragma unroll
+    for (int hs = 0; hs < C::NSW; ++hs) {
+      const int hd = hs * 32 + l32;
+      if (hd >= C::H) continue;
+      float* dst = a.part_o + (part * C::H + hd) * C::L;
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) {
+        const int f = ft * 32 + rb * 8 + g2 * 4;
+        if (f < C::L)
+          *(f32x4*)(dst + f) = f32x4{o[dt][hs][rb * 4 + 0], o[dt][hs][rb * 4 + 1],
+                                     o[dt][hs][rb * 4 + 2], o[dt][hs][rb * 4 + 3]};
+      }
+    }
+  }
+}
+
+// Combine the splits of one (sequence, head): o = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.
+template <class S>
+__global__ __launch_bounds__(256) void decode_merge_kernel(DecodeAttnArgs a) {
+  using C = DecodeCfg<S>;
+  const int bh = blockIdx.x;
+  const int b = bh / C::H, h = bh % C::H;
+  const int ns = a.n_splits;
+  const size_t base = (size_t)b * ns;
+  float M = -INFINITY;
+  for (int s = 0; s < ns; ++s) M = fmaxf(M, a.part_ml[((base + s) * C::H + h) * 2]);
+  float den = 0.f;
+  for (int s = 0; s < ns; ++s) {
+    const float m = a.part_ml[((base + s) * C::H + h) * 2];
+    if (m != -INFINITY) den += fast_exp2(m - M) * a.part_ml[((base + s) * C::H + h) * 2 + 1];
+  }
+  const float inv = den > 0.f ? 1.0f / den : 0.f;  // no visible position: zeros
+  for (int f = threadIdx.x; f < C::L; f += blockDim.x) {
+    float acc = 0.f;
+    for (int s = 0; s < ns; ++s) {
+      const float m = a.part_ml[((base + s) * C::H + h) * 2];
+      if (m != -INFINITY) acc += fast_exp2(m - M) * a.part_o[((base + s) * C::H + h) * C::L + f];
+    }
+    a.o_latent[((size_t)b * C::H + h) * C::L + f] = acc * inv;
+  }
+  if (threadIdx.x == 0 && a.lse) a.lse[(size_t)b * C::H + h] = (M + __log2f(den)) * 0.6931471805599453f;
+}
+
+// q~[b,h,:L] = W^K_h^T q_nope[b,h], q~[b,h,L:] = q_shared[b,h]  (fp32 accumulate, bf16 out).
+// One workgroup per head; thread t owns latent features t, t+256, ...; tokens in chunks of 8.
+template <class S>
+__global__ __launch_bounds__(256) void absorb_q_kernel(const uint16_t* __restrict__ q, int ldq,
+                                                       const uint16_t* __restrict__ wkvb, int B,
+                                                       uint16_t* __restrict__ qt) {
+  constexpr int H = S::H, DN = S::DN, DS = S::DS, DV = S::DV, L = S::L, DQK = DN + DS;
+  constexpr int BC = 8;
+  __shared__ float qn[BC][DN];
+  const int h = blockIdx.x;
+  const uint16_t* wk = wkvb + (size_t)h * (DN + DV) * L;
+  for (int b0 = 0; b0 < B; b0 += BC) {
+    __syncthreads();
+    for (int i = threadIdx.x; i < BC * DN; i += blockDim.x) {
+      const int bb = i / DN, e = i % DN;
+      qn[bb][e] = (b0 + bb < B) ? bf16_bits_to_f32(q[(size_t)(b0 + bb) * ldq + h * DQK + e]) : 0.f;
+    }
+    __syncthreads();
+    for (int c = threadIdx.x; c < L; c += blockDim.x) {
+      float acc[BC];
+#pragma unroll
+      for (int bb = 0; bb < BC; ++bb) acc[bb] = 0.f;
+      for (int i = 0; i < DN; ++i) {
+        const float w = bf16_bits_to_f32(wk[(size_t)i * L + c]);
+#pragma unroll
+        for (int bb = 0; bb < BC; ++bb) acc[bb] += qn[bb][i] * w;
+      }
+#pragma unroll
+      for (int bb = 0; bb < BC; ++bb)
+        if (b0 + bb < B) qt[((size_t)(b0 + bb) * H + h) * (L + DS) + c] = f32_to_bf16_bits(acc[bb]);
+    }
+    for (int i = threadIdx.x; i < BC * DS; i += blockDim.x) {
+      const int bb = i / DS, e = i % DS;
+      if (b0 + bb < B)
+        qt[((size_t)(b0 + bb) * H + h) * (L + DS) + L + e] = q[(size_t)(b0 + bb) * ldq + h * DQK + DN + e];
+    }
+  }
+}
+
+// u[b, h*DV + d] = (W^V_h o[b,h])[d] * sigmoid(g_pre[b, h*DV + d])  (fp32 throughout).
+// One workgroup per head; thread t takes value row d = t % DV and the latent slice t / DV.
+template <class S>
+__global__ __launch_bounds__(256) void vup_gate_kernel(const float* __restrict__ o,
+                                                       const uint16_t* __restrict__ wkvb,
+                                                       const uint16_t* __restrict__ g_pre, int B,
+                                                       void* __restrict__ u, int u_f32) {
+  constexpr int H = S::H, DN = S::DN, DV = S::DV, L = S::L;
+  constexpr int PARTS = (256 / DV) < (L / 8) ? (256 / DV) : (L / 8);  // latent slices of >= 8
+  constexpr int SL = L / PARTS;
+  constexpr int BC = 8;
+  static_assert(L % PARTS == 0, "slice");
+  __shared__ float os[BC][L];
+  __shared__ float red[PARTS][BC][DV];
+  const int h = blockIdx.x;
+  const int d = threadIdx.x % DV, part = threadIdx.x / DV;
+  const uint16_t* wrow = wkvb + ((size_t)h * (DN + DV) + DN + d) * L + part * SL;
+  for (int b0 = 0; b0 < B; b0 += BC) {
+    __syncthreads();
+    for (int i = threadIdx.x; i < BC * L; i += blockDim.x) {
+      const int bb = i / L, c = i % L;
+      os[bb][c] = (b0 + bb < B) ? o[((size_t)(b0 + bb) * H + h) * L + c] : 0.f;
+    }
+    __syncthreads();
+    float acc[BC];
+#pragma unroll
+    for (int bb = 0; bb < BC; ++bb) acc[bb] = 0.f;
+    for (int c = 0; c < (part < PARTS ? SL : 0); c += 8) {
+      const u32x4 w = ld16(wrow + c);
+      const float wf[8] = {lo_bf16(w.x), hi_bf16(w.x), lo_bf16(w.y), hi_bf16(w.y),
+                           lo_bf16(w.z), hi_bf16(w.z), lo_bf16(w.w), hi_bf16(w.w)};
+#pragma unroll
+      for (int bb = 0; bb < BC; ++bb)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[bb] += wf[e] * os[bb][part * SL + c + e];
+    }
+    if (part < PARTS) {
+#pragma unroll
+      for (int bb = 0; bb < BC; ++bb) red[part][bb][d] = acc[bb];
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < BC * DV; i += blockDim.x) {
+      const int bb = i / DV, dd = i % DV;
+      if (b0 + bb >= B) continue;
+      float z = 0.f;
+      for (int p = 0; p < PARTS; ++p) z += red[p][bb][dd];
+      const size_t ui = (size_t)(b0 + bb) * H * DV + h * DV + dd;
+      if (g_pre) z *= sigmoidf_(bf16_bits_to_f32(g_pre[ui]));
+      if (u_f32)
+        ((float*)u)[ui] = z;
+      else
+        ((uint16_t*)u)[ui] = f32_to_bf16_bits(z);
+    }
+  }
+}
+
+template <class S>
+static hipError_t launch_decode_t(const DecodeAttnArgs& a, bool gather, hipStream_t st) {
+  const int grid = a.B * a.n_splits;
+  if (gather)
+    decode_attn_kernel<S, true><<<grid, 256, 0, st>>>(a);
+  else
+    decode_attn_kernel<S, false><<<grid, 256, 0, st>>>(a);
+  decode_merge_kernel<S><<<a.B * S::H, 256, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_attention(Shape s, const DecodeAttnArgs& a, bool gather, hipStream_t st) {
+  if (a.B <= 0) return hipSuccess;
+  if (s == Shape::K3) return launch_decode_t<ShapeK3>(a, gather, st);
+  return launch_decode_t<ShapeTiny>(a, gather, st);
+}
+
+hipError_t launch_absorb_q(Shape s, const uint16_t* q, int ldq, const uint16_t* wkvb, int B,
+                           uint16_t* qt, hipStream_t st) {
+  if (B <= 0) return hipSuccess;
+  if (s == Shape::K3)
+    absorb_q_kernel<ShapeK3><<<ShapeK3::H, 256, 0, st>>>(q, ldq, wkvb, B, qt);
+  else
+    absorb_q_kernel<ShapeTiny><<<ShapeTiny::H, 256, 0, st>>>(q, ldq, wkvb, B, qt);
+  return hipGetLastError();
+}
+
+hipError_t launch_vup_gate(Shape s, const float* o, const uint16_t* wkvb, const uint16_t* g_pre,
+                           int B, void* u, int u_f32, hipStream_t st) {
+  if (B <= 0) return hipSuccess;
+  if (s == Shape::K3)
+    vup_gate_kernel<ShapeK3><<<ShapeK3::H, 256, 0, st>>>(o, wkvb, g_pre, B, u, u_f32);
+  else
+    vup_gate_kernel<ShapeTiny><<<ShapeTiny::H, 256, 0, st>>>(o, wkvb, g_pre, B, u, u_f32);
+  return hipGetLastError();
+}
+
+}  // namespace gmla

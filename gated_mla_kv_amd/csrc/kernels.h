@@ -1,0 +1,107 @@
+// Internal launchers of the gfx950 kernels (host side). The C ABI in api.cpp validates its
+// arguments and calls these.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gmla {
+
+enum class Shape { K3, Tiny };
+
+hipError_t launch_rmsnorm(const float* x, int ldx, const uint16_t* gain, int M, int N, float eps,
+                          uint16_t* out, int ldo, hipStream_t s);
+hipError_t launch_layernorm(const float* x, int ldx, const uint16_t* gain, const uint16_t* bias,
+                            int M, int N, float eps, uint16_t* out, int ldo, hipStream_t s);
+
+struct KvAppendArgs {
+  const int32_t* pos;  // [B] first position of each sequence's new tokens
+  int B, T, T_cap, H, L, DS, DN, DV, DI;
+  const uint16_t* c; int ld_c;            // [B*T, ld_c]
+  const uint16_t* r; int ld_r;            // [B*T, ld_r]
+  const uint16_t* k_nope; int ld_k_tok, ld_k_head;
+  const uint16_t* v_new; int ld_v_tok, ld_v_head;
+  const uint16_t* idx_new; int ld_idx;
+  uint16_t* latent;  // [B, T_cap, L+DS] or null
+  uint16_t* k;       // [B, H, T_cap, DN+DS] or null
+  uint16_t* v;       // [B, H, T_cap, DV] or null
+  uint16_t* idx;     // [B, T_cap, DI] or null
+};
+hipError_t launch_kv_append(const KvAppendArgs& a, hipStream_t s);
+
+struct PrefillAttnArgs {
+  const uint16_t* q;       // [B, T, H, DQK]
+  const uint16_t* k;       // [B, H, T_cap, DQK]
+  const uint16_t* v;       // [B, H, T_cap, DV]
+  const int32_t* start;    // [B]
+  const uint16_t* g_pre;   // [B, T, H*DV] or null
+  void* u;                 // [B, T, H*DV]
+  int u_f32;
+  float* lse;              // [B, H, T] or null
+  int B, T, T_cap;
+  float scale;             // softmax scale
+};
+hipError_t launch_prefill_attention(Shape s, const PrefillAttnArgs& a, hipStream_t st);
+
+struct DecodeAttnArgs {
+  const uint16_t* q_tilde;  // [B, H, L+DS]
+  const uint16_t* latent;   // [B, T_cap, L+DS]
+  const int32_t* n_vis;     // [B] visible positions (contiguous mode), plus vis_offset
+  int vis_offset;
+  const int32_t* sel_idx;   // [B, sel_stride] selected positions (gather mode)
+  const int32_t* sel_cnt;   // [B]
+  int sel_stride;
+  int B, T_cap, n_splits, chunk;
+  float scale;
+  float* part_o;    // [B, n_splits, H, L]
+  float* part_ml;   // [B, n_splits, H, 2]
+  float* o_latent;  // [B, H, L]
+  float* lse;       // [B, H] or null
+};
+hipError_t launch_decode_attention(Shape s, const DecodeAttnArgs& a, bool gather, hipStream_t st);
+hipError_t launch_absorb_q(Shape s, const uint16_t* q, int ldq, const uint16_t* wkvb, int B,
+                           uint16_t* qt, hipStream_t st);
+hipError_t launch_vup_gate(Shape s, const float* o, const uint16_t* wkvb, const uint16_t* g_pre,
+                           int B, void* u, int u_f32, hipStream_t st);
+
+struct IndexScoreArgs {
+  const uint16_t* q_idx;  // [B, 32, 128]
+  const float* w_idx;     // [B, 32]
+  const uint16_t* idx_k;  // [B, T_cap, 128]
+  const int32_t* n_vis;   // [B], plus vis_offset
+  int vis_offset;
+  int B, T_cap;
+  float scale;            // 1/sqrt(n_idx * d_idx)
+  float* scores;          // [B, score_stride]
+  int score_stride;
+};
+hipError_t launch_index_scores(const IndexScoreArgs& a, int max_visible, hipStream_t st);
+
+struct TopkArgs {
+  const float* scores;  // [B, score_stride]
+  int score_stride;
+  const int32_t* n_vis;  // [B], plus vis_offset
+  int vis_offset;
+  int B, k;
+  int32_t* out_idx;  // [B, out_stride]
+  int out_stride;
+  int32_t* out_cnt;  // [B]
+};
+hipError_t launch_topk(const TopkArgs& a, hipStream_t st);
+
+struct ExpandedAttnArgs {
+  const uint16_t* q;  // [B, H, DQK]
+  const uint16_t* k;  // [B, H, T_cap, DQK]
+  const uint16_t* v;  // [B, H, T_cap, DV]
+  const int32_t* n_vis;
+  int vis_offset;
+  int B, T_cap;
+  float scale;
+  float* z;    // [B, H, DV]
+  float* lse;  // [B, H] or null
+};
+hipError_t launch_expanded_attention(Shape s, const ExpandedAttnArgs& a, hipStream_t st);
+hipError_t launch_gate_mul(const float* z, const uint16_t* g_pre, int n, void* u, int u_f32,
+                           hipStream_t st);
+
+}  // namespace gmla

@@ -1,0 +1,146 @@
+"""C ABI contract on the host (no GPU needed): the library loads, exports every function that
+include/gmla.h declares, and its host-side validation returns the documented error codes
+before anything is launched."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gmla.h")
+
+gm = pytest.importorskip("gated_mla_kv_amd")
+from workloads import K3, TINY  # noqa: E402
+
+if not os.path.exists(gm.LIB_PATH):
+    pytest.skip("libgmla.so not built", allow_module_level=True)
+
+OK, ERR_NULL, ERR_SHAPE, ERR_CAPACITY, ERR_UNSUPPORTED, ERR_WORKSPACE = 0, -1, -2, -3, -4, -5
+FAKE = 0x1000  # a non-null pointer value; never dereferenced by the validation paths tested
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w]+\s*\*?\s*(mla_\w+|kv_append|dsa_index_topk)\s*\(",
+                                 text, flags=re.M)))
+
+
+def test_every_declared_function_is_exported():
+    names = declared_functions()
+    assert len(names) >= 17, names
+    L = gm.lib()
+    for n in names:
+        assert hasattr(L, n), f"{n} declared in gmla.h but not exported"
+    # and nothing the binding calls is undeclared
+    for n in gm._SIGS:
+        assert n in names, n
+
+
+def test_status_strings():
+    assert gm.status_string(0) == "MLA_OK"
+    assert gm.status_string(-4) == "MLA_ERR_UNSUPPORTED"
+    assert gm.status_string(123) == "MLA_ERR_UNKNOWN"
+
+
+def test_dims_supported():
+    assert gm.dims_supported(gm.make_dims(K3))
+    assert gm.dims_supported(gm.make_dims(TINY))
+    assert not gm.dims_supported(gm.make_dims(K3.replace(n_heads=64)))
+    assert not gm.dims_supported(gm.make_dims(TINY.replace(n_idx_heads=4, d_idx=16, topk=8)))
+    assert not gm.dims_supported(gm.make_dims(K3.replace(topk=4096)))
+
+
+def test_workspace_bytes():
+    d = gm.make_dims(K3)
+    pre = gm.workspace_bytes(d, 1, 4096, 4096)
+    assert pre > 4096 * 12288 * 2  # at least the gated head outputs
+    dec = gm.workspace_bytes(d, 32, 1, 8193, gm.PATH_ABSORBED)
+    assert dec > 32 * 8 * 96 * 512 * 4  # split partials
+    assert gm.workspace_bytes(d, 32, 1, 8193, gm.PATH_ABSORBED, 16) > dec
+    assert gm.workspace_bytes(gm.make_dims(K3.replace(n_heads=8)), 1, 1, 10) == 0
+
+
+def _cache(latent=FAKE, k=FAKE, v=FAKE, idx=None, B=2, T_cap=100):
+    return gm.MlaCache(latent, k, v, idx, B, T_cap)
+
+
+def _weights():
+    return gm.MlaWeights(*([FAKE] * 8 + [None] * 5))
+
+
+def _call_prefill(dims, cache, max_end=50, B=2, T=10, ws_bytes=1 << 40, weights=None, x=FAKE):
+    L = gm.lib()
+    return L.mla_prefill(ctypes.byref(dims), ctypes.byref(weights or _weights()), ctypes.byref(cache), FAKE,
+                         max_end, x, B, T, FAKE, 0, None, FAKE, ws_bytes, None)
+
+
+def test_prefill_validation():
+    d = gm.make_dims(K3)
+    assert _call_prefill(gm.make_dims(K3.replace(hidden=1000)), _cache()) == ERR_UNSUPPORTED
+    assert _call_prefill(d, _cache(), x=None) == ERR_NULL
+    assert _call_prefill(d, _cache(k=None)) == ERR_NULL
+    assert _call_prefill(d, _cache(T_cap=100), max_end=101) == ERR_CAPACITY
+    assert _call_prefill(d, _cache(B=1), B=2) == ERR_SHAPE
+    assert _call_prefill(d, _cache(), B=-1) == ERR_SHAPE
+    assert _call_prefill(d, _cache(), ws_bytes=10) == ERR_WORKSPACE
+    w = _weights()
+    w.w_g = None
+    assert _call_prefill(d, _cache(), weights=w) == ERR_NULL
+    # empty work is valid and launches nothing
+    assert _call_prefill(d, _cache(), B=0) == OK
+    assert _call_prefill(d, _cache(), T=0) == OK
+
+
+def _call_decode(dims, cache, path=0, max_len=50, B=2, ws_bytes=1 << 40, weights=None, splits=0):
+    L = gm.lib()
+    return L.mla_decode(ctypes.byref(dims), ctypes.byref(weights or _weights()), ctypes.byref(cache), FAKE,
+                        max_len, FAKE, B, path, splits, None, None, FAKE, 0, FAKE, ws_bytes, None)
+
+
+def test_decode_validation():
+    d = gm.make_dims(K3)
+    assert _call_decode(d, _cache(), path=7) == ERR_UNSUPPORTED
+    assert _call_decode(d, _cache(T_cap=64), max_len=65) == ERR_CAPACITY
+    assert _call_decode(d, _cache(k=None, v=None), path=gm.PATH_EXPANDED) == ERR_NULL
+    assert _call_decode(d, _cache(), ws_bytes=1000) == ERR_WORKSPACE
+    # sparse needs the indexer
+    assert _call_decode(gm.make_dims(K3.replace(n_idx_heads=0)), _cache(), path=gm.PATH_SPARSE) == ERR_UNSUPPORTED
+    assert _call_decode(d, _cache(idx=None), path=gm.PATH_SPARSE) == ERR_NULL
+    assert _call_decode(d, _cache(), B=0) == OK
+    assert _call_decode(d, _cache(), splits=-1) == ERR_SHAPE
+
+
+def test_kv_append_validation():
+    L = gm.lib()
+    d = gm.make_dims(TINY)
+    c = _cache(T_cap=16)
+    call = lambda max_end, B=2, T=4, idx=None, cc=c, dd=d, cp=FAKE: L.kv_append(  # noqa: E731
+        ctypes.byref(dd), ctypes.byref(cc), FAKE, max_end, B, T, cp, FAKE, FAKE, FAKE, idx, None)
+    assert call(17) == ERR_CAPACITY
+    assert call(3) == ERR_SHAPE           # max_end below T
+    assert call(8, cp=None) == ERR_NULL
+    assert call(8, idx=FAKE) == ERR_UNSUPPORTED   # index keys without the indexer
+    assert call(8, B=0) == OK
+
+
+def test_dsa_and_stage_validation():
+    L = gm.lib()
+    d = gm.make_dims(K3)
+    assert L.dsa_index_topk(ctypes.byref(gm.make_dims(TINY)), FAKE, FAKE, FAKE, 10, FAKE, 5, 1, FAKE, FAKE,
+                            None, FAKE, 1 << 20, None) == ERR_UNSUPPORTED
+    assert L.dsa_index_topk(ctypes.byref(d), FAKE, FAKE, FAKE, 10, FAKE, 11, 1, FAKE, FAKE, None, FAKE,
+                            1 << 20, None) == ERR_CAPACITY
+    assert L.dsa_index_topk(ctypes.byref(d), FAKE, FAKE, FAKE, 100, FAKE, 90, 2, FAKE, FAKE, None, FAKE,
+                            100, None) == ERR_WORKSPACE
+    assert L.mla_gemm(FAKE, 30, FAKE, 4, 4, 30, FAKE, 4, 0, None) == ERR_SHAPE   # K not a multiple of 8
+    assert L.mla_gemm(FAKE, 32, FAKE, 4, 4, 32, FAKE, 4, 5, None) == ERR_UNSUPPORTED
+    assert L.mla_rmsnorm(None, 64, FAKE, 4, 64, 1e-6, FAKE, 64, None) == ERR_NULL
+    c = _cache()
+    assert L.mla_decode_attention(ctypes.byref(d), FAKE, ctypes.byref(c), FAKE, 101, 2, 0, FAKE, None, FAKE,
+                                  1 << 40, None) == ERR_CAPACITY
+    assert L.mla_decode_attention(ctypes.byref(d), FAKE, ctypes.byref(c), FAKE, 50, 2, 0, FAKE, None, FAKE,
+                                  16, None) == ERR_WORKSPACE
+    assert L.mla_expanded_attention(ctypes.byref(d), FAKE, ctypes.byref(_cache(v=None)), FAKE, 10, 2, FAKE,
+                                    None, None) == ERR_NULL

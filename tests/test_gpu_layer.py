@@ -1,0 +1,129 @@
+"""Whole-layer parity on the GPU: mla_prefill then mla_decode against the oracle's layer on the
+same seeded bf16 inputs (tolerances in gpu_helpers)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from gpu_helpers import check_rows, dev_bf16, f64, i32, to_np
+from workloads import (K3, K3_SMALL_TOPK, TINY, make_index_prefix, make_latent_prefix, make_layer_weights,
+                       make_tokens)
+
+pytestmark = pytest.mark.gpu
+gm = pytest.importorskip("gated_mla_kv_amd")
+
+
+def _layer(d, seed, dist):
+    from gated_mla_kv_amd.layer import LayerBuffers
+    lw = make_layer_weights(d, seed=seed, dist=dist, perturb_norms=True)
+    return lw, LayerBuffers(d, lw.w)
+
+
+def _w64(lw):
+    return {k: f64(v) for k, v in lw.w.items()}
+
+
+@pytest.mark.parametrize("dims,dist,B,T,steps,path", [
+    (TINY, "fan_in", 1, 64, 8, gm.PATH_ABSORBED),     # the tiny oracle-scale layer
+    (TINY, "fan_in", 1, 64, 8, gm.PATH_EXPANDED),
+    (K3, "k3", 2, 40, 3, gm.PATH_ABSORBED),
+    (K3, "k3", 1, 150, 2, gm.PATH_EXPANDED),
+])
+def test_prefill_then_decode(dims, dist, B, T, steps, path):
+    d = dims
+    print(f"layer H={d.n_heads} B={B} T={T} steps={steps} path={path}", flush=True)
+    lw, L = _layer(d, 90, dist)
+    w = _w64(lw)
+    T_cap = T + steps + 3
+    cache = L.new_cache(B, T_cap, expanded=True)
+    x = make_tokens(d, B, T, seed=90)
+    y = L.prefill(cache, dev_bf16(x), i32([0] * B), T, out_dtype=gm.OUT_F32)
+    oc = O.Cache(d, B)
+    y_ref, _ = O.layer_forward(f64(x), w, oc, d)
+    torch.cuda.synchronize()
+    check_rows(to_np(y), y_ref, "prefill y")
+    for s in range(steps):
+        xs = make_tokens(d, B, 1, seed=90, step=s)[:, 0]
+        yd = L.decode(cache, dev_bf16(xs), i32([T + s] * B), T + s + 1, path=path, out_dtype=gm.OUT_F32)
+        yd_ref, _ = O.layer_forward(f64(xs)[:, None], w, oc, d, form="absorbed" if path == gm.PATH_ABSORBED
+                                    else "expanded")
+        torch.cuda.synchronize()
+        check_rows(to_np(yd), yd_ref[:, 0], f"decode step {s} y")
+    # the caches the GPU kept equal the oracle's bf16 caches
+    from gated_mla_kv_amd.layer import bf16_bits
+    n = T + steps
+    np.testing.assert_array_equal(f64(bf16_bits(cache.latent))[:, :n].shape, oc.latent.shape)
+    lat_err = np.abs(f64(bf16_bits(cache.latent))[:, :n] - oc.latent)
+    # equal up to an occasional one-ulp difference where fp32 and fp64 round differently
+    assert np.mean(lat_err > 0) < 0.02
+
+
+def test_prefill_bf16_output_and_chunked_start():
+    """Two prefill calls (P = 0 then P = 24) equal one 40-token prefill."""
+    d = K3
+    lw, L = _layer(d, 91, "k3")
+    w = _w64(lw)
+    B, T1, T2 = 1, 24, 16
+    cache = L.new_cache(B, T1 + T2)
+    x = make_tokens(d, B, T1 + T2, seed=91)
+    L.prefill(cache, dev_bf16(x[:, :T1]), i32([0]), T1)
+    y2 = L.prefill(cache, dev_bf16(x[:, T1:]), i32([T1]), T1 + T2)
+    y_ref, _ = O.layer_forward(f64(x), w, O.Cache(d, B), d)
+    torch.cuda.synchronize()
+    check_rows(to_np(y2), y_ref[:, T1:], "chunked prefill y (bf16)", bf16_out=True)
+
+
+def test_decode_ragged_lengths():
+    d = K3
+    lw, L = _layer(d, 92, "k3")
+    w = _w64(lw)
+    lens = [3, 130, 57]
+    B = len(lens)
+    T_cap = max(lens) + 2
+    cache = L.new_cache(B, T_cap, expanded=True)
+    lat = make_latent_prefix(d, B, max(lens), seed=92)
+    cache.latent[:, :max(lens)] = dev_bf16(lat)
+    x = make_tokens(d, B, 1, seed=92, step=0)[:, 0]
+    y = L.decode(cache, dev_bf16(x), i32(lens), max(lens) + 1, path=gm.PATH_ABSORBED, out_dtype=gm.OUT_F32)
+    torch.cuda.synchronize()
+    for b in range(B):
+        oc = O.Cache(d, 1, expanded=False)
+        oc.set_prefix(f64(lat[b:b + 1, :lens[b]]))
+        yr, _ = O.layer_forward(f64(x[b:b + 1])[:, None], w, oc, d, form="absorbed")
+        check_rows(to_np(y[b]), yr[0, 0], f"ragged decode b={b}")
+
+
+def test_dsa_sparse_decode_step():
+    d = K3_SMALL_TOPK
+    lw, L = _layer(d, 93, "k3")
+    w = _w64(lw)
+    B, T = 2, 300
+    T_cap = T + 4
+    cache = L.new_cache(B, T_cap, expanded=False, index=True)
+    lat = make_latent_prefix(d, B, T, seed=93)
+    idx = make_index_prefix(d, B, T, seed=93)
+    cache.latent[:, :T] = dev_bf16(lat)
+    cache.idx[:, :T] = dev_bf16(idx)
+    x = make_tokens(d, B, 1, seed=93, step=0)[:, 0]
+    sel = torch.empty((B, d.topk), dtype=torch.int32, device="cuda")
+    cnt = torch.empty((B,), dtype=torch.int32, device="cuda")
+    y = L.decode(cache, dev_bf16(x), i32([T] * B), T + 1, path=gm.PATH_SPARSE, out_dtype=gm.OUT_F32,
+                 sel_idx=sel, sel_cnt=cnt)
+    torch.cuda.synchronize()
+    oc = O.Cache(d, B, expanded=False)
+    oc.set_prefix(f64(lat), f64(idx))
+    y_ref, ex = O.dsa_decode_step(f64(x), w, oc, d)
+    check_rows(to_np(y), y_ref, "dsa decode y")
+    sel_np = sel.cpu().numpy()
+    assert (cnt.cpu().numpy() == d.topk).all()
+    for b in range(B):
+        got = sel_np[b]
+        assert np.all(np.diff(got) > 0) and got.max() <= T
+        # positions chosen on bf16 index queries agree with the float64 oracle's up to swaps near
+        # its k-th score (the index query is rounded to bf16 before scoring)
+        I = ex["scores"][b]
+        tau = np.sort(I)[::-1][d.topk - 1]
+        differ = np.setxor1d(got, ex["selected"][b])
+        assert np.all(np.abs(I[differ] - tau) < 2e-2 * np.std(I)), differ
+    # the current token's index key was appended at position T
+    assert torch.count_nonzero(cache.idx[:, T].float()) > 0
