@@ -297,8 +297,11 @@ def layer_forward(x, w, cache: Cache, dims, form: str = "expanded"):
     P = cache.length
     cq, q_nope, q_shared = query_path(x, w, dims)
     c, r = kv_down_path(x, w, dims)
-    k_nope, v = kv_up(c, w, dims)
-    k = expand_keys(k_nope, r)
+    # Each head's key and value are W^K_h c_s and W^V_h c_s of the latent as the cache holds it
+    # ([DSA] eqs. (7)-(8): the cache keeps the normalised c_s and r_s; [KV]: in bfloat16).
+    c_s = cache._store(c)
+    k_nope, v = kv_up(c_s, w, dims)
+    k = expand_keys(k_nope, cache._store(r))
     cache.append(c, r, k, v.transpose(0, 2, 1, 3))
     scale = softmax_scale(dims)
     if form == "expanded":
@@ -374,22 +377,32 @@ def attention_absorbed_subset(q_tilde, latent, positions, scale: float, dims):
     return o, (m + np.log(l))[:, 0]
 
 
-def dsa_decode_step(x, w, cache: Cache, dims):
+def dsa_decode_step(x, w, cache: Cache, dims, index_query_bf16: bool = True):
     """One decode token per sequence through the Gated DSA layer (the per-query pseudocode).
 
     x [B, hidden]. The main latent and the index key of the current token are appended
     first, so t includes it; scores, top-k, then sparse MLA with the main q and latent
     cache, then the gate and o_proj. Returns (y [B, hidden], extras).
+
+    With ``index_query_bf16`` the indexer's query side is held in bfloat16 (c^Q as it enters
+    W_q^I, and q^I itself) before scoring: the top-k is an integer decision taken on scores,
+    and the blog's eq. (5) leaves out the low-precision quantisation that the deployed path
+    applies to the index query (text after eq. (5)); bf16 is the precision the library's
+    kernels hold it in. The index keys are held in the index cache's bf16 either way.
     """
     x = np.asarray(x, dtype=F64)
     B = x.shape[0]
     cq, q_nope, q_shared = query_path(x, w, dims)
     c, r = kv_down_path(x, w, dims)
-    qi, ki, a = index_projections(x, cq, w, dims)
+    if index_query_bf16:
+        qi, ki, a = index_projections(x, round_to_bf16(cq), w, dims)
+        qi = round_to_bf16(qi)
+    else:
+        qi, ki, a = index_projections(x, cq, w, dims)
     H = dims.n_heads
     if cache.expanded:
-        k_nope, v = kv_up(c, w, dims)
-        cache.append(c[:, None], r[:, None], expand_keys(k_nope[:, None], r[:, None]),
+        k_nope, v = kv_up(cache._store(c), w, dims)
+        cache.append(c[:, None], r[:, None], expand_keys(k_nope[:, None], cache._store(r)[:, None]),
                      v[:, None].transpose(0, 2, 1, 3), ki[:, None])
     else:
         cache.append(c[:, None], r[:, None], idx_k=ki[:, None])
