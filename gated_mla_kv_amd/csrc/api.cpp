@@ -66,7 +66,7 @@ struct Ws {
   float* xq;       // [M, q_lora]   q_a_proj output (pre-norm)
   float* xc;       // [M, kv_lora]  latent before its norm
   uint16_t* r;     // [M, d_shared] shared key
-  uint16_t* gpre;  // [M, H*d_v]    gate pre-activation
+  float* gpre;     // [M, H*d_v]    gate pre-activation (fp32)
   float* kpre;     // [M, d_idx]    index key before its LayerNorm
   float* aw;       // [M, n_idx]    index head weights
   uint16_t* cq;    // [M, q_lora]
@@ -97,7 +97,7 @@ Ws carve(const mla_dims* d, int M, bool decode, int max_len, int path, int split
   w.xq = cv.take<float>((size_t)M * d->q_lora);
   w.xc = cv.take<float>((size_t)M * d->kv_lora);
   w.r = cv.take<uint16_t>((size_t)M * d->d_shared);
-  w.gpre = cv.take<uint16_t>((size_t)M * H * d->d_v);
+  w.gpre = cv.take<float>((size_t)M * H * d->d_v);
   w.kpre = cv.take<float>(dsa ? (size_t)M * d->d_idx : 0);
   w.aw = cv.take<float>(dsa ? (size_t)M * d->n_idx_heads : 0);
   w.cq = cv.take<uint16_t>((size_t)M * d->q_lora);
@@ -174,7 +174,7 @@ int run_x_gemm(const mla_dims* d, const mla_weights* w, const void* x, int M, co
   push(g, seg(w->w_kv_a, d->kv_lora, ws.xc, d->kv_lora, true, n));
   push(g, seg((const uint16_t*)w->w_kv_a + (size_t)d->kv_lora * d->hidden, d->d_shared, ws.r,
               d->d_shared, false, n));
-  if (d->use_gate) push(g, seg(w->w_g, d->n_heads * d->d_v, ws.gpre, d->n_heads * d->d_v, false, n));
+  if (d->use_gate) push(g, seg(w->w_g, d->n_heads * d->d_v, ws.gpre, d->n_heads * d->d_v, true, n));
   if (with_idx) {
     push(g, seg(w->w_idx_k, d->d_idx, ws.kpre, d->d_idx, true, n));
     push(g, seg(w->w_idx_w, d->n_idx_heads, ws.aw, d->n_idx_heads, true, n));
@@ -299,7 +299,7 @@ int mla_layernorm(const float* x, int32_t ldx, const void* gain, const void* bia
 
 int mla_prefill_attention(const mla_dims* d, const void* q, const mla_cache* cache,
                           const int32_t* start_pos, int32_t max_end, int32_t B, int32_t T,
-                          const void* g_pre, void* u, int32_t out_dtype, float* lse,
+                          const float* g_pre, void* u, int32_t out_dtype, float* lse,
                           hipStream_t stream) {
   Shape s;
   if (!d) return MLA_ERR_NULL;
@@ -316,7 +316,7 @@ int mla_prefill_attention(const mla_dims* d, const void* q, const mla_cache* cac
   a.k = (const uint16_t*)cache->k;
   a.v = (const uint16_t*)cache->v;
   a.start = start_pos;
-  a.g_pre = (const uint16_t*)g_pre;
+  a.g_pre = g_pre;
   a.u = u;
   a.u_f32 = out_dtype == MLA_OUT_F32;
   a.lse = lse;
@@ -423,7 +423,7 @@ int mla_expanded_attention(const mla_dims* d, const void* q, const mla_cache* ca
   return MLA_OK;
 }
 
-int mla_value_up_gate(const mla_dims* d, const float* o_latent, const void* w_kv_b, const void* g_pre,
+int mla_value_up_gate(const mla_dims* d, const float* o_latent, const void* w_kv_b, const float* g_pre,
                       int32_t B, void* u, int32_t out_dtype, hipStream_t stream) {
   Shape s;
   if (!d) return MLA_ERR_NULL;
@@ -432,7 +432,7 @@ int mla_value_up_gate(const mla_dims* d, const float* o_latent, const void* w_kv
   if (B == 0) return MLA_OK;
   if (!o_latent || !w_kv_b || !u) return MLA_ERR_NULL;
   if (out_dtype != MLA_OUT_BF16 && out_dtype != MLA_OUT_F32) return MLA_ERR_UNSUPPORTED;
-  CHECK_HIP(launch_vup_gate(s, o_latent, (const uint16_t*)w_kv_b, (const uint16_t*)g_pre, B, u,
+  CHECK_HIP(launch_vup_gate(s, o_latent, (const uint16_t*)w_kv_b, g_pre, B, u,
                             out_dtype == MLA_OUT_F32, stream));
   return MLA_OK;
 }
@@ -690,7 +690,7 @@ int mla_decode(const mla_dims* d, const mla_weights* w, const mla_cache* cache, 
     }
     CHECK_HIP(launch_kv_append(a, stream));
   }
-  const uint16_t* gate = d->use_gate ? wsp.gpre : nullptr;
+  const float* gate = d->use_gate ? wsp.gpre : nullptr;
   if (path == MLA_PATH_EXPANDED) {
     ExpandedAttnArgs a{};
     a.q = wsp.q;

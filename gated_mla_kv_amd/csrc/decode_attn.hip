@@ -286,7 +286,7 @@ __global__ __launch_bounds__(256) void absorb_q_kernel(const uint16_t* __restric
 template <class S>
 __global__ __launch_bounds__(256) void vup_gate_kernel(const float* __restrict__ o,
                                                        const uint16_t* __restrict__ wkvb,
-                                                       const uint16_t* __restrict__ g_pre, int B,
+                                                       const float* __restrict__ g_pre, int B,
                                                        void* __restrict__ u, int u_f32) {
   constexpr int H = S::H, DN = S::DN, DV = S::DV, L = S::L;
   constexpr int PARTS = (256 / DV) < (L / 8) ? (256 / DV) : (L / 8);  // latent slices of >= 8
@@ -328,7 +328,7 @@ __global__ __launch_bounds__(256) void vup_gate_kernel(const float* __restrict__
       float z = 0.f;
       for (int p = 0; p < PARTS; ++p) z += red[p][bb][dd];
       const size_t ui = (size_t)(b0 + bb) * H * DV + h * DV + dd;
-      if (g_pre) z *= sigmoidf_(bf16_bits_to_f32(g_pre[ui]));
+      if (g_pre) z *= sigmoidf_(g_pre[ui]);
       if (u_f32)
         ((float*)u)[ui] = z;
       else
@@ -364,7 +364,7 @@ hipError_t launch_absorb_q(Shape s, const uint16_t* q, int ldq, const uint16_t* 
   return hipGetLastError();
 }
 
-hipError_t launch_vup_gate(Shape s, const float* o, const uint16_t* wkvb, const uint16_t* g_pre,
+hipError_t launch_vup_gate(Shape s, const float* o, const uint16_t* wkvb, const float* g_pre,
                            int B, void* u, int u_f32, hipStream_t st) {
   if (B <= 0) return hipSuccess;
   if (s == Shape::K3)

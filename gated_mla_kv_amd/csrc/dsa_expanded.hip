@@ -275,12 +275,12 @@ __global__ __launch_bounds__(256) void expanded_attn_kernel(ExpandedAttnArgs a) 
   if (threadIdx.x == 0 && a.lse) a.lse[bh] = (M + __log2f(den)) * 0.6931471805599453f;
 }
 
-// u[i] = z[i] * sigmoid(g_pre[i]) over B*H*DV elements (z f32, g_pre bf16 or null).
-__global__ void gate_mul_kernel(const float* z, const uint16_t* g_pre, int n, void* u, int u_f32) {
+// u[i] = z[i] * sigmoid(g_pre[i]) over B*H*DV elements (z and g_pre f32; g_pre may be null).
+__global__ void gate_mul_kernel(const float* z, const float* g_pre, int n, void* u, int u_f32) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= n) return;
   float v = z[i];
-  if (g_pre) v *= sigmoidf_(bf16_bits_to_f32(g_pre[i]));
+  if (g_pre) v *= sigmoidf_(g_pre[i]);
   if (u_f32)
     ((float*)u)[i] = v;
   else
@@ -308,7 +308,7 @@ hipError_t launch_expanded_attention(Shape s, const ExpandedAttnArgs& a, hipStre
   return hipGetLastError();
 }
 
-hipError_t launch_gate_mul(const float* z, const uint16_t* g_pre, int n, void* u, int u_f32,
+hipError_t launch_gate_mul(const float* z, const float* g_pre, int n, void* u, int u_f32,
                            hipStream_t st) {
   if (n <= 0) return hipSuccess;
   gate_mul_kernel<<<cdiv(n, 256), 256, 0, st>>>(z, g_pre, n, u, u_f32);

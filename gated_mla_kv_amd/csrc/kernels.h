@@ -34,7 +34,7 @@ struct PrefillAttnArgs {
   const uint16_t* k;       // [B, H, T_cap, DQK]
   const uint16_t* v;       // [B, H, T_cap, DV]
   const int32_t* start;    // [B]
-  const uint16_t* g_pre;   // [B, T, H*DV] or null
+  const float* g_pre;      // [B, T, H*DV] f32 or null
   void* u;                 // [B, T, H*DV]
   int u_f32;
   float* lse;              // [B, H, T] or null
@@ -61,7 +61,7 @@ struct DecodeAttnArgs {
 hipError_t launch_decode_attention(Shape s, const DecodeAttnArgs& a, bool gather, hipStream_t st);
 hipError_t launch_absorb_q(Shape s, const uint16_t* q, int ldq, const uint16_t* wkvb, int B,
                            uint16_t* qt, hipStream_t st);
-hipError_t launch_vup_gate(Shape s, const float* o, const uint16_t* wkvb, const uint16_t* g_pre,
+hipError_t launch_vup_gate(Shape s, const float* o, const uint16_t* wkvb, const float* g_pre,
                            int B, void* u, int u_f32, hipStream_t st);
 
 struct IndexScoreArgs {
@@ -101,7 +101,7 @@ struct ExpandedAttnArgs {
   float* lse;  // [B, H] or null
 };
 hipError_t launch_expanded_attention(Shape s, const ExpandedAttnArgs& a, hipStream_t st);
-hipError_t launch_gate_mul(const float* z, const uint16_t* g_pre, int n, void* u, int u_f32,
+hipError_t launch_gate_mul(const float* z, const float* g_pre, int n, void* u, int u_f32,
                            hipStream_t st);
 
 }  // namespace gmla

@@ -222,11 +222,11 @@ __global__ __launch_bounds__(64 * NW) void prefill_attn_kernel(PrefillAttnArgs a
 #pragma unroll
         for (int i = 0; i < 4; ++i) z[i] = o[d][rb * 4 + i] * inv_l;
         if (a.g_pre) {
-          const u32x2 gw = *(const u32x2*)(a.g_pre + urow + dv);
-          z[0] *= sigmoidf_(lo_bf16(gw.x));
-          z[1] *= sigmoidf_(hi_bf16(gw.x));
-          z[2] *= sigmoidf_(lo_bf16(gw.y));
-          z[3] *= sigmoidf_(hi_bf16(gw.y));
+          const f32x4 gv = *(const f32x4*)(a.g_pre + urow + dv);
+          z[0] *= sigmoidf_(gv[0]);
+          z[1] *= sigmoidf_(gv[1]);
+          z[2] *= sigmoidf_(gv[2]);
+          z[3] *= sigmoidf_(gv[3]);
         }
         if (a.u_f32) {
           *(f32x4*)((float*)a.u + urow + dv) = f32x4{z[0], z[1], z[2], z[3]};

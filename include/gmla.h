@@ -201,11 +201,11 @@ int mla_layernorm(const float* x, int32_t ldx, const void* gain, const void* bia
 /* Prefill attention with the gate epilogue ([DSA] eqs. (9)-(10) before W_o):
  *   u[b,i,h*d_v+d] = z[b,i,h,d] * sigmoid(g_pre[b,i,h*d_v+d])  (times 1 when g_pre is NULL)
  *   z = softmax_j(q[b,i,h].k[b,h,j] * scale) v[b,h,j] over j <= start_pos[b]+i.
- * q [B,T,H,d_nope+d_shared] bf16, K/V from cache->k / cache->v, g_pre [B,T,H*d_v] bf16 or NULL,
+ * q [B,T,H,d_nope+d_shared] bf16, K/V from cache->k / cache->v, g_pre [B,T,H*d_v] f32 or NULL,
  * u [B,T,H*d_v] (bf16 or f32), lse [B,H,T] f32 or NULL. */
 int mla_prefill_attention(const mla_dims* dims, const void* q, const mla_cache* cache,
                           const int32_t* start_pos, int32_t max_end, int32_t B, int32_t T,
-                          const void* g_pre, void* u, int32_t out_dtype, float* lse,
+                          const float* g_pre, void* u, int32_t out_dtype, float* lse,
                           hipStream_t stream);
 
 /* Query absorption ([DSA] latent absorption): q_tilde[b,h] = [ W^K_h^T q_nope[b,h] ‖ q_shared[b,h] ]
@@ -240,9 +240,9 @@ int mla_expanded_attention(const mla_dims* dims, const void* q, const mla_cache*
 
 /* Value up-projection and gate: u[b,h*d_v+d] = (W^V_h o_latent[b,h])[d] * sigmoid(g_pre[b,h*d_v+d])
  * with W^V_h = w_kv_b rows [h*(d_nope+d_v)+d_nope, (h+1)*(d_nope+d_v)).
- * o_latent [B,H,kv_lora] f32, g_pre [B,H*d_v] bf16 or NULL, u [B,H*d_v] bf16 or f32. */
+ * o_latent [B,H,kv_lora] f32, g_pre [B,H*d_v] f32 or NULL, u [B,H*d_v] bf16 or f32. */
 int mla_value_up_gate(const mla_dims* dims, const float* o_latent, const void* w_kv_b,
-                      const void* g_pre, int32_t B, void* u, int32_t out_dtype,
+                      const float* g_pre, int32_t B, void* u, int32_t out_dtype,
                       hipStream_t stream);
 
 #ifdef __cplusplus

@@ -125,16 +125,17 @@ def test_prefill_attention(dims, B, T, starts):
     q = rand_bf16((B, T, H, d.d_qk), 20, std=0.8)
     kc = rand_bf16((B, H, T_cap, d.d_qk), 21, std=0.8)
     vc = rand_bf16((B, H, T_cap, d.d_v), 22)
-    g = rand_bf16((B, T, H * d.d_v), 23)
+    g = np.random.default_rng(23).standard_normal((B, T, H * d.d_v)).astype(np.float32)
+    gd = torch.tensor(g, device="cuda")
     K, V = dev_bf16(kc), dev_bf16(vc)
     cache = gm.MlaCache(None, K.data_ptr(), V.data_ptr(), None, B, T_cap)
     u = torch.empty((B, T, H * d.d_v), dtype=torch.float32, device="cuda")
     lse = torch.empty((B, H, T), dtype=torch.float32, device="cuda")
     dims_c = gm.make_dims(d)
-    gm.mla_prefill_attention(dims_c, dev_bf16(q), cache, i32(starts), max(starts) + T, B, T, dev_bf16(g), u,
+    gm.mla_prefill_attention(dims_c, dev_bf16(q), cache, i32(starts), max(starts) + T, B, T, gd, u,
                              gm.OUT_F32, lse)
     u16 = torch.empty((B, T, H * d.d_v), dtype=torch.bfloat16, device="cuda")
-    gm.mla_prefill_attention(dims_c, dev_bf16(q), cache, i32(starts), max(starts) + T, B, T, dev_bf16(g), u16,
+    gm.mla_prefill_attention(dims_c, dev_bf16(q), cache, i32(starts), max(starts) + T, B, T, gd, u16,
                              gm.OUT_BF16, None)
     _sync()
     scale = O.softmax_scale(d)
@@ -142,7 +143,7 @@ def test_prefill_attention(dims, B, T, starts):
         P = starts[b]
         z, lse_ref = O.attention_expanded(f64(q[b:b + 1]), f64(kc[b:b + 1, :, :P + T]), f64(vc[b:b + 1, :, :P + T]),
                                           scale, P)
-        u_ref = z.reshape(1, T, H * d.d_v) * O.sigmoid(f64(g[b:b + 1]))
+        u_ref = z.reshape(1, T, H * d.d_v) * O.sigmoid(g[b:b + 1].astype(np.float64))
         check_rows(to_np(u[b:b + 1]), u_ref, f"prefill u b={b}")
         check_rows(to_np(u16[b:b + 1]), u_ref, f"prefill u bf16 b={b}", bf16_out=True)
         check_scores(to_np(lse[b]), lse_ref[0], f"prefill lse b={b}")
@@ -241,12 +242,13 @@ def test_absorb_query_and_value_up(dims, B):
     qv = f64(q).reshape(B, H, d.d_qk)
     qt_ref = O.absorbed_query(qv[..., :d.d_nope], qv[..., d.d_nope:], w64, d)
     o = rand_bf16((B, H, d.kv_lora), 62)
-    g = rand_bf16((B, H * d.d_v), 63)
+    g = np.random.default_rng(63).standard_normal((B, H * d.d_v)).astype(np.float32)
     u = torch.empty((B, H * d.d_v), dtype=torch.float32, device="cuda")
-    gm.mla_value_up_gate(dims_c, torch.tensor(bf16_bits_to_f32(o), device="cuda"), Wd, dev_bf16(g), B, u, gm.OUT_F32)
+    gm.mla_value_up_gate(dims_c, torch.tensor(bf16_bits_to_f32(o), device="cuda"), Wd, torch.tensor(g, device="cuda"),
+                         B, u, gm.OUT_F32)
     _sync()
     check_rows(to_np(qt), qt_ref, "absorbed query", bf16_out=True)
-    u_ref = O.value_up(f64(o), w64, d).reshape(B, H * d.d_v) * O.sigmoid(f64(g))
+    u_ref = O.value_up(f64(o), w64, d).reshape(B, H * d.d_v) * O.sigmoid(g.astype(np.float64))
     check_rows(to_np(u), u_ref, "value up + gate")
 
 

@@ -105,9 +105,14 @@ class TensorId:
 def bf16_bits(a: np.ndarray) -> np.ndarray:
     """Round float32 values to bfloat16 (round to nearest, ties to even); returns uint16 bits."""
     f = np.ascontiguousarray(a, dtype=np.float32)
-    u = f.view(np.uint32).astype(np.uint64)
-    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
-    return rounded.astype(np.uint16)
+    u = f.view(np.uint32)
+    # finite inputs: u <= 0xFF7FFFFF, so the rounding add cannot overflow 32 bits
+    t = u >> np.uint32(16)
+    t &= np.uint32(1)
+    t += np.uint32(0x7FFF)
+    t += u
+    t >>= np.uint32(16)
+    return t.astype(np.uint16)
 
 
 def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
