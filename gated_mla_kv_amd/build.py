@@ -26,7 +26,7 @@ FLAGS = [
     "-Wno-unused-command-line-argument",
 ]
 SOURCES = ["api.cpp", "gemm.hip", "norm_append.hip", "prefill_attn.hip", "decode_attn.hip",
-           "dsa_expanded.hip"]
+           "decode_attn_k3.hip", "dsa_expanded.hip"]
 
 
 def _hipcc() -> str:

@@ -6,7 +6,8 @@
 // position is read once, as one 576-value latent row, for all 96 heads at once: 1,152 bytes
 // instead of the expanded cache's 61,440 (KV cache card: 30,720 values per position).
 //
-// decode_attn_kernel: one workgroup per (sequence, split of the positions), 4 waves.
+// decode_attn_kernel: the generic form, used for the tiny oracle-scale shape (the K3 shape has
+// its own kernel in decode_attn_k3.hip). One workgroup per (sequence, split), 4 waves.
 // * The latent rows of a 32-position tile are staged in LDS (double-buffered, via registers,
 //   16-byte loads, each HBM byte read once).
 // * Waves 0..HP/32-1 each own 32 heads: their q~ rows sit in VGPRs as the B operand of
@@ -216,9 +217,11 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeAttnArgs a) {
 }
 
 // Combine the splits of one (sequence, head): o = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.
+// One workgroup of 128 threads per (b, h); thread t owns latent features 4t .. 4t+3.
 template <class S>
-__global__ __launch_bounds__(256) void decode_merge_kernel(DecodeAttnArgs a) {
+__global__ __launch_bounds__(128) void decode_merge_kernel(DecodeAttnArgs a) {
   using C = DecodeCfg<S>;
+  static_assert(C::L % 4 == 0 && C::L <= 512, "features per thread");
   const int bh = blockIdx.x;
   const int b = bh / C::H, h = bh % C::H;
   const int ns = a.n_splits;
@@ -231,13 +234,17 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeAttnArgs a) {
     if (m != -INFINITY) den += fast_exp2(m - M) * a.part_ml[((base + s) * C::H + h) * 2 + 1];
   }
   const float inv = den > 0.f ? 1.0f / den : 0.f;  // no visible position: zeros
-  for (int f = threadIdx.x; f < C::L; f += blockDim.x) {
-    float acc = 0.f;
+  const int f = threadIdx.x * 4;
+  if (f < C::L) {
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int s = 0; s < ns; ++s) {
       const float m = a.part_ml[((base + s) * C::H + h) * 2];
-      if (m != -INFINITY) acc += fast_exp2(m - M) * a.part_o[((base + s) * C::H + h) * C::L + f];
+      if (m == -INFINITY) continue;
+      const float wgt = fast_exp2(m - M);
+      const f32x4 v = *(const f32x4*)(a.part_o + ((base + s) * C::H + h) * C::L + f);
+      acc += wgt * v;
     }
-    a.o_latent[((size_t)b * C::H + h) * C::L + f] = acc * inv;
+    *(f32x4*)(a.o_latent + ((size_t)b * C::H + h) * C::L + f) = acc * inv;
   }
   if (threadIdx.x == 0 && a.lse) a.lse[(size_t)b * C::H + h] = (M + __log2f(den)) * 0.6931471805599453f;
 }
@@ -337,14 +344,20 @@ __global__ __launch_bounds__(256) void vup_gate_kernel(const float* __restrict__
   }
 }
 
+hipError_t launch_decode_attention_k3(const DecodeAttnArgs& a, bool gather, hipStream_t st);
+
 template <class S>
 static hipError_t launch_decode_t(const DecodeAttnArgs& a, bool gather, hipStream_t st) {
   const int grid = a.B * a.n_splits;
-  if (gather)
+  if constexpr (S::H == ShapeK3::H) {
+    const hipError_t e = launch_decode_attention_k3(a, gather, st);
+    if (e != hipSuccess) return e;
+  } else if (gather) {
     decode_attn_kernel<S, true><<<grid, 256, 0, st>>>(a);
-  else
+  } else {
     decode_attn_kernel<S, false><<<grid, 256, 0, st>>>(a);
-  decode_merge_kernel<S><<<a.B * S::H, 256, 0, st>>>(a);
+  }
+  decode_merge_kernel<S><<<a.B * S::H, 128, 0, st>>>(a);
   return hipGetLastError();
 }
 

@@ -1,0 +1,238 @@
+// Absorbed (latent-space) decode attention for the K3 layer shape, dense and gathered (DSA).
+//
+// Same computation as decode_attn_kernel (see decode_attn.hip): for every head h of sequence b,
+// scores q~_h . [c_j ; r_j] * scale over the positions of one split, an online softmax, and the
+// unnormalised latent-space output sum_j p_j c_j, with (max, sum) per head for the merge.
+// (K3.1 Gated DSA blog, the note on latent absorption after eq. (10); eq. (9).)
+//
+// Layout of the work on one CU (448 threads = 7 waves):
+// * 32-position tiles of latent rows (32 x 1,152 B) stream from HBM straight into LDS with
+//   global_load_lds_dwordx4 (no staging registers), into a ring of 3 slots, two tiles ahead of
+//   the compute; the three score waves issue them (12 wave-wide loads each per tile, so at most
+//   24 are outstanding per wave). 16-byte chunk c of row r sits at chunk
+//   r*72 + (c ^ swz(r)), which keeps the score MFMA's row reads free of bank conflicts.
+// * waves 0-2 hold q~ for 32 heads each in VGPRs (the B operand of S^T = Lat Q~^T, 36 k-steps
+//   of v_mfma_f32_32x32x16_bf16 over the 576 features) and run the online softmax: lane l owns
+//   head l%32, so max and sum need one xor-32 shuffle. P^T goes to LDS as bf16.
+// * waves 3-6 each accumulate O^T = Lat^T P^T for 128 of the 512 latent features and all 96
+//   heads (192 fp32 accumulators per lane), reading Lat^T from the row-major tile with
+//   ds_read_b64_tr_b16.
+// * The running max is only moved when it grows by more than 8 (base 2): otherwise the old
+//   max stays and the rescale factor is exactly 1, so the accumulators are rarely rescaled.
+//   The result is the same softmax; only the reference point of the exponentials differs.
+#include "common.h"
+#include "kernels.h"
+
+namespace gmla {
+
+namespace k3dec {
+constexpr int H = 96, L = 512, DL = 576;
+constexpr int BT = 32;                        // positions per tile
+constexpr int CH = DL / 8;                    // 72 chunks of 16 bytes per latent row
+constexpr int TILE_BYTES = BT * DL * 2;       // 36,864
+constexpr int NSLOT = 3;
+constexpr int NLOAD = TILE_BYTES / 1024;      // 36 wave-wide 1 KB DMA loads per tile
+constexpr int NLOAD_W = NLOAD / 3;            // issued by each of the 3 score waves
+constexpr int NTHREADS = 7 * 64;
+constexpr int PROW = BT + 8;                  // P^T [head][position] row stride (bf16)
+constexpr int KSD = DL / 16;                  // 36 score k-steps
+constexpr int MAX_SEL = 2048;                 // gathered positions per split (<= top-k)
+constexpr float RESCALE_SLACK = 8.0f;         // base-2 growth of the max before rescaling
+}  // namespace k3dec
+
+__device__ __forceinline__ int swz_row(int r) { return ((r ^ (r >> 2)) & 1) | (r & 2) | ((r >> 1) & 4); }
+
+__device__ __forceinline__ int perm_row_k3(int m) {
+  const int a = m >> 3, g = (m >> 2) & 1, b = m & 3;
+  return 16 * (a >> 1) + 8 * g + 4 * (a & 1) + b;
+}
+
+template <bool GATHER>
+__global__ __launch_bounds__(k3dec::NTHREADS) void decode_attn_k3_kernel(DecodeAttnArgs a) {
+  using namespace k3dec;
+  __shared__ __attribute__((aligned(1024))) uint8_t lat_s[NSLOT][TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) uint16_t Ps[H * PROW];
+  __shared__ float alpha_s[H];
+  __shared__ int sel_s[GATHER ? MAX_SEL : 1];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g2 = lane >> 5, l32 = lane & 31;
+  const int b = blockIdx.x / a.n_splits, split = blockIdx.x % a.n_splits;
+  const int n_vis = GATHER ? min(a.sel_cnt[b], a.sel_stride) : min(a.n_vis[b] + a.vis_offset, a.T_cap);
+  const int p0 = split * a.chunk;
+  const int p1 = min(p0 + a.chunk, n_vis);
+  const int n_pos = GATHER ? min(max(p1 - p0, 0), MAX_SEL) : max(p1 - p0, 0);
+  const int n_tiles = (n_pos + BT - 1) / BT;
+  const uint16_t* lat = a.latent + (size_t)b * a.T_cap * DL;
+
+  if (GATHER) {  // this split's selected positions, clamped into the cache
+    const int32_t* sel = a.sel_idx + (size_t)b * a.sel_stride;
+    for (int i = tid; i < n_pos; i += NTHREADS) {
+      const int p = sel[p0 + i];
+      sel_s[i] = (p >= 0 && p < a.T_cap) ? p : 0;
+    }
+    __syncthreads();
+  }
+
+  // ---- tile loads, issued by the score waves (wave w takes loads 12w .. 12w+11) ----
+  const int pw = wave - 3;
+  auto issue = [&](int t) {
+    if (t >= n_tiles) return;
+    uint8_t* slot = lat_s[t % NSLOT];
+    const int j0 = t * BT;  // relative to p0
+#pragma unroll 1
+    for (int k = 0; k < NLOAD_W; ++k) {
+      const int i = wave * NLOAD_W + k;
+      const int P = i * 64 + lane;  // destination chunk of this lane
+      const int r = P / CH, cs = P - r * CH;
+      const int c = cs ^ swz_row(r);
+      const int jr = min(j0 + r, n_pos - 1);  // rows past the end repeat a valid row (masked)
+      const int pos = GATHER ? sel_s[jr] : p0 + jr;
+      const uint16_t* src = lat + (size_t)pos * DL + c * 8;
+      __builtin_amdgcn_global_load_lds(src, (GMLA_LDS void*)(slot + i * 1024), 16, 0, 0);
+    }
+  };
+  const float sl2 = a.scale * 1.4426950408889634f;
+  const size_t part = (size_t)b * a.n_splits + split;
+
+  // The two roles run separate loops with the same barriers (two per tile), so that the score
+  // waves' q~ registers and the P.V waves' accumulators are never live in the same code.
+  if (wave < 3) {
+    // ---------------- score waves: heads wave*32 + l32 ----------------
+    const int head = wave * 32 + l32;
+    u32x4 qf[KSD];
+    const uint16_t* qrow = a.q_tilde + ((size_t)b * H + head) * DL + g2 * 8;
+#pragma unroll
+    for (int s = 0; s < KSD; ++s) qf[s] = ld16(qrow + s * 16);
+    const int srow = perm_row_k3(l32);
+    const int srow_base = srow * CH * 16;
+    const int srow_swz = swz_row(srow);
+    float m_run = -INFINITY, l_run = 0.f;
+    issue(0);
+    issue(1);
+    if (n_tiles > 1)
+      asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();  // tile 0 is in LDS
+    for (int t = 0; t < n_tiles; ++t) {
+      const uint8_t* slot = lat_s[t % NSLOT];
+      issue(t + 2);
+      f32x16 sacc = f32x16{};
+#pragma unroll
+      for (int s = 0; s < KSD; ++s) {
+        const int c = (2 * s + g2) ^ srow_swz;
+        sacc = mfma32(*(const u32x4*)(slot + srow_base + c * 16), qf[s], sacc);
+      }
+      const int jbase = t * BT;
+      float mt = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int j = jbase + 16 * (r >> 3) + 8 * g2 + (r & 7);
+        const float x = (j < n_pos) ? sacc[r] * sl2 : -INFINITY;
+        sacc[r] = x;
+        mt = fmaxf(mt, x);
+      }
+      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+      float alpha = 1.f;
+      if (mt > m_run + RESCALE_SLACK || m_run == -INFINITY) {
+        alpha = fast_exp2(m_run - mt);  // 0 on the first tile
+        m_run = mt;
+      }
+      float ls = 0.f;
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        float p[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          p[i] = fast_exp2(sacc[hh * 8 + i] - m_run);
+          ls += p[i];
+        }
+        st16(&Ps[head * PROW + hh * 16 + g2 * 8],
+             u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
+                   pack_bf16x2(p[6], p[7])});
+      }
+      l_run = l_run * alpha + ls;
+      if (g2 == 0) alpha_s[head] = alpha;
+      __syncthreads();  // P and alpha of tile t are ready
+      if (t + 2 < n_tiles)
+        asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();  // tile t is consumed; tile t+1 is in LDS
+    }
+    const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+    if (g2 == 0) {
+      a.part_ml[(part * H + head) * 2 + 0] = m_run;
+      a.part_ml[(part * H + head) * 2 + 1] = l_tot;
+    }
+  } else {
+    // ---------------- P.V waves: latent features [pw*128, pw*128 + 128) ----------------
+    const int G = lane >> 4, jj = lane & 15;
+    f32x16 o[4][3];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 3; ++j) o[i][j] = f32x16{};
+    __syncthreads();  // tile 0 is in LDS
+    for (int t = 0; t < n_tiles; ++t) {
+      const uint8_t* slot = lat_s[t % NSLOT];
+      __syncthreads();  // P and alpha of tile t are ready
+      float al[3];
+      u32x4 pb[3][2];
+#pragma unroll
+      for (int hs = 0; hs < 3; ++hs) {
+        al[hs] = alpha_s[hs * 32 + l32];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) pb[hs][ks] = ld16(&Ps[(hs * 32 + l32) * PROW + ks * 16 + g2 * 8]);
+      }
+#pragma unroll
+      for (int hs = 0; hs < 3; ++hs) {
+        if (__any(al[hs] != 1.f)) {
+#pragma unroll
+          for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) o[dt][hs][r] *= al[hs];
+        }
+      }
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        const int fcol = (pw * 4 + dt) * 32 + 16 * (G & 1) + 4 * (jj & 3);
+        const int c = fcol >> 3, off = (fcol & 7) * 2;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const int r0 = ks * 16 + 8 * (G >> 1) + (jj >> 2), r1 = r0 + 4;
+          const u32x2 lo = lds_read_tr16(slot + (r0 * CH + (c ^ swz_row(r0))) * 16 + off);
+          const u32x2 hi = lds_read_tr16(slot + (r1 * CH + (c ^ swz_row(r1))) * 16 + off);
+          const u32x4 af = u32x4{lo.x, lo.y, hi.x, hi.y};
+#pragma unroll
+          for (int hs = 0; hs < 3; ++hs) o[dt][hs] = mfma32(af, pb[hs][ks], o[dt][hs]);
+        }
+      }
+      __syncthreads();  // tile t is consumed; tile t+1 is in LDS
+    }
+#pragma unroll
+    for (int hs = 0; hs < 3; ++hs) {
+      float* dst = a.part_o + (part * H + hs * 32 + l32) * L;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) {
+          const int f = (pw * 4 + dt) * 32 + rb * 8 + g2 * 4;
+          *(f32x4*)(dst + f) = f32x4{o[dt][hs][rb * 4 + 0], o[dt][hs][rb * 4 + 1], o[dt][hs][rb * 4 + 2],
+                                     o[dt][hs][rb * 4 + 3]};
+        }
+    }
+  }
+}
+
+hipError_t launch_decode_attention_k3(const DecodeAttnArgs& a, bool gather, hipStream_t st) {
+  const int grid = a.B * a.n_splits;
+  if (gather)
+    decode_attn_k3_kernel<true><<<grid, k3dec::NTHREADS, 0, st>>>(a);
+  else
+    decode_attn_k3_kernel<false><<<grid, k3dec::NTHREADS, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace gmla
