@@ -23,14 +23,14 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
   return __uint_as_float(((uint32_t)b) << 16);
 }
-__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
-// two floats -> packed bf16 pair (lo in bits 0..15)
+typedef float f32x2_ __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_ __attribute__((ext_vector_type(2)));
+// two floats -> packed bf16 pair (lo in bits 0..15): one v_cvt_pk_bf16_f32 on gfx950
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_{lo, hi}, bf16x2_));
+}
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  return (uint16_t)(pack_bf16x2(f, 0.f) & 0xFFFFu);
 }
 __device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
@@ -63,6 +63,33 @@ __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
 __device__ __forceinline__ u32x2 lds_read_tr16(const void* p) {
   i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((GMLA_LDS i16x4*)(p));
   return __builtin_bit_cast(u32x2, v);
+}
+
+// One wave-wide global_load_lds_dwordx4: lane L's 16 bytes from `gsrc` land in LDS at
+// lds_byte_addr + 16*L (which must be the same in every lane). Issued from inline asm so that the compiler does not place a blanket
+// vmcnt(0) wait in front of every later LDS read (it cannot tell LDS-DMA destinations apart);
+// callers wait on vmcnt themselves before the data is read.
+__device__ __forceinline__ void lds_dma16(const void* gsrc, uint32_t lds_byte_addr) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off"
+      :
+      : "s"(__builtin_amdgcn_readfirstlane(lds_byte_addr)), "v"(gsrc)
+      : "memory", "m0");
+}
+// As lds_dma16, with the source at sbase (wave-uniform, kept in SGPRs) + voff bytes (per lane).
+__device__ __forceinline__ void lds_dma16_sbase(uint32_t voff, const void* sbase, uint32_t lds_byte_addr) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2"
+      :
+      : "s"(__builtin_amdgcn_readfirstlane(lds_byte_addr)), "v"(voff), "s"(sbase)
+      : "memory", "m0");
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(GMLA_LDS const void*)p;
 }
 
 // ---------------------------------------------------------------------------------------

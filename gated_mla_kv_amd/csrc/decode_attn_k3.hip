@@ -5,12 +5,14 @@
 // unnormalised latent-space output sum_j p_j c_j, with (max, sum) per head for the merge.
 // (K3.1 Gated DSA blog, the note on latent absorption after eq. (10); eq. (9).)
 //
-// Layout of the work on one CU (448 threads = 7 waves):
+// Layout of the work on one CU (448 threads = 7 waves), software-pipelined by tile:
 // * 32-position tiles of latent rows (32 x 1,152 B) stream from HBM straight into LDS with
-//   global_load_lds_dwordx4 (no staging registers), into a ring of 3 slots, two tiles ahead of
-//   the compute; the three score waves issue them (12 wave-wide loads each per tile, so at most
-//   24 are outstanding per wave). 16-byte chunk c of row r sits at chunk
-//   r*72 + (c ^ swz(r)), which keeps the score MFMA's row reads free of bank conflicts.
+//   global_load_lds_dwordx4 (no staging registers) into a ring of NSLOT slots (4 dense, 3 when
+//   gathering); the four P.V waves issue them (9 wave-wide loads each per tile), NSLOT-1 tiles
+//   ahead of the tile they consume. 16-byte chunk c of row r sits at chunk r*72 + (c ^ swz(r)),
+//   which keeps the score MFMA's row reads free of bank conflicts.
+// * In step t the score waves work on tile t+1 while the P.V waves consume tile t, with P^T and
+//   the rescale factors double-buffered: one barrier per tile.
 // * waves 0-2 hold q~ for 32 heads each in VGPRs (the B operand of S^T = Lat Q~^T, 36 k-steps
 //   of v_mfma_f32_32x32x16_bf16 over the 576 features) and run the online softmax: lane l owns
 //   head l%32, so max and sum need one xor-32 shuffle. P^T goes to LDS as bf16.
@@ -30,9 +32,8 @@ constexpr int H = 96, L = 512, DL = 576;
 constexpr int BT = 32;                        // positions per tile
 constexpr int CH = DL / 8;                    // 72 chunks of 16 bytes per latent row
 constexpr int TILE_BYTES = BT * DL * 2;       // 36,864
-constexpr int NSLOT = 3;
 constexpr int NLOAD = TILE_BYTES / 1024;      // 36 wave-wide 1 KB DMA loads per tile
-constexpr int NLOAD_W = NLOAD / 3;            // issued by each of the 3 score waves
+constexpr int NLOAD_W = NLOAD / 4;            // issued by each of the 4 P.V waves
 constexpr int NTHREADS = 7 * 64;
 constexpr int PROW = BT + 8;                  // P^T [head][position] row stride (bf16)
 constexpr int KSD = DL / 16;                  // 36 score k-steps
@@ -47,12 +48,23 @@ __device__ __forceinline__ int perm_row_k3(int m) {
   return 16 * (a >> 1) + 8 * g + 4 * (a & 1) + b;
 }
 
+// vmcnt wait leaving at most `tiles` of this wave's most recent tile loads (9 each) in flight.
+__device__ __forceinline__ void wait_tiles_in_flight(int tiles) {
+  if (tiles >= 2)
+    asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
+  else if (tiles == 1)
+    asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
 template <bool GATHER>
 __global__ __launch_bounds__(k3dec::NTHREADS) void decode_attn_k3_kernel(DecodeAttnArgs a) {
   using namespace k3dec;
+  constexpr int NSLOT = GATHER ? 3 : 4;
   __shared__ __attribute__((aligned(1024))) uint8_t lat_s[NSLOT][TILE_BYTES];
-  __shared__ __attribute__((aligned(16))) uint16_t Ps[H * PROW];
-  __shared__ float alpha_s[H];
+  __shared__ __attribute__((aligned(16))) uint16_t Ps[2][H * PROW];
+  __shared__ float alpha_s[2][H];
   __shared__ int sel_s[GATHER ? MAX_SEL : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -74,29 +86,11 @@ __global__ __launch_bounds__(k3dec::NTHREADS) void decode_attn_k3_kernel(DecodeA
     __syncthreads();
   }
 
-  // ---- tile loads, issued by the score waves (wave w takes loads 12w .. 12w+11) ----
-  const int pw = wave - 3;
-  auto issue = [&](int t) {
-    if (t >= n_tiles) return;
-    uint8_t* slot = lat_s[t % NSLOT];
-    const int j0 = t * BT;  // relative to p0
-#pragma unroll 1
-    for (int k = 0; k < NLOAD_W; ++k) {
-      const int i = wave * NLOAD_W + k;
-      const int P = i * 64 + lane;  // destination chunk of this lane
-      const int r = P / CH, cs = P - r * CH;
-      const int c = cs ^ swz_row(r);
-      const int jr = min(j0 + r, n_pos - 1);  // rows past the end repeat a valid row (masked)
-      const int pos = GATHER ? sel_s[jr] : p0 + jr;
-      const uint16_t* src = lat + (size_t)pos * DL + c * 8;
-      __builtin_amdgcn_global_load_lds(src, (GMLA_LDS void*)(slot + i * 1024), 16, 0, 0);
-    }
-  };
   const float sl2 = a.scale * 1.4426950408889634f;
   const size_t part = (size_t)b * a.n_splits + split;
 
-  // The two roles run separate loops with the same barriers (two per tile), so that the score
-  // waves' q~ registers and the P.V waves' accumulators are never live in the same code.
+  // The two roles run separate code with the same barriers, so that the score waves' q~
+  // registers and the P.V waves' accumulators are never live at the same point.
   if (wave < 3) {
     // ---------------- score waves: heads wave*32 + l32 ----------------
     const int head = wave * 32 + l32;
@@ -104,25 +98,28 @@ __global__ __launch_bounds__(k3dec::NTHREADS) void decode_attn_k3_kernel(DecodeA
     const uint16_t* qrow = a.q_tilde + ((size_t)b * H + head) * DL + g2 * 8;
 #pragma unroll
     for (int s = 0; s < KSD; ++s) qf[s] = ld16(qrow + s * 16);
+    // use q~ here, so that its loads are waited for once, before the loop
+#pragma unroll
+    for (int s = 0; s < KSD; ++s) asm volatile("" ::"v"(qf[s]));
     const int srow = perm_row_k3(l32);
     const int srow_base = srow * CH * 16;
     const int srow_swz = swz_row(srow);
     float m_run = -INFINITY, l_run = 0.f;
-    issue(0);
-    issue(1);
-    if (n_tiles > 1)
-      asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
-    else
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();  // tile 0 is in LDS
-    for (int t = 0; t < n_tiles; ++t) {
-      const uint8_t* slot = lat_s[t % NSLOT];
-      issue(t + 2);
+
+    // scores, online-softmax statistics and P^T of tile t into buffer t%2
+    auto score_tile = [&](int t) {
+      const uint8_t* arow = lat_s[t % NSLOT] + srow_base;
+      constexpr int PF = 8;  // LDS reads run PF k-steps ahead of their MFMA
+      u32x4 ar[PF];
+#pragma unroll
+      for (int s = 0; s < PF; ++s) ar[s] = *(const u32x4*)(arow + (((2 * s + g2) ^ srow_swz) << 4));
       f32x16 sacc = f32x16{};
 #pragma unroll
       for (int s = 0; s < KSD; ++s) {
-        const int c = (2 * s + g2) ^ srow_swz;
-        sacc = mfma32(*(const u32x4*)(slot + srow_base + c * 16), qf[s], sacc);
+        const u32x4 cur = ar[s % PF];
+        if (s + PF < KSD) ar[s % PF] = *(const u32x4*)(arow + (((2 * (s + PF) + g2) ^ srow_swz) << 4));
+        __builtin_amdgcn_sched_barrier(0);
+        sacc = mfma32(cur, qf[s], sacc);
       }
       const int jbase = t * BT;
       float mt = -INFINITY;
@@ -140,6 +137,7 @@ __global__ __launch_bounds__(k3dec::NTHREADS) void decode_attn_k3_kernel(DecodeA
         m_run = mt;
       }
       float ls = 0.f;
+      uint16_t* prow = Ps[t & 1] + head * PROW + g2 * 8;
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
         float p[8];
@@ -148,18 +146,19 @@ __global__ __launch_bounds__(k3dec::NTHREADS) void decode_attn_k3_kernel(DecodeA
           p[i] = fast_exp2(sacc[hh * 8 + i] - m_run);
           ls += p[i];
         }
-        st16(&Ps[head * PROW + hh * 16 + g2 * 8],
-             u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
-                   pack_bf16x2(p[6], p[7])});
+        st16(prow + hh * 16, u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
+                                   pack_bf16x2(p[6], p[7])});
       }
       l_run = l_run * alpha + ls;
-      if (g2 == 0) alpha_s[head] = alpha;
-      __syncthreads();  // P and alpha of tile t are ready
-      if (t + 2 < n_tiles)
-        asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
-      else
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();  // tile t is consumed; tile t+1 is in LDS
+      if (g2 == 0) alpha_s[t & 1][head] = alpha;
+    };
+
+    __syncthreads();  // tile 0 is in LDS
+    if (n_tiles > 0) score_tile(0);
+    __syncthreads();  // P of tile 0 is ready; tile 1 is in LDS
+    for (int t = 0; t < n_tiles; ++t) {
+      if (t + 1 < n_tiles) score_tile(t + 1);
+      __syncthreads();
     }
     const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
     if (g2 == 0) {
@@ -168,6 +167,44 @@ __global__ __launch_bounds__(k3dec::NTHREADS) void decode_attn_k3_kernel(DecodeA
     }
   } else {
     // ---------------- P.V waves: latent features [pw*128, pw*128 + 128) ----------------
+    const int pw = wave - 3;
+    // Per-lane source offsets (bytes from the tile's first row) of this wave's 9 loads, with the
+    // row in the top bits for the clamped path: chunk P = i*64 + lane of the tile is row P/72,
+    // swizzled chunk (P%72) ^ swz(row).
+    uint32_t doff[NLOAD_W];
+#pragma unroll
+    for (int k = 0; k < NLOAD_W; ++k) {
+      const int P = (pw * NLOAD_W + k) * 64 + lane;
+      const int r = P / CH, c = (P - r * CH) ^ swz_row(r);
+      doff[k] = (uint32_t)(r * DL * 2 + c * 16) | ((uint32_t)r << 16);
+    }
+    auto issue = [&](int t) {  // this wave's 9 of the 36 DMA loads of tile t
+      if (t >= n_tiles) return;
+      const uint32_t slot_addr = lds_addr(lat_s[t % NSLOT]);
+      const int j0 = t * BT;
+      if (!GATHER && j0 + BT <= n_pos) {  // whole tile of consecutive rows: offsets only
+        const char* base = (const char*)(lat + (size_t)(p0 + j0) * DL);
+#pragma unroll
+        for (int k = 0; k < NLOAD_W; ++k)
+          lds_dma16_sbase(doff[k] & 0xFFFFu, base, slot_addr + (pw * NLOAD_W + k) * 1024);
+        return;
+      }
+#pragma unroll 1
+      for (int k = 0; k < NLOAD_W; ++k) {
+        const int i = pw * NLOAD_W + k;
+        const int P = i * 64 + lane;  // destination chunk of this lane
+        const int r = P / CH, cs = P - r * CH;
+        const int c = cs ^ swz_row(r);
+        const int jr = min(j0 + r, n_pos - 1);  // rows past the end repeat a valid row (masked)
+        const int pos = GATHER ? sel_s[jr] : p0 + jr;
+        lds_dma16(lat + (size_t)pos * DL + c * 8, slot_addr + i * 1024);
+      }
+    };
+    // tiles issued so far are [0, issued); wait until tile `need` has landed
+    auto wait_for = [&](int need, int issued) { wait_tiles_in_flight(max(0, issued - 1 - need)); };
+    int issued = min(n_tiles, NSLOT - 1);
+    for (int t = 0; t < issued; ++t) issue(t);
+    wait_for(0, issued);
     const int G = lane >> 4, jj = lane & 15;
     f32x16 o[4][3];
 #pragma unroll
@@ -175,17 +212,15 @@ __global__ __launch_bounds__(k3dec::NTHREADS) void decode_attn_k3_kernel(DecodeA
 #pragma unroll
       for (int j = 0; j < 3; ++j) o[i][j] = f32x16{};
     __syncthreads();  // tile 0 is in LDS
+    if (n_tiles > 1) wait_for(1, issued);
+    __syncthreads();  // P of tile 0 is ready; tile 1 is in LDS
     for (int t = 0; t < n_tiles; ++t) {
+      if (issued < n_tiles) issue(issued++);  // tile t + NSLOT - 1, into the slot tile t-1 used
       const uint8_t* slot = lat_s[t % NSLOT];
-      __syncthreads();  // P and alpha of tile t are ready
+      const uint16_t* pbuf = Ps[t & 1];
       float al[3];
-      u32x4 pb[3][2];
 #pragma unroll
-      for (int hs = 0; hs < 3; ++hs) {
-        al[hs] = alpha_s[hs * 32 + l32];
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) pb[hs][ks] = ld16(&Ps[(hs * 32 + l32) * PROW + ks * 16 + g2 * 8]);
-      }
+      for (int hs = 0; hs < 3; ++hs) al[hs] = alpha_s[t & 1][hs * 32 + l32];
 #pragma unroll
       for (int hs = 0; hs < 3; ++hs) {
         if (__any(al[hs] != 1.f)) {
@@ -196,20 +231,24 @@ __global__ __launch_bounds__(k3dec::NTHREADS) void decode_attn_k3_kernel(DecodeA
         }
       }
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
-        const int fcol = (pw * 4 + dt) * 32 + 16 * (G & 1) + 4 * (jj & 3);
-        const int c = fcol >> 3, off = (fcol & 7) * 2;
+      for (int ks = 0; ks < 2; ++ks) {
+        u32x4 pb[3];
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const int r0 = ks * 16 + 8 * (G >> 1) + (jj >> 2), r1 = r0 + 4;
+        for (int hs = 0; hs < 3; ++hs) pb[hs] = ld16(pbuf + (hs * 32 + l32) * PROW + ks * 16 + g2 * 8);
+        const int r0 = ks * 16 + 8 * (G >> 1) + (jj >> 2), r1 = r0 + 4;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          const int fcol = (pw * 4 + dt) * 32 + 16 * (G & 1) + 4 * (jj & 3);
+          const int c = fcol >> 3, off = (fcol & 7) * 2;
           const u32x2 lo = lds_read_tr16(slot + (r0 * CH + (c ^ swz_row(r0))) * 16 + off);
           const u32x2 hi = lds_read_tr16(slot + (r1 * CH + (c ^ swz_row(r1))) * 16 + off);
           const u32x4 af = u32x4{lo.x, lo.y, hi.x, hi.y};
 #pragma unroll
-          for (int hs = 0; hs < 3; ++hs) o[dt][hs] = mfma32(af, pb[hs][ks], o[dt][hs]);
+          for (int hs = 0; hs < 3; ++hs) o[dt][hs] = mfma32(af, pb[hs], o[dt][hs]);
         }
       }
-      __syncthreads();  // tile t is consumed; tile t+1 is in LDS
+      if (t + 2 < n_tiles) wait_for(t + 2, issued);  // the score waves read it in the next step
+      __syncthreads();
     }
 #pragma unroll
     for (int hs = 0; hs < 3; ++hs) {
