@@ -152,7 +152,7 @@ def main():
     ua = torch.empty((1, T, H * d.d_v), dtype=torch.bfloat16, device=dev)
     stages["prefill_attention"] = (lambda: gm.mla_prefill_attention(L.dims, qa, cache.c, start, T, 1, T, gpre, ua,
                                                                     gm.OUT_BF16, None),
-                                   attn_fl, "prefill_attn_kernel")
+                                   attn_fl, "prefill_attn_k3_kernel")
     stage_ms = {}
     for name, (fn, fl, kern) in stages.items():
         fn()

@@ -25,7 +25,8 @@ FLAGS = [
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
     "-Wno-unused-command-line-argument",
 ]
-SOURCES = ["api.cpp", "gemm.hip", "norm_append.hip", "prefill_attn.hip", "decode_attn.hip",
+SOURCES = ["api.cpp", "gemm.hip", "norm_append.hip", "prefill_attn.hip", "prefill_attn_k3.hip",
+           "decode_attn.hip",
            "decode_attn_k3.hip", "dsa_expanded.hip"]
 
 

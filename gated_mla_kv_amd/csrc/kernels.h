@@ -42,6 +42,7 @@ struct PrefillAttnArgs {
   float scale;             // softmax scale
 };
 hipError_t launch_prefill_attention(Shape s, const PrefillAttnArgs& a, hipStream_t st);
+hipError_t launch_prefill_attention_k3(const PrefillAttnArgs& a, hipStream_t st);
 
 struct DecodeAttnArgs {
   const uint16_t* q_tilde;  // [B, H, L+DS]

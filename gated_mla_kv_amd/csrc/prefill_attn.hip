@@ -247,7 +247,7 @@ static hipError_t launch_prefill_t(const PrefillAttnArgs& a, hipStream_t st) {
 
 hipError_t launch_prefill_attention(Shape s, const PrefillAttnArgs& a, hipStream_t st) {
   if (a.B <= 0 || a.T <= 0) return hipSuccess;
-  if (s == Shape::K3) return launch_prefill_t<ShapeK3, 4>(a, st);
+  if (s == Shape::K3) return launch_prefill_attention_k3(a, st);
   return launch_prefill_t<ShapeTiny, 4>(a, st);
 }
 

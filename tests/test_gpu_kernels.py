@@ -116,6 +116,7 @@ def test_kv_append_bit_exact(dims, with_idx):
 # ---------------------------------------------------------------------------------------------
 
 @pytest.mark.parametrize("dims,B,T,starts", [(K3, 1, 64, [0]), (K3, 2, 200, [0, 37]), (K3, 1, 300, [129]),
+                                             (K3, 1, 1000, [300]), (K3, 2, 520, [0, 700]),
                                              (TINY, 1, 64, [0]), (TINY, 2, 70, [5, 0])])
 def test_prefill_attention(dims, B, T, starts):
     d = dims
