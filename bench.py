@@ -134,19 +134,19 @@ def main():
     out_x = torch.empty((M, w_x.shape[0]), dtype=torch.float32, device=dev)
     stages["x_proj_gemm"] = (lambda: gm.mla_gemm(xa, d.hidden, w_x, M, w_x.shape[0], d.hidden, out_x,
                                                  w_x.shape[0], gm.OUT_F32),
-                             2 * M * d.hidden * w_x.shape[0], "gemm_nt_big")
+                             2 * M * d.hidden * w_x.shape[0], "gemm_nt_dma")
     cq = torch.randn((M, d.q_lora), device=dev).to(torch.bfloat16)
     qb = torch.empty((M, H * d.d_qk), dtype=torch.bfloat16, device=dev)
     stages["q_b_gemm"] = (lambda: gm.mla_gemm(cq, d.q_lora, L.w["w_q_b"], M, H * d.d_qk, d.q_lora, qb, H * d.d_qk),
-                          2 * M * d.q_lora * H * d.d_qk, "gemm_nt_big")
+                          2 * M * d.q_lora * H * d.d_qk, "gemm_nt_dma")
     c = torch.randn((M, d.kv_lora), device=dev).to(torch.bfloat16)
     kvb = torch.empty((M, H * (d.d_nope + d.d_v)), dtype=torch.bfloat16, device=dev)
     stages["kv_b_gemm"] = (lambda: gm.mla_gemm(c, d.kv_lora, L.w["w_kv_b"], M, H * 256, d.kv_lora, kvb, H * 256),
-                           2 * M * d.kv_lora * H * 256, "gemm_nt_big")
+                           2 * M * d.kv_lora * H * 256, "gemm_nt_dma")
     u = torch.randn((M, H * d.d_v), device=dev).to(torch.bfloat16)
     yo = torch.empty((M, d.hidden), dtype=torch.bfloat16, device=dev)
     stages["o_proj_gemm"] = (lambda: gm.mla_gemm(u, H * d.d_v, L.w["w_o"], M, d.hidden, H * d.d_v, yo, d.hidden),
-                             2 * M * H * d.d_v * d.hidden, "gemm_nt_big")
+                             2 * M * H * d.d_v * d.hidden, "gemm_nt_dma")
     qa = (torch.randn((1, T, H, d.d_qk), device=dev) * 0.8).to(torch.bfloat16)
     gpre = torch.randn((1, T, H * d.d_v), device=dev)
     ua = torch.empty((1, T, H * d.d_v), dtype=torch.bfloat16, device=dev)
@@ -214,7 +214,7 @@ def main():
         decode = {"workload": "K3 absorbed decode attention, B=32, cache T=8192 (8193 visible), bf16 latent",
                   "kv_bytes": kv_bytes, "us": round(t_cold * 1e3, 2), "us_hot_cache": round(median(hot) * 1e3, 2),
                   "value": round(gbs, 1), "unit": "GB/s",
-                  "roofline": {"kernel": "decode_attn_kernel+decode_merge_kernel", "bound": "hbm",
+                  "roofline": {"kernel": "decode_attn_k3_kernel+decode_merge_kernel", "bound": "hbm",
                                "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None},
                   "mla_decode_step_us": round(t_step * 1e3, 2)}

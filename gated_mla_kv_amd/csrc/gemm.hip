@@ -3,7 +3,9 @@
 // Weights are nn.Linear [out, in] matrices, so both operands are K-contiguous and feed the
 // bf16 MFMA directly (v_mfma_f32_32x32x16_bf16, fp32 accumulation).
 //
-// * gemm_nt_big: M >= 64 (prefill). 256 threads, a BM x BN tile per workgroup, BK = 64,
+// * gemm_nt_dma: M > 128 with K % 64 == 0 (prefill). 256 x 256 tiles, operands copied straight
+//   into LDS by global_load_lds, two waves per SIMD, LDS-staged row-contiguous epilogue.
+// * gemm_nt_big: the other M > 32 shapes. 256 threads, a BM x BN tile per workgroup, BK = 64,
 //   double-buffered LDS tiles with a 144-byte row stride (conflict-free 16-byte reads over 16
 //   consecutive rows), workgroup ids remapped so that each XCD walks a contiguous, M-grouped
 //   range of tiles (operands reused from that XCD's L2).
@@ -173,6 +175,256 @@ __global__ __launch_bounds__(256) void gemm_nt_big(GemmArgs g) {
 }
 
 // ----------------------------------------------------------------------------------------
+// Large-M kernel with LDS-DMA operand staging (M > 128, K % BK == 0)
+//
+// 256 x 256 output tile per workgroup, NWV waves (8: two per SIMD, 128 x 64 each). BK-wide K slabs
+// of x and W are copied HBM/L2 -> LDS by global_load_lds_dwordx4 (no register staging) into an
+// NST-stage ring, NST - 1 slabs ahead of the MFMAs, one barrier per slab. Only one wave per SIMD
+// issues the copies, so its partner's MFMAs cover the issue time.
+// LDS rows are 2*BK bytes; 16-byte chunk c of row r sits at position c ^ f(r), with f chosen so
+// that the fragment reads (32 consecutive rows, one chunk each) are free of bank conflicts
+// whether the LDS serves 8 or 16 lanes per cycle:
+//   BK = 64 (8 chunks): f(r) = (r & 7) ^ ((r >> 3) & 1)
+//   BK = 32 (4 chunks): f(r) = ((r >> 1) ^ (r >> 3)) & 3
+// The MFMA A operand is the weight tile, so each lane ends with 4 consecutive output columns of
+// one row: the epilogue stores 16 bytes (fp32) or 8 bytes (bf16) per lane and register group.
+// ----------------------------------------------------------------------------------------
+template <int BK_, int NST_, int NWV_>
+struct GdCfg {
+  static constexpr int BM = 256, BN = 256, BK = BK_, NST = NST_, NWV = NWV_;
+  static constexpr int NIW = 4;  // waves that issue the copies (one per SIMD)
+  static constexpr int WN = 128, WM = 256 * 256 / NWV / WN;  // per-wave tile (n x m)
+  static constexpr int TI = WN / 32, TJ = WM / 32;
+  static constexpr int ROWB = BK * 2, CPR = BK / 8, RPL = 1024 / ROWB;  // chunks per row, rows per 1 KB load
+  static constexpr int ABYTES = BM * ROWB, STAGE = 2 * ABYTES;
+  static constexpr int LOADS_W = ABYTES / 1024 / NIW;  // DMA loads per issuing wave per operand per slab
+  static constexpr int LPW = 2 * LOADS_W;             // per issuing wave per slab
+  static constexpr int PITCH = 68;                    // epilogue staging row pitch (floats)
+  static constexpr int LDS_BYTES = NST * STAGE > NWV * WM * PITCH * 4 ? NST * STAGE : NWV * WM * PITCH * 4;
+  static constexpr int KSUB = BK / 16;
+  static_assert(NST * STAGE <= 160 * 1024, "LDS");
+  static_assert((NST - 1) * LPW <= 63, "vmcnt range");
+};
+
+template <int BK>
+__device__ __forceinline__ int gd_swz(int r) {
+  if constexpr (BK == 64)
+    return (r & 7) ^ ((r >> 3) & 1);
+  else
+    return ((r >> 1) ^ (r >> 3)) & 3;
+}
+
+// wait until at most n slabs of this wave's copies (LPW loads each) are still in flight
+template <int LPW>
+__device__ __forceinline__ void gd_wait_slabs(int n) {
+  if (n >= 3) {
+    if constexpr (3 * LPW <= 63) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * LPW) : "memory");
+  } else if (n == 2) {
+    if constexpr (2 * LPW <= 63) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * LPW) : "memory");
+  } else if (n == 1) {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LPW) : "memory");
+  } else {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+}
+
+template <int BK, int NST, int NWV>
+__global__ __launch_bounds__(NWV * 64) void gemm_nt_dma(GemmArgs g) {
+  using C = GdCfg<BK, NST, NWV>;
+  constexpr int WM = C::WM, TI = C::TI, TJ = C::TJ;
+  constexpr int BM = C::BM, BN = C::BN, ROWB = C::ROWB, CPR = C::CPR, RPL = C::RPL;
+  constexpr int ABYTES = C::ABYTES, STAGE = C::STAGE, LOADS_W = C::LOADS_W, LPW = C::LPW;
+  constexpr int KSUB = C::KSUB, NIW = C::NIW, PITCH = C::PITCH;
+  static_assert(NST - 2 <= 3, "gd_wait_slabs covers up to three slabs");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS_BYTES];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int tiles_m = cdiv(g.M, BM), tiles_n = cdiv(g.N, BN);
+  const int pid = xcd_contiguous(blockIdx.x, tiles_m * tiles_n);
+  constexpr int GROUP = 8;
+  const int in_group = GROUP * tiles_n;
+  const int first_m = (pid / in_group) * GROUP;
+  const int gsize = min(tiles_m - first_m, GROUP);
+  const int tile_m = first_m + (pid % in_group) % gsize;
+  const int tile_n = (pid % in_group) / gsize;
+  const int m0 = tile_m * BM, n0 = tile_n * BN;
+
+  // ---- DMA: load i of an operand fills rows RPL*i .. RPL*i + RPL-1 of its region; lane L writes
+  // row RPL*i + L/CPR at position L%CPR, i.e. logical chunk (L%CPR) ^ f(row). f(RPL*i + x)
+  // depends on i only through its parity. Waves 0..NIW-1 (one per SIMD) issue the copies, wave w
+  // loads w*LOADS_W .. +LOADS_W-1; their partner waves keep the SIMD's matrix core busy meanwhile.
+  const int iw = wave < NIW ? wave : 0;  // loads computed for the partner waves go unused
+  const int lr = lane / CPR;
+  int coff[2];
+#pragma unroll
+  for (int p = 0; p < 2; ++p) coff[p] = (lane % CPR) ^ gd_swz<BK>(RPL * p + lr);
+  uint32_t aoffs[LOADS_W];  // x rows clamped to M - 1 (rows past M are computed, never stored)
+#pragma unroll
+  for (int k = 0; k < LOADS_W; ++k) {
+    const int i = iw * LOADS_W + k;
+    const int row = min(RPL * i + lr, g.M - 1 - m0);
+    aoffs[k] = (uint32_t)(row * g.lda * 2 + (coff[i & 1] << 4));
+  }
+  uint32_t woff[2];
+#pragma unroll
+  for (int p = 0; p < 2; ++p) woff[p] = (uint32_t)(lr * g.K * 2 + (coff[p] << 4));
+  const uint8_t* abase = (const uint8_t*)g.a + (size_t)m0 * g.lda * 2;
+  const uint8_t* wbase[LOADS_W];  // weight rows n0 + RPL*i (segments start at multiples of RPL)
+#pragma unroll
+  for (int k = 0; k < LOADS_W; ++k) {
+    int nf = n0 + RPL * (iw * LOADS_W + k);
+    if (nf >= g.N) nf = g.N - RPL;  // rows past N re-read the last RPL (never stored)
+    const int sg = seg_of(g, nf);
+    wbase[k] = (const uint8_t*)g.seg[sg].w + (size_t)(nf - g.seg[sg].n0) * g.K * 2;
+  }
+  const uint32_t smem0 = lds_addr(smem);
+  const uint32_t dst0 = smem0 + iw * LOADS_W * 1024;
+  const int KT = g.K / BK;
+
+  auto issue = [&](int kt) __attribute__((always_inline)) {
+    if (wave >= NIW) return;
+    const uint32_t sa = dst0 + (kt % NST) * STAGE;
+    const int k0b = kt * BK * 2;
+#pragma unroll
+    for (int k = 0; k < LOADS_W; ++k) lds_dma16_sbase(aoffs[k], abase + k0b, sa + k * 1024);
+#pragma unroll
+    for (int k = 0; k < LOADS_W; ++k)
+      lds_dma16_sbase(woff[(iw * LOADS_W + k) & 1], wbase[k] + k0b, sa + ABYTES + k * 1024);
+  };
+
+  // ---- fragment addresses: row 32b + (lane % 32) of a region, chunk (2s + lane/32) ^ f(row)
+  const int fr = lane & 31, fg = lane >> 5;
+  uint32_t koff[KSUB];
+#pragma unroll
+  for (int s = 0; s < KSUB; ++s) koff[s] = fr * ROWB + ((((2 * s + fg) ^ gd_swz<BK>(fr))) << 4);
+
+  const int wn0 = (wave & 1) * 128, wm0 = (wave >> 1) * WM;
+  f32x16 acc[TI][TJ];  // [n block][m block]
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) acc[i][j] = f32x16{};
+
+  u32x4 fw[2][TI], fx[2][TJ];
+  auto load_frags = [&](uint32_t sb, int s, int fb) __attribute__((always_inline)) {
+    const uint32_t ba = sb + koff[s];
+#pragma unroll
+    for (int i = 0; i < TI; ++i) fw[fb][i] = *(GMLA_LDS const u32x4*)(ba + ABYTES + (wn0 + 32 * i) * ROWB);
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) fx[fb][j] = *(GMLA_LDS const u32x4*)(ba + (wm0 + 32 * j) * ROWB);
+  };
+  auto mfmas = [&](int fb) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) acc[i][j] = mfma32(fw[fb][i], fx[fb][j], acc[i][j]);
+  };
+  // the MFMAs of a step with the fragment reads of the next step spread between them
+  auto interleave = [&]() __attribute__((always_inline)) {
+    constexpr int NR = TI + TJ, NM = TI * TJ;
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, NM / NR, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, NM - (NM / NR) * NR, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // Per slab kt: fragments of step s + 1 load while the MFMAs of step s run. Before the last
+  // step's MFMAs (its fragments already in registers) the wave waits for slab kt+1, meets the
+  // others at the barrier (slab kt is now drained everywhere), starts the copy of slab kt+NST
+  // into slab kt's stage, and loads the first fragments of slab kt+1.
+#pragma unroll
+  for (int t = 0; t < NST; ++t)
+    if (t < KT) issue(t);
+  gd_wait_slabs<LPW>(min(NST, KT) - 1);
+  __syncthreads();
+  load_frags(smem0, 0, 0);
+  for (int kt = 0; kt < KT; ++kt) {
+    const uint32_t sb = smem0 + (kt % NST) * STAGE;
+#pragma unroll
+    for (int s = 0; s + 1 < KSUB; ++s) {
+      load_frags(sb, s + 1, (s + 1) & 1);
+      mfmas(s & 1);
+      interleave();
+    }
+    gd_wait_slabs<LPW>(min(NST - 2, KT - 2 - kt));  // slab kt+1 has landed
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (kt + NST < KT) issue(kt + NST);
+    if (kt + 1 < KT) load_frags(smem0 + ((kt + 1) % NST) * STAGE, 0, 0);
+    mfmas((KSUB - 1) & 1);
+    interleave();
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+  // ---- epilogue, staged through LDS so that global stores are row-contiguous:
+  // acc[i][j][4q + e] = out(m0 + wm0 + 32j + lane%32, n0 + wn0 + 32i + 8q + 4(lane/32) + e).
+  // Per pass of 64 columns each wave writes its WM x 64 fp32 block to its own LDS area (row pitch
+  // 68 floats: conflict-free), then reads it back as 16-byte row chunks and stores them with the
+  // column's segment type (fp32: 16 bytes, bf16: 8 bytes per lane).
+  __syncthreads();  // every wave is done with the ring
+  GMLA_LDS float* stg = (GMLA_LDS float*)(smem0) + wave * (WM * PITCH);
+  const int nl = 4 * (lane & 15);
+#pragma unroll
+  for (int pass = 0; pass < TI / 2; ++pass) {
+#pragma unroll
+    for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+      for (int j = 0; j < TJ; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x16& a = acc[2 * pass + ii][j];
+          *(GMLA_LDS f32x4*)(stg + (32 * j + fr) * PITCH + 32 * ii + 8 * q + 4 * fg) =
+              f32x4{a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]};
+        }
+    const int n = n0 + wn0 + 64 * pass + nl;
+    if (n < g.N) {
+      // this lane's segment (a 4-column chunk never straddles one: segments start at multiples of 8)
+      const GemmSeg& s0 = g.seg[0];
+      char* outp = (char*)s0.out;
+      int ldo = s0.ldo, f32 = s0.out_f32, sn0 = s0.n0;
+#pragma unroll
+      for (int i = 1; i < kMaxSegs; ++i)
+        if (i < g.nseg && n >= g.seg[i].n0) {
+          outp = (char*)g.seg[i].out;
+          ldo = g.seg[i].ldo;
+          f32 = g.seg[i].out_f32;
+          sn0 = g.seg[i].n0;
+        }
+      const int col = n - sn0;
+#pragma unroll
+      for (int k = 0; k < WM / 4; ++k) {
+        const int ml = (lane >> 4) + 4 * k;
+        const int m = m0 + wm0 + ml;
+        const f32x4 v = *(GMLA_LDS const f32x4*)(stg + ml * PITCH + nl);
+        if (m < g.M) {
+          if (f32)
+            *(f32x4*)((float*)outp + (size_t)m * ldo + col) = v;
+          else
+            *(u32x2*)((uint16_t*)outp + (size_t)m * ldo + col) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+        }
+      }
+    }
+  }
+}
+
+// the DMA kernel's layout needs K % BK == 0, 16-byte aligned rows, and weight segments (and N)
+// in whole RPL-row loads
+static bool dma_gemm_ok(const GemmArgs& g, int BK) {
+  const int rpl = 1024 / (2 * BK);
+  if (g.M <= 128 || g.K % BK != 0 || g.lda % 8 != 0 || g.N % rpl != 0 || g.N < rpl) return false;
+  for (int i = 0; i < g.nseg; ++i) {
+    const GemmSeg& s = g.seg[i];
+    if (s.n0 % rpl != 0 || s.ldo % 4 != 0) return false;
+    if (((uintptr_t)s.out & 15) != 0 || ((uintptr_t)s.w & 15) != 0) return false;
+  }
+  return ((uintptr_t)g.a & 15) == 0;
+}
+
+// ----------------------------------------------------------------------------------------
 // Small-M kernel (M <= 32)
 // ----------------------------------------------------------------------------------------
 constexpr int kSkinnyUnroll = 8;
@@ -267,7 +519,9 @@ hipError_t launch_gemm(const GemmArgs& g, void* ws, size_t ws_bytes, hipStream_t
     }
     return hipGetLastError();
   }
-  if (g.M <= 128) {
+  if (dma_gemm_ok(g, 64)) {
+    gemm_nt_dma<64, 2, 8><<<cdiv(g.M, 256) * cdiv(g.N, 256), 512, 0, stream>>>(g);
+  } else if (g.M <= 128) {
     const int tiles = cdiv(g.M, 64) * cdiv(g.N, 128);
     gemm_nt_big<64, 128, 2, 2><<<tiles, 256, 0, stream>>>(g);
   } else {

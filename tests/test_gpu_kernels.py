@@ -22,7 +22,8 @@ def _sync():
 # ---------------------------------------------------------------------------------------------
 
 @pytest.mark.parametrize("M,N,K", [(1, 14400, 7168), (7, 300, 1536), (32, 7168, 12288), (33, 200, 256),
-                                   (64, 2112, 512), (300, 1000, 64), (513, 2112, 7168), (256, 24576, 32)])
+                                   (64, 2112, 512), (300, 1000, 64), (513, 2112, 7168), (256, 24576, 32),
+                                   (1000, 2120, 1536), (768, 520, 128)])
 def test_gemm(M, N, K):
     print(f"gemm M={M} N={N} K={K}", flush=True)
     a = rand_bf16((M, K), 1)
