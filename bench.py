@@ -10,7 +10,9 @@ Also reported on the same JSON line:
   on, against the bf16 MFMA peak (2.5 PFLOP/s) or HBM (8 TB/s);
 * decode: latent-absorbed decode attention for B=32 sequences with a T=8192 cache (8,193
   visible positions: the new token is appended first), as KV GB/s against HBM, Infinity
-  Cache flushed between iterations; and the whole mla_decode step;
+  Cache flushed between iterations; the whole mla_decode step; the expanded-cache path at the
+  same shape; long-context decode (B=4, T=131072); Gated DSA decode (B=8, T=65536, top-2048);
+  and the attainable HBM bandwidth of a plain device copy;
 * cpu_baseline: the oracle (float64 NumPy) timed on the host on a bounded sample of the same
   prefill workload.
 All inputs are seeded synthetic data (workloads module); no trained weights are involved.
@@ -65,6 +67,186 @@ def median(v):
     return v[n // 2] if n % 2 else 0.5 * (v[n // 2 - 1] + v[n // 2])
 
 
+def hbm_copy_gbs(torch, log):
+    """Attainable HBM bandwidth: a 2 GiB device-to-device copy (read + write bytes / time)."""
+    src = torch.empty(1 << 31, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    t = median(time_events(lambda: dst.copy_(src), 10))
+    del src, dst
+    gbs = 2 * (1 << 31) / (t * 1e-3) / 1e9
+    log(f"[bench] attainable HBM (2 GiB copy): {gbs:.0f} GB/s")
+    return gbs
+
+
+def roof_hbm(kernel, nbytes, us):
+    gbs = nbytes / (us * 1e-6) / 1e9
+    return {"kernel": kernel, "bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None}
+
+
+def decode_benches(args, d, lw, log):
+    """Decode-side configurations: batched decode (absorbed and expanded caches, and the whole
+    mla_decode step), long-context absorbed decode with split-K and merge, and Gated DSA decode
+    (index scores + top-k, then sparse latent attention)."""
+    import torch
+
+    import gated_mla_kv_amd as gm
+    from gated_mla_kv_amd.layer import LayerBuffers, bf16_tensor
+    from workloads import K3, make_index_prefix, make_latent_prefix, make_tokens, normal_bf16
+
+    dev = "cuda"
+    H = d.n_heads
+    it = args.decode_iters
+    flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    flush = lambda: flush_buf.zero_()  # noqa: E731
+    out = {"hbm_copy_gbs": round(hbm_copy_gbs(torch, log), 1)}
+    L = LayerBuffers(d, {k: v for k, v in lw.w.items() if not k.startswith(("w_idx", "g_idx", "b_idx"))}, dev)
+
+    # -- batched decode: B=32, cache T=8192 (8,193 visible) --
+    B, Tc = 32, 8192
+    nvis = Tc + 1
+    log("[bench] batched decode workload (B=32, T=8192)")
+    lat = bf16_tensor(make_latent_prefix(d, B, nvis, seed=0), dev)
+    dcache = gm.MlaCache(lat.data_ptr(), None, None, None, B, nvis)
+    qt = bf16_tensor(normal_bf16((B, H, d.d_latent), 0.05, 0, 22), dev)
+    n_vis = torch.full((B,), nvis, dtype=torch.int32, device=dev)
+    o = torch.empty((B, H, d.kv_lora), dtype=torch.float32, device=dev)
+    dws = torch.empty(gm.workspace_bytes(L.dims, B, 1, nvis, gm.PATH_ABSORBED), dtype=torch.uint8, device=dev)
+
+    def dec():
+        gm.mla_decode_attention(L.dims, qt, dcache, n_vis, nvis, B, o, None, 0, dws)
+
+    dec()
+    torch.cuda.synchronize()
+    t_cold = median(time_events(dec, it, flush=flush))
+    t_hot = median(time_events(dec, it))
+    kv_bytes = B * nvis * d.d_latent * 2
+    r = roof_hbm("decode_attn_k3_kernel+decode_merge_kernel", kv_bytes, t_cold * 1e3)
+    log(f"[bench] absorbed decode attention: {t_cold * 1e3:.1f} us cold, {t_hot * 1e3:.1f} us hot, "
+        f"{r['achieved']:.0f} GB/s")
+    out.update({"workload": "K3 absorbed decode attention, B=32, cache T=8192 (8193 visible), bf16 latent",
+                "kv_bytes": kv_bytes, "us": round(t_cold * 1e3, 2), "us_hot_cache": round(t_hot * 1e3, 2),
+                "value": r["achieved"], "unit": "GB/s", "roofline": r})
+    # whole decode step (projections, append, attention, gate, o_proj) at the same shape
+    dc2 = L.new_cache(B, nvis, expanded=False)
+    dc2.latent.copy_(lat)
+    xd = bf16_tensor(make_tokens(d, B, 1, seed=0, step=0)[:, 0], dev)
+    seq = torch.full((B,), Tc, dtype=torch.int32, device=dev)
+    wsd = L.workspace(B, 1, nvis, gm.PATH_ABSORBED)
+    yd = torch.empty((B, d.hidden), dtype=torch.bfloat16, device=dev)
+    step = lambda: gm.mla_decode(L.dims, L.cw, dc2.c, seq, nvis, xd, B, gm.PATH_ABSORBED, yd,  # noqa: E731
+                                 gm.OUT_BF16, None, None, 0, wsd)
+    step()
+    torch.cuda.synchronize()
+    out["mla_decode_step_us"] = round(median(time_events(step, it, flush=flush)) * 1e3, 2)
+    log(f"[bench] whole mla_decode step (absorbed): {out['mla_decode_step_us']:.1f} us")
+    del dc2, wsd
+
+    # expanded cache for the same sequences, built from the latents by the kv_b projection (setup)
+    log("[bench] expanded decode workload: building K/V [32, 96, 8193, 192|128] from the latents")
+    ecache = L.new_cache(B, nvis, expanded=True)
+    ecache.latent.copy_(lat)
+    pos0 = torch.zeros(1, dtype=torch.int32, device=dev)
+    kvb = torch.empty((nvis, H * (d.d_nope + d.d_v)), dtype=torch.bfloat16, device=dev)
+    for b in range(B):
+        cb = lat[b, :, :d.kv_lora].contiguous()
+        rb = lat[b, :, d.kv_lora:].contiguous()
+        gm.mla_gemm(cb, d.kv_lora, L.w["w_kv_b"], nvis, kvb.shape[1], d.kv_lora, kvb, kvb.shape[1])
+        kv4 = kvb.view(nvis, H, d.d_nope + d.d_v)
+        kn, vv = kv4[..., :d.d_nope].contiguous(), kv4[..., d.d_nope:].contiguous()
+        view = gm.MlaCache(ecache.latent[b].data_ptr(), ecache.k[b].data_ptr(), ecache.v[b].data_ptr(), None, 1,
+                           nvis)
+        gm.kv_append(L.dims, view, pos0, nvis, 1, nvis, cb, rb, kn, vv)
+    torch.cuda.synchronize()
+    del kvb, kn, vv, cb, rb
+    qe = bf16_tensor(normal_bf16((B, H, d.d_qk), 0.8, 0, 23), dev)
+    z = torch.empty((B, H, d.d_v), dtype=torch.float32, device=dev)
+    exp_fn = lambda: gm.mla_expanded_attention(L.dims, qe, ecache.c, n_vis, nvis, B, z)  # noqa: E731
+    exp_fn()
+    torch.cuda.synchronize()
+    t_exp = median(time_events(exp_fn, max(3, it // 4), flush=flush))
+    e_bytes = B * H * nvis * (d.d_qk + d.d_v) * 2
+    re = roof_hbm("expanded_attn_kernel", e_bytes, t_exp * 1e3)
+    log(f"[bench] expanded decode attention: {t_exp * 1e3:.1f} us, {re['achieved']:.0f} GB/s")
+    out["expanded"] = {"workload": "K3 expanded-cache decode attention, B=32, T=8192 (8193 visible)",
+                       "kv_bytes": e_bytes, "us": round(t_exp * 1e3, 2), "value": re["achieved"], "unit": "GB/s",
+                       "roofline": re}
+    del ecache, lat, dcache, o, dws, qe, z
+    torch.cuda.empty_cache()
+
+    # -- long-context decode: B=4, cache T=131072 --
+    B4, T4 = 4, 131072
+    nv4 = T4 + 1
+    log("[bench] long-context decode workload (B=4, T=131072)")
+    lat4 = bf16_tensor(make_latent_prefix(d, B4, nv4, seed=0), dev)
+    c4 = gm.MlaCache(lat4.data_ptr(), None, None, None, B4, nv4)
+    qt4 = bf16_tensor(normal_bf16((B4, H, d.d_latent), 0.05, 0, 24), dev)
+    n4 = torch.full((B4,), nv4, dtype=torch.int32, device=dev)
+    o4 = torch.empty((B4, H, d.kv_lora), dtype=torch.float32, device=dev)
+    ws4 = torch.empty(gm.workspace_bytes(L.dims, B4, 1, nv4, gm.PATH_ABSORBED), dtype=torch.uint8, device=dev)
+    f4 = lambda: gm.mla_decode_attention(L.dims, qt4, c4, n4, nv4, B4, o4, None, 0, ws4)  # noqa: E731
+    f4()
+    torch.cuda.synchronize()
+    t4 = median(time_events(f4, it, flush=flush))
+    b4 = B4 * nv4 * d.d_latent * 2
+    r4 = roof_hbm("decode_attn_k3_kernel+decode_merge_kernel", b4, t4 * 1e3)
+    log(f"[bench] long-context absorbed decode: {t4 * 1e3:.1f} us, {r4['achieved']:.0f} GB/s")
+    out["long_context"] = {"workload": "K3 absorbed decode attention, B=4, cache T=131072 (131073 visible), "
+                                       "split-K + softmax merge", "kv_bytes": b4, "us": round(t4 * 1e3, 2),
+                           "value": r4["achieved"], "unit": "GB/s", "roofline": r4}
+    del lat4, c4, o4, ws4
+    torch.cuda.empty_cache()
+
+    # -- Gated DSA decode: B=8, cache T=65536 (65,537 visible), top-2048 --
+    dd = K3
+    B5, T5 = 8, 65536
+    nv5 = T5 + 1
+    log("[bench] DSA decode workload (B=8, T=65536)")
+    L5 = LayerBuffers(dd, lw.w, dev)
+    lat5 = bf16_tensor(make_latent_prefix(dd, B5, nv5, seed=0), dev)
+    idx5 = bf16_tensor(make_index_prefix(dd, B5, nv5, seed=0), dev)
+    c5 = gm.MlaCache(lat5.data_ptr(), None, None, idx5.data_ptr(), B5, nv5)
+    f32 = lambda bits: torch.from_numpy((bits.astype("uint32") << 16).view("float32")).to(dev)  # noqa: E731
+    qi = f32(normal_bf16((B5, dd.n_idx_heads, dd.d_idx), 0.5, 0, 25))
+    wi = f32(normal_bf16((B5, dd.n_idx_heads), 1.0, 0, 26))
+    n5 = torch.full((B5,), nv5, dtype=torch.int32, device=dev)
+    sel = torch.empty((B5, dd.topk), dtype=torch.int32, device=dev)
+    cnt = torch.empty((B5,), dtype=torch.int32, device=dev)
+    ws5 = torch.empty(gm.workspace_bytes(L5.dims, B5, 1, nv5, gm.PATH_SPARSE), dtype=torch.uint8, device=dev)
+    qt5 = bf16_tensor(normal_bf16((B5, H, dd.d_latent), 0.05, 0, 27), dev)
+    o5 = torch.empty((B5, H, dd.kv_lora), dtype=torch.float32, device=dev)
+    topk_fn = lambda: gm.dsa_index_topk(L5.dims, qi, wi, idx5, nv5, n5, nv5, B5, sel, cnt, None, ws5)  # noqa: E731
+    sparse_fn = lambda: gm.mla_sparse_attention(L5.dims, qt5, c5, sel, cnt, B5, o5, None, 0, ws5)  # noqa: E731
+
+    def dsa_fn():
+        topk_fn()
+        sparse_fn()
+
+    dsa_fn()
+    torch.cuda.synchronize()
+    t_topk = median(time_events(topk_fn, it, flush=flush))
+    t_sparse = median(time_events(sparse_fn, it, flush=flush))
+    t_dsa = median(time_events(dsa_fn, it, flush=flush))
+    b_idx = B5 * nv5 * dd.d_idx * 2
+    b_sel = B5 * dd.topk * dd.d_latent * 2
+    r5 = roof_hbm("index_scores_kernel+topk_kernel+decode_attn_k3_kernel<gather>+decode_merge_kernel",
+                  b_idx + b_sel, t_dsa * 1e3)
+    log(f"[bench] DSA decode: index+top-k {t_topk * 1e3:.1f} us, sparse {t_sparse * 1e3:.1f} us, "
+        f"together {t_dsa * 1e3:.1f} us, {r5['achieved']:.0f} GB/s")
+    out["dsa"] = {"workload": "K3.1 Gated DSA decode, B=8, cache T=65536 (65537 visible), top-2048",
+                  "bytes": b_idx + b_sel, "us": round(t_dsa * 1e3, 2), "value": r5["achieved"], "unit": "GB/s",
+                  "roofline": r5,
+                  "index_topk": {"us": round(t_topk * 1e3, 2), "bytes": b_idx,
+                                 "gbs": round(b_idx / (t_topk * 1e-6 * 1e3) / 1e9, 1)},
+                  "sparse_attention": {"us": round(t_sparse * 1e3, 2), "bytes": b_sel,
+                                       "gbs": round(b_sel / (t_sparse * 1e-6 * 1e3) / 1e9, 1)}}
+    del flush_buf
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -93,7 +275,7 @@ def main():
     T = args.T
     log = lambda *a: print(*a, file=sys.stderr, flush=True)  # noqa: E731
     log(f"[bench] building K3 weights and inputs (T={T})")
-    lw = make_layer_weights(d, seed=0)
+    lw = make_layer_weights(K3, seed=0)  # dense layer weights plus the DSA indexer's
     L = LayerBuffers(d, lw.w, dev)
     x_bits = make_tokens(d, 1, T, seed=0)
     x = bf16_tensor(x_bits, dev)
@@ -169,57 +351,12 @@ def main():
                for k, v in stage_ms.items()}
     del out_x, w_x, cq, qb, c, kvb, u, yo, qa, gpre, ua
 
-    # ---- decode: latent-absorbed attention over B=32 x 8,193 positions ----
+    # ---- decode configurations (each kernel timed alone; Infinity Cache flushed between calls) ----
     decode = None
     if not args.no_decode:
-        B, Tc = 32, 8192
-        nvis = Tc + 1
-        log("[bench] building the decode workload (B=32, T=8192)")
-        lat = bf16_tensor(make_latent_prefix(d, B, nvis, seed=0), dev)
-        dcache = gm.MlaCache(lat.data_ptr(), None, None, None, B, nvis)
-        qt = bf16_tensor(normal_bf16((B, H, d.d_latent), 0.05, 0, 22), dev)
-        n_vis = torch.full((B,), nvis, dtype=torch.int32, device=dev)
-        o = torch.empty((B, H, d.kv_lora), dtype=torch.float32, device=dev)
-        dws = torch.empty(gm.workspace_bytes(L.dims, B, 1, nvis, gm.PATH_ABSORBED), dtype=torch.uint8, device=dev)
-        flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-
-        def dec():
-            gm.mla_decode_attention(L.dims, qt, dcache, n_vis, nvis, B, o, None, 0, dws)
-
-        dec()
-        torch.cuda.synchronize()
-        cold = time_events(dec, args.decode_iters, flush=lambda: flush_buf.zero_())
-        hot = time_events(dec, args.decode_iters)
-        kv_bytes = B * nvis * d.d_latent * 2
-        t_cold = median(cold)
-        gbs = kv_bytes / (t_cold * 1e-3) / 1e9
-        log(f"[bench] absorbed decode attention: {t_cold * 1e3:.1f} us cold, {median(hot) * 1e3:.1f} us hot, "
-            f"{gbs:.0f} GB/s")
-        # whole decode step (projections, append, attention, gate, o_proj) at the same shape
-        dcache2 = L.new_cache(B, nvis, expanded=False)
-        dcache2.latent.copy_(lat)
-        del lat
-        xd = bf16_tensor(make_tokens(d, B, 1, seed=0, step=0)[:, 0], dev)
-        seq = torch.full((B,), Tc, dtype=torch.int32, device=dev)
-        wsd = L.workspace(B, 1, nvis, gm.PATH_ABSORBED)
-        yd = torch.empty((B, d.hidden), dtype=torch.bfloat16, device=dev)
-
-        def dstep():
-            gm.mla_decode(L.dims, L.cw, dcache2.c, seq, nvis, xd, B, gm.PATH_ABSORBED, yd, gm.OUT_BF16, None, None,
-                          0, wsd)
-
-        dstep()
-        torch.cuda.synchronize()
-        t_step = median(time_events(dstep, args.decode_iters, flush=lambda: flush_buf.zero_()))
-        decode = {"workload": "K3 absorbed decode attention, B=32, cache T=8192 (8193 visible), bf16 latent",
-                  "kv_bytes": kv_bytes, "us": round(t_cold * 1e3, 2), "us_hot_cache": round(median(hot) * 1e3, 2),
-                  "value": round(gbs, 1), "unit": "GB/s",
-                  "roofline": {"kernel": "decode_attn_k3_kernel+decode_merge_kernel", "bound": "hbm",
-                               "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                               "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None},
-                  "mla_decode_step_us": round(t_step * 1e3, 2)}
-        del flush_buf
-
+        del cache
+        torch.cuda.empty_cache()
+        decode = decode_benches(args, d, lw, log)
     # ---- CPU baseline: the oracle on a bounded sample of the prefill workload ----
     cpu = None
     if not args.no_cpu_baseline:

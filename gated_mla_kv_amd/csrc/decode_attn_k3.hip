@@ -107,20 +107,33 @@ __global__ __launch_bounds__(k3dec::NTHREADS) void decode_attn_k3_kernel(DecodeA
     float m_run = -INFINITY, l_run = 0.f;
 
     // scores, online-softmax statistics and P^T of tile t into buffer t%2
+    // chunk (2s + g2) ^ swz = 8*(s/4) + ((2*(s%4) + g2) ^ swz): four per-lane LDS offsets plus
+    // immediates
+    uint32_t aoff[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) aoff[m] = lds_addr(lat_s[0]) + srow_base + (((2 * m + g2) ^ srow_swz) << 4);
     auto score_tile = [&](int t) {
-      const uint8_t* arow = lat_s[t % NSLOT] + srow_base;
-      constexpr int PF = 8;  // LDS reads run PF k-steps ahead of their MFMA
+      const uint32_t so = (t % NSLOT) * TILE_BYTES;
+      uint32_t ab[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) ab[m] = aoff[m] + so;
+      auto lat_row = [&](int s) __attribute__((always_inline)) {
+        return *(GMLA_LDS const u32x4*)(ab[s & 3] + 128 * (s >> 2));
+      };
+      constexpr int PF = GATHER ? 6 : 8;  // LDS reads run PF k-steps ahead of their MFMA
       u32x4 ar[PF];
 #pragma unroll
-      for (int s = 0; s < PF; ++s) ar[s] = *(const u32x4*)(arow + (((2 * s + g2) ^ srow_swz) << 4));
-      f32x16 sacc = f32x16{};
+      for (int s = 0; s < PF; ++s) ar[s] = lat_row(s);
+      // two accumulator chains (even and odd k-steps) so that consecutive MFMAs are independent
+      f32x16 sacc2[2] = {f32x16{}, f32x16{}};
 #pragma unroll
       for (int s = 0; s < KSD; ++s) {
         const u32x4 cur = ar[s % PF];
-        if (s + PF < KSD) ar[s % PF] = *(const u32x4*)(arow + (((2 * (s + PF) + g2) ^ srow_swz) << 4));
+        if (s + PF < KSD) ar[s % PF] = lat_row(s + PF);
         __builtin_amdgcn_sched_barrier(0);
-        sacc = mfma32(cur, qf[s], sacc);
+        sacc2[s & 1] = mfma32(cur, qf[s], sacc2[s & 1]);
       }
+      f32x16 sacc = sacc2[0] + sacc2[1];
       const int jbase = t * BT;
       float mt = -INFINITY;
 #pragma unroll
@@ -230,22 +243,28 @@ __global__ __launch_bounds__(k3dec::NTHREADS) void decode_attn_k3_kernel(DecodeA
             for (int r = 0; r < 16; ++r) o[dt][hs][r] *= al[hs];
         }
       }
+      // P^T for both 16-position halves, then Lat^T fragments one (half, block) ahead of their MFMAs
+      u32x4 pb[2][3];
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        u32x4 pb[3];
+      for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-        for (int hs = 0; hs < 3; ++hs) pb[hs] = ld16(pbuf + (hs * 32 + l32) * PROW + ks * 16 + g2 * 8);
+        for (int hs = 0; hs < 3; ++hs) pb[ks][hs] = ld16(pbuf + (hs * 32 + l32) * PROW + ks * 16 + g2 * 8);
+      auto lat_frag = [&](int k) __attribute__((always_inline)) {
+        const int ks = k >> 2, dt = k & 3;
         const int r0 = ks * 16 + 8 * (G >> 1) + (jj >> 2), r1 = r0 + 4;
+        const int fcol = (pw * 4 + dt) * 32 + 16 * (G & 1) + 4 * (jj & 3);
+        const int c = fcol >> 3, off = (fcol & 7) * 2;
+        const u32x2 lo = lds_read_tr16(slot + (r0 * CH + (c ^ swz_row(r0))) * 16 + off);
+        const u32x2 hi = lds_read_tr16(slot + (r1 * CH + (c ^ swz_row(r1))) * 16 + off);
+        return u32x4{lo.x, lo.y, hi.x, hi.y};
+      };
+      u32x4 af = lat_frag(0);
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
-          const int fcol = (pw * 4 + dt) * 32 + 16 * (G & 1) + 4 * (jj & 3);
-          const int c = fcol >> 3, off = (fcol & 7) * 2;
-          const u32x2 lo = lds_read_tr16(slot + (r0 * CH + (c ^ swz_row(r0))) * 16 + off);
-          const u32x2 hi = lds_read_tr16(slot + (r1 * CH + (c ^ swz_row(r1))) * 16 + off);
-          const u32x4 af = u32x4{lo.x, lo.y, hi.x, hi.y};
+      for (int k = 0; k < 8; ++k) {
+        const u32x4 an = lat_frag(k < 7 ? k + 1 : 7);
 #pragma unroll
-          for (int hs = 0; hs < 3; ++hs) o[dt][hs] = mfma32(af, pb[hs], o[dt][hs]);
-        }
+        for (int hs = 0; hs < 3; ++hs) o[k & 3][hs] = mfma32(af, pb[k >> 2][hs], o[k & 3][hs]);
+        af = an;
       }
       if (t + 2 < n_tiles) wait_for(t + 2, issued);  // the score waves read it in the next step
       __syncthreads();

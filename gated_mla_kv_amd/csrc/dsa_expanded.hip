@@ -9,10 +9,13 @@
 // into a exactly.
 //
 // topk_kernel (eq. (6)): S = the min(k, t) largest I, ties to the lower position, -0 == +0,
-// written in ascending position order. Radix select over order-preserving 32-bit keys (four
-// 8-bit passes, LDS histograms) finds the k-th largest key tau; a compaction over contiguous
-// per-thread position ranges then keeps every key > tau and the lowest-position keys == tau,
-// using two block-wide exclusive scans, so the output is ascending by construction.
+// written in ascending position order. One workgroup per query row. A radix select over
+// order-preserving 32-bit keys with 12-, 12- and 8-bit digits (the row's keys held in registers,
+// LDS histograms) narrows the
+// k-th largest key down until a whole bin is taken or the key tau is exact. The compaction gives
+// each wave a contiguous run of positions: a counting pass, a scan of the 16 wave counts, and a
+// writing pass with ballot prefix counts, so the output is ascending by construction and the
+// copies of tau kept are the lowest-position ones.
 //
 // expanded_attn_kernel: one query per (b, h) against the expanded cache k [B,H,T_cap,192],
 // v [B,H,T_cap,128] (KV cache card): 61,440 bytes per position, HBM bound at ~1 flop per byte,
@@ -26,7 +29,7 @@ namespace gmla {
 // ------------------------------------------------------------------------------------------
 // Index scores (K3 indexer: 32 heads x 128)
 // ------------------------------------------------------------------------------------------
-constexpr int kScorePosPerWG = 1024;
+constexpr int kScorePosPerWG = 256;
 
 __global__ __launch_bounds__(256) void index_scores_kernel(IndexScoreArgs a) {
   constexpr int NIH = 32, DI = 128, KS = DI / 16;
@@ -36,6 +39,18 @@ __global__ __launch_bounds__(256) void index_scores_kernel(IndexScoreArgs a) {
   const int t = min(min(a.n_vis[b] + a.vis_offset, a.T_cap), a.score_stride);
   const int base = blockIdx.x * kScorePosPerWG;
   if (base >= t) return;
+  const int end = min(base + kScorePosPerWG, t);
+  const uint16_t* kb = a.idx_k + (size_t)b * a.T_cap * DI;
+  // keys of this wave's positions p0 + l32 (two 32-position steps per wave), both loads in flight
+  auto load_keys = [&](int p0, u32x4* kf) __attribute__((always_inline)) {
+    const int pos = min(p0 + l32, end - 1);  // rows past the end re-read a valid row (not stored)
+#pragma unroll
+    for (int s = 0; s < KS; ++s) kf[s] = ld16(kb + (size_t)pos * DI + s * 16 + g2 * 8);
+  };
+  const int p0a = base + wave * 32, p0b = p0a + 4 * 32;
+  u32x4 kfa[KS], kfb[KS];
+  load_keys(p0a, kfa);
+  if (p0b < end) load_keys(p0b, kfb);
   // A operand: q^I rows (heads) for this lane's head l32
   u32x4 qa[KS];
   const uint16_t* qrow = a.q_idx + ((size_t)b * NIH + l32) * DI;
@@ -45,14 +60,7 @@ __global__ __launch_bounds__(256) void index_scores_kernel(IndexScoreArgs a) {
   float wgt[16];
 #pragma unroll
   for (int r = 0; r < 16; ++r) wgt[r] = a.w_idx[(size_t)b * NIH + (r >> 2) * 8 + g2 * 4 + (r & 3)] * a.scale;
-  const uint16_t* kb = a.idx_k + (size_t)b * a.T_cap * DI;
-  const int end = min(base + kScorePosPerWG, t);
-  for (int p0 = base + wave * 32; p0 < end; p0 += 4 * 32) {
-    const int pos = p0 + l32;
-    const bool ok = pos < end;
-    u32x4 kf[KS];
-#pragma unroll
-    for (int s = 0; s < KS; ++s) kf[s] = ok ? ld16(kb + (size_t)pos * DI + s * 16 + g2 * 8) : zero16();
+  auto score = [&](int p0, const u32x4* kf) __attribute__((always_inline)) {
     f32x16 acc = f32x16{};
 #pragma unroll
     for (int s = 0; s < KS; ++s) acc = mfma32(qa[s], kf[s], acc);
@@ -60,8 +68,11 @@ __global__ __launch_bounds__(256) void index_scores_kernel(IndexScoreArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) sc += wgt[r] * fmaxf(acc[r], 0.f);
     sc += __shfl_xor(sc, 32, 64);
-    if (ok && g2 == 0) a.scores[(size_t)b * a.score_stride + pos] = sc;
-  }
+    const int pos = p0 + l32;
+    if (pos < end && g2 == 0) a.scores[(size_t)b * a.score_stride + pos] = sc;
+  };
+  if (p0a < end) score(p0a, kfa);
+  if (p0b < end) score(p0b, kfb);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -101,73 +112,169 @@ __device__ int block_exclusive_scan(int v, int* tmp /* NT/64 + 1 ints */, int& t
 }
 
 constexpr int kTopkThreads = 1024;
+constexpr int kTopkWaves = kTopkThreads / 64;
 
+// number of lanes below this one with `pred` set, and the wave's total
+__device__ __forceinline__ int lanes_below(uint64_t m) {
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+constexpr int kTopkR = 65;                        // keys held per thread (one segment)
+constexpr int kTopkSeg = kTopkR * kTopkThreads;    // 66,560 positions per segment
+
+constexpr int kHistRep = 8;        // histogram replicas (lane % 8): at most 8 lanes per address
+constexpr int kHistPitch = 4097;   // replica stride in words (not a multiple of the bank count)
+
+// Positions past the row hold key 0. A real score never maps to a key below 2^20 (those are NaN
+// bit patterns), so key 0 sits in digit-0 bin 0, under any threshold, and no pass needs a
+// bounds test.
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
-  __shared__ int hist[256];
+  __shared__ int hist[kHistRep * kHistPitch];
   __shared__ int scan_tmp[kTopkThreads / 64 + 1];
-  __shared__ uint32_t sh_prefix;
-  __shared__ int sh_krem;
+  __shared__ int sh_bin, sh_above, sh_cnt;
+  __shared__ int wcnt[2][kTopkWaves];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int b = blockIdx.x;
   const int t = min(a.n_vis[b] + a.vis_offset, a.score_stride);
   const int k = min(a.k, t);
   int32_t* out = a.out_idx + (size_t)b * a.out_stride;
   const float* sc = a.scores + (size_t)b * a.score_stride;
   if (t <= a.k) {  // short history: every visible position is kept
-    for (int i = threadIdx.x; i < a.k; i += kTopkThreads) out[i] = (i < t) ? i : -1;
-    if (threadIdx.x == 0) a.out_cnt[b] = t;
+    for (int i = tid; i < a.k; i += kTopkThreads) out[i] = (i < t) ? i : -1;
+    if (tid == 0) a.out_cnt[b] = t;
     return;
   }
+
+  // Keys of segment sg: wave w owns positions sg*kTopkSeg + w*65*64 .. +65*64-1, its key u being
+  // position ... + u*64 + lane (coalesced), all loads in flight at once. A row of one segment
+  // (t <= 66,560) stays in registers for every pass.
+  const int n_segs = cdiv(t, kTopkSeg);
+  uint32_t keys[kTopkR];
+  auto seg_base = [&](int sg) __attribute__((always_inline)) { return sg * kTopkSeg + wave * (kTopkR * 64); };
+  auto load_seg = [&](int sg) __attribute__((always_inline)) {
+    const int base = seg_base(sg);
+    const float* p = sc + base + lane;
+    const int lim = t - 1 - base - lane;  // u*64 <= lim <=> the position is visible
+#pragma unroll
+    for (int u = 0; u < kTopkR; ++u) keys[u] = __float_as_uint(p[min(u * 64, max(lim, 0))]);
+#pragma unroll
+    for (int u = 0; u < kTopkR; ++u) keys[u] = u * 64 <= lim ? order_key(__uint_as_float(keys[u])) : 0u;
+  };
+  load_seg(0);
+
+  // ---- radix select over the keys: digits of 12, 12 and 8 bits from the top ----
   uint32_t prefix = 0, pmask = 0;
   int krem = k;
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    for (int i = threadIdx.x; i < 256; i += kTopkThreads) hist[i] = 0;
+  bool whole_bin = false;  // the last decided bin is taken entirely
+  int* my_hist = hist + (lane & (kHistRep - 1)) * kHistPitch;
+#pragma unroll 1
+  for (int level = 0; level < 3; ++level) {
+    const int shift = level == 0 ? 20 : (level == 1 ? 8 : 0);
+    const int nbins = level == 2 ? 256 : 4096;
+    for (int i = tid; i < kHistRep * kHistPitch; i += kTopkThreads) hist[i] = 0;
     __syncthreads();
-    for (int i = threadIdx.x; i < t; i += kTopkThreads) {
-      const uint32_t key = order_key(sc[i]);
-      if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255], 1);
+#pragma unroll 1
+    for (int sg = 0; sg < n_segs; ++sg) {
+      if (n_segs > 1) load_seg(sg);
+#pragma unroll
+      for (int u = 0; u < kTopkR; ++u)
+        if ((keys[u] & pmask) == prefix) atomicAdd(&my_hist[(keys[u] >> shift) & (uint32_t)(nbins - 1)], 1);
     }
     __syncthreads();
-    if (threadIdx.x == 0) {
-      int cum = 0, bin = 255;
-      for (; bin > 0; --bin) {
-        if (cum + hist[bin] >= krem) break;
-        cum += hist[bin];
+    // the bin where the count from the top reaches krem: thread j owns bins nbins-1-4j .. -3
+    constexpr int PER = 4096 / kTopkThreads;
+    int cntb[PER];
+    int local = 0;
+    const int top = nbins - 1 - PER * tid;
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      cntb[q] = 0;
+      if (top - q >= 0)
+#pragma unroll
+        for (int r = 0; r < kHistRep; ++r) cntb[q] += hist[r * kHistPitch + top - q];
+      local += cntb[q];
+    }
+    int total;
+    const int before = block_exclusive_scan<kTopkThreads>(local, scan_tmp, total);
+    if (before < krem && before + local >= krem) {
+      int cum = before;
+#pragma unroll
+      for (int q = 0; q < PER; ++q) {
+        if (cum < krem && cum + cntb[q] >= krem) {
+          sh_bin = top - q;
+          sh_above = cum;
+          sh_cnt = cntb[q];
+        }
+        cum += cntb[q];
       }
-      sh_prefix = prefix | ((uint32_t)bin << shift);
-      sh_krem = krem - cum;
     }
     __syncthreads();
-    prefix = sh_prefix;
-    krem = sh_krem;
-    pmask |= 255u << shift;
+    prefix |= (uint32_t)sh_bin << shift;
+    pmask |= (uint32_t)(nbins - 1) << shift;
+    krem -= sh_above;
+    const int cnt = sh_cnt;
+    __syncthreads();
+    if (cnt == krem) {
+      whole_bin = true;
+      break;
+    }
+  }
+  // kept: key > thr, plus (all 32 bits decided, tau = prefix) the krem lowest-position copies
+  // of tau. A whole bin taken is key >= prefix (its undecided low bits are zero): thr = prefix-1.
+  const uint32_t tau = prefix;
+  const uint32_t thr = whole_bin ? prefix - 1u : tau;
+  if (whole_bin) krem = 0;
+  auto kept_gt = [&](uint32_t key) __attribute__((always_inline)) { return key > thr; };
+
+  // ---- ordered compaction: wave w owns a contiguous run of each segment ----
+  int out_base = 0, eq_base = 0;
+#pragma unroll 1
+  for (int sg = 0; sg < n_segs; ++sg) {
+    if (n_segs > 1) load_seg(sg);
+    int nk = 0, ne = 0;
+#pragma unroll
+    for (int u = 0; u < kTopkR; ++u) {
+      nk += (int)__popcll(__ballot(kept_gt(keys[u])));
+      ne += (int)__popcll(__ballot(!whole_bin && keys[u] == tau));
+    }
+    if (lane == 0) {
+      wcnt[0][wave] = nk;
+      wcnt[1][wave] = ne;
+    }
+    // recompute the predicates in the writing pass rather than keep 2 x 65 of them live
+#pragma unroll
+    for (int u = 0; u < kTopkR; ++u) asm volatile("" : "+v"(keys[u]));
+    __syncthreads();
+    int eq_before = eq_base, out_before = out_base, seg_keep = 0, seg_eq = 0;
+    for (int w = 0; w < kTopkWaves; ++w) {
+      const int take = max(0, min(krem - (eq_base + seg_eq), wcnt[1][w]));
+      if (w < wave) {
+        eq_before += wcnt[1][w];
+        out_before += wcnt[0][w] + take;
+      }
+      seg_keep += wcnt[0][w] + take;
+      seg_eq += wcnt[1][w];
+    }
+    const int take_w = max(0, min(krem - eq_before, ne));  // copies of tau this wave keeps
+    int wpos = out_before, eq_seen = 0;
+    const int base = seg_base(sg);
+#pragma unroll
+    for (int u = 0; u < kTopkR; ++u) {
+      const bool eq = !whole_bin && keys[u] == tau;
+      const uint64_t em = __ballot(eq);
+      const bool keep = kept_gt(keys[u]) || (eq && eq_seen + lanes_below(em) < take_w);
+      const uint64_t km = __ballot(keep);
+      const int w = wpos + lanes_below(km);
+      if (keep && w < a.k) out[w] = base + u * 64 + lane;
+      wpos += (int)__popcll(km);
+      eq_seen += (int)__popcll(em);
+    }
+    out_base += seg_keep;
+    eq_base += seg_eq;
     __syncthreads();
   }
-  const uint32_t tau = prefix;  // the k-th largest key; krem of its copies are taken
-  const int per = cdiv(t, kTopkThreads);
-  const int lo = min((int)threadIdx.x * per, t), hi = min(lo + per, t);
-  int n_gt = 0, n_eq = 0;
-  for (int i = lo; i < hi; ++i) {
-    const uint32_t key = order_key(sc[i]);
-    n_gt += key > tau;
-    n_eq += key == tau;
-  }
-  int tot;
-  const int eq_before = block_exclusive_scan<kTopkThreads>(n_eq, scan_tmp, tot);
-  const int take_eq = max(0, min(krem - eq_before, n_eq));
-  const int off = block_exclusive_scan<kTopkThreads>(n_gt + take_eq, scan_tmp, tot);
-  int w = off, eq_seen = 0;
-  for (int i = lo; i < hi; ++i) {
-    const uint32_t key = order_key(sc[i]);
-    bool keep = key > tau;
-    if (key == tau) {
-      keep = eq_seen < take_eq;
-      ++eq_seen;
-    }
-    if (keep && w < a.k) out[w++] = i;
-  }
-  for (int i = k + threadIdx.x; i < a.k; i += kTopkThreads) out[i] = -1;
-  if (threadIdx.x == 0) a.out_cnt[b] = k;
+  for (int i = k + tid; i < a.k; i += kTopkThreads) out[i] = -1;
+  if (tid == 0) a.out_cnt[b] = k;
 }
 
 // ------------------------------------------------------------------------------------------
