@@ -215,3 +215,16 @@ def make_latent_prefix(dims: MLADims, B: int, T: int, seed: int = 0) -> np.ndarr
 def make_index_prefix(dims: MLADims, B: int, T: int, seed: int = 0) -> np.ndarray:
     """Cached index keys [B, T, d_idx] ~ N(0, 1), bf16 bits."""
     return normal_bf16((B, T, dims.d_idx), 1.0, seed, TensorId.INDEX_PREFIX)
+
+
+def device_normal_bf16(shape, std: float, seed: int, tensor_id: int, device="cuda"):
+    """N(0, std^2) bf16 tensor drawn on the device by torch's seeded generator (Philox), for the
+    full-size inputs (the expanded cache alone holds 8 G values). The same bits go to both sides:
+    the GPU path reads the tensor, the oracle the rows copied back from it."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed) * 1_000_003 + int(tensor_id))
+    t = torch.randn(tuple(shape), generator=g, device=device, dtype=torch.bfloat16)
+    if std != 1.0:
+        t.mul_(std)
+    return t
