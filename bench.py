@@ -61,10 +61,43 @@ def time_events(fn, iters, flush=None):
     return out
 
 
+def time_batched(fn, iters):
+    """Average duration (ms) of back-to-back calls, events around the whole batch (launch gaps
+    amortised, so it compares with a kernel trace's per-dispatch average)."""
+    import torch
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(iters):
+        fn()
+    e.record()
+    e.synchronize()
+    return s.elapsed_time(e) / iters
+
+
 def median(v):
     v = sorted(v)
     n = len(v)
     return v[n // 2] if n % 2 else 0.5 * (v[n // 2 - 1] + v[n // 2])
+
+
+def traffic_for(key):
+    """HBM bytes per launch of a kernel (or kernel group) from the committed counter runs
+    (profiles/traffic.json: rocprofv3 FETCH_SIZE and WRITE_SIZE per dispatch, scaled by what the
+    same counters read for a 256 MiB device copy), or None when the kernel's sources changed
+    since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            e = json.load(f)["entries"][key]
+        h = hashlib.sha256()
+        for fn in e["sources"]:
+            with open(os.path.join(ROOT, "gated_mla_kv_amd", "csrc", fn), "rb") as f:
+                h.update(f.read())
+        return e["hbm_bytes_per_launch"] if h.hexdigest()[:16] == e["sources_sha256_16"] else None
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def hbm_copy_gbs(torch, log):
@@ -81,10 +114,10 @@ def hbm_copy_gbs(torch, log):
     return gbs
 
 
-def roof_hbm(kernel, nbytes, us):
+def roof_hbm(kernel, nbytes, us, traffic_key=None):
     gbs = nbytes / (us * 1e-6) / 1e9
     return {"kernel": kernel, "bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-            "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None}
+            "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": traffic_for(traffic_key) if traffic_key else None}
 
 
 def decode_benches(args, d, lw, log):
@@ -124,7 +157,7 @@ def decode_benches(args, d, lw, log):
     t_cold = median(time_events(dec, it, flush=flush))
     t_hot = median(time_events(dec, it))
     kv_bytes = B * nvis * d.d_latent * 2
-    r = roof_hbm("decode_attn_k3_kernel+decode_merge_kernel", kv_bytes, t_cold * 1e3)
+    r = roof_hbm("decode_attn_k3_kernel+decode_merge_kernel", kv_bytes, t_cold * 1e3, "decode:B32_T8192")
     log(f"[bench] absorbed decode attention: {t_cold * 1e3:.1f} us cold, {t_hot * 1e3:.1f} us hot, "
         f"{r['achieved']:.0f} GB/s")
     out.update({"workload": "K3 absorbed decode attention, B=32, cache T=8192 (8193 visible), bf16 latent",
@@ -192,7 +225,7 @@ def decode_benches(args, d, lw, log):
     torch.cuda.synchronize()
     t4 = median(time_events(f4, it, flush=flush))
     b4 = B4 * nv4 * d.d_latent * 2
-    r4 = roof_hbm("decode_attn_k3_kernel+decode_merge_kernel", b4, t4 * 1e3)
+    r4 = roof_hbm("decode_attn_k3_kernel+decode_merge_kernel", b4, t4 * 1e3, "decode:B4_T131072")
     log(f"[bench] long-context absorbed decode: {t4 * 1e3:.1f} us, {r4['achieved']:.0f} GB/s")
     out["long_context"] = {"workload": "K3 absorbed decode attention, B=4, cache T=131072 (131073 visible), "
                                        "split-K + softmax merge", "kv_bytes": b4, "us": round(t4 * 1e3, 2),
@@ -233,7 +266,7 @@ def decode_benches(args, d, lw, log):
     b_idx = B5 * nv5 * dd.d_idx * 2
     b_sel = B5 * dd.topk * dd.d_latent * 2
     r5 = roof_hbm("index_scores_kernel+topk_kernel+decode_attn_k3_kernel<gather>+decode_merge_kernel",
-                  b_idx + b_sel, t_dsa * 1e3)
+                  b_idx + b_sel, t_dsa * 1e3, "dsa:B8_T65536")
     log(f"[bench] DSA decode: index+top-k {t_topk * 1e3:.1f} us, sparse {t_sparse * 1e3:.1f} us, "
         f"together {t_dsa * 1e3:.1f} us, {r5['achieved']:.0f} GB/s")
     out["dsa"] = {"workload": "K3.1 Gated DSA decode, B=8, cache T=65536 (65537 visible), top-2048",
@@ -247,6 +280,84 @@ def decode_benches(args, d, lw, log):
     return out
 
 
+def counter_pass(log):
+    """--counters: each measured kernel launched twice at the bench's shapes, and a plain device
+    copy of 256 MiB (reads 256 MiB, writes 256 MiB) that calibrates rocprofv3's FETCH_SIZE and
+    WRITE_SIZE, for counter runs (rocprofv3 --pmc ... -- python3 bench.py --counters)."""
+    import torch
+
+    import gated_mla_kv_amd as gm
+    from workloads import K3, device_normal_bf16
+
+    dev = "cuda"
+    d, dd = K3.replace(n_idx_heads=0), K3
+    H, T = d.n_heads, 4096
+    dims, dims5 = gm.make_dims(d), gm.make_dims(dd)
+    src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    log("[counters] copy 256 MiB x2 done")
+    # prefill stages (same calls as the timed stages)
+    x = device_normal_bf16((T, d.hidden), 1.0, 9, 1)
+    w_x = device_normal_bf16((d.q_lora + d.kv_lora + d.d_shared + H * d.d_v, d.hidden), 0.02, 9, 2)
+    out_x = torch.empty((T, w_x.shape[0]), dtype=torch.float32, device=dev)
+    for _ in range(2):
+        gm.mla_gemm(x, d.hidden, w_x, T, w_x.shape[0], d.hidden, out_x, w_x.shape[0], gm.OUT_F32)
+    del out_x, w_x
+    u = device_normal_bf16((T, H * d.d_v), 1.0, 9, 3)
+    w_o = device_normal_bf16((d.hidden, H * d.d_v), 0.02, 9, 4)
+    y = torch.empty((T, d.hidden), dtype=torch.bfloat16, device=dev)
+    for _ in range(2):
+        gm.mla_gemm(u, H * d.d_v, w_o, T, d.hidden, H * d.d_v, y, d.hidden)
+    del u, w_o, y
+    q = device_normal_bf16((1, T, H, d.d_qk), 0.8, 9, 5)
+    K = device_normal_bf16((1, H, T, d.d_qk), 0.8, 9, 6)
+    V = device_normal_bf16((1, H, T, d.d_v), 1.0, 9, 7)
+    g = torch.zeros((1, T, H * d.d_v), device=dev)
+    ua = torch.empty((1, T, H * d.d_v), dtype=torch.bfloat16, device=dev)
+    cache = gm.MlaCache(None, K.data_ptr(), V.data_ptr(), None, 1, T)
+    start = torch.zeros(1, dtype=torch.int32, device=dev)
+    for _ in range(2):
+        gm.mla_prefill_attention(dims, q, cache, start, T, 1, T, g, ua, gm.OUT_BF16, None)
+    torch.cuda.synchronize()
+    del q, K, V, g, ua
+    log("[counters] prefill stages done")
+    # absorbed decode: B=32 x 8193 and B=4 x 131073
+    for B, nv in ((32, 8193), (4, 131073)):
+        lat = device_normal_bf16((B, nv, d.d_latent), 1.0, 9, 8)
+        qt = device_normal_bf16((B, H, d.d_latent), 0.05, 9, 9)
+        c = gm.MlaCache(lat.data_ptr(), None, None, None, B, nv)
+        n = torch.full((B,), nv, dtype=torch.int32, device=dev)
+        o = torch.empty((B, H, d.kv_lora), dtype=torch.float32, device=dev)
+        ws = torch.empty(gm.workspace_bytes(dims, B, 1, nv, gm.PATH_ABSORBED), dtype=torch.uint8, device=dev)
+        for _ in range(2):
+            gm.mla_decode_attention(dims, qt, c, n, nv, B, o, None, 0, ws)
+        torch.cuda.synchronize()
+        del lat, qt, o, ws
+    log("[counters] absorbed decode done")
+    # DSA decode: B=8 x 65537
+    B, nv = 8, 65537
+    lat = device_normal_bf16((B, nv, dd.d_latent), 1.0, 9, 10)
+    idx = device_normal_bf16((B, nv, dd.d_idx), 1.0, 9, 11)
+    qi = device_normal_bf16((B, dd.n_idx_heads, dd.d_idx), 0.5, 9, 12)
+    wi = torch.ones((B, dd.n_idx_heads), device=dev)
+    qt = device_normal_bf16((B, H, dd.d_latent), 0.05, 9, 13)
+    c = gm.MlaCache(lat.data_ptr(), None, None, idx.data_ptr(), B, nv)
+    n = torch.full((B,), nv, dtype=torch.int32, device=dev)
+    sel = torch.empty((B, dd.topk), dtype=torch.int32, device=dev)
+    cnt = torch.empty((B,), dtype=torch.int32, device=dev)
+    o = torch.empty((B, H, dd.kv_lora), dtype=torch.float32, device=dev)
+    ws = torch.empty(gm.workspace_bytes(dims5, B, 1, nv, gm.PATH_SPARSE), dtype=torch.uint8, device=dev)
+    for _ in range(2):
+        gm.dsa_index_topk(dims5, qi, wi, idx, nv, n, nv, B, sel, cnt, None, ws)
+        gm.mla_sparse_attention(dims5, qt, c, sel, cnt, B, o, None, 0, ws)
+    torch.cuda.synchronize()
+    log("[counters] DSA decode done")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -257,11 +368,16 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--decode-iters", type=int, default=20)
+    ap.add_argument("--counters", action="store_true",
+                    help="launch each measured kernel twice (for rocprofv3 --pmc runs) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (sharding is described in "
               "DESIGN.md but not built); run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+    if args.counters:
+        counter_pass(lambda *a: print(*a, file=sys.stderr, flush=True))
+        return
 
     import numpy as np
     import torch
@@ -339,14 +455,17 @@ def main():
     for name, (fn, fl, kern) in stages.items():
         fn()
         torch.cuda.synchronize()
-        stage_ms[name] = median(time_events(fn, iters))
+        stage_ms[name] = time_batched(fn, iters)
         log(f"[bench] {name}: {stage_ms[name]:.3f} ms, {fl / (stage_ms[name] * 1e-3) / 1e12:.1f} TFLOP/s")
     dom = max(stage_ms, key=stage_ms.get)
     dom_fl = stages[dom][1]
     ach = dom_fl / (stage_ms[dom] * 1e-3) / 1e12
+    tkey = {"x_proj_gemm": "prefill:x_proj_gemm", "o_proj_gemm": "prefill:o_proj_gemm",
+            "prefill_attention": "prefill:attention"}.get(dom)
     roofline = {"kernel": stages[dom][2], "stage": dom, "bound": "mfma", "achieved": round(ach, 1),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
-                "traffic": None, "flops_per_launch": dom_fl, "ms_per_launch": round(stage_ms[dom], 4)}
+                "traffic": traffic_for(tkey) if tkey else None, "flops_per_launch": dom_fl,
+                "ms_per_launch": round(stage_ms[dom], 4)}
     kernels = {k: {"ms": round(v, 4), "tflops": round(stages[k][1] / (v * 1e-3) / 1e12, 1)}
                for k, v in stage_ms.items()}
     del out_x, w_x, cq, qb, c, kvb, u, yo, qa, gpre, ua
