@@ -77,7 +77,7 @@ struct Ws {
   uint16_t* kv;    // [M, H*(d_nope+d_v)]
   uint16_t* u;     // [M, H*d_v]
   uint16_t* qt;    // [M, H, kv_lora+d_shared]   (decode)
-  float* part_o;   // [M, S, H, kv_lora]         (decode)
+  uint16_t* part_o;  // [M, S, H, kv_lora] fp16  (decode)
   float* part_ml;  // [M, S, H, 2]
   float* olat;     // [M, H, kv_lora]
   float* z;        // [M, H, d_v]
@@ -110,7 +110,7 @@ Ws carve(const mla_dims* d, int M, bool decode, int max_len, int path, int split
   if (decode) {
     const int S = splits;
     w.qt = cv.take<uint16_t>((size_t)M * H * (d->kv_lora + d->d_shared));
-    w.part_o = cv.take<float>((size_t)M * S * H * d->kv_lora);
+    w.part_o = cv.take<uint16_t>((size_t)M * S * H * d->kv_lora);
     w.part_ml = cv.take<float>((size_t)M * S * H * 2);
     w.olat = cv.take<float>((size_t)M * H * d->kv_lora);
     w.z = cv.take<float>((size_t)M * H * d->d_v);
@@ -359,7 +359,7 @@ static int decode_attention_common(const mla_dims* d, const void* q_tilde, const
   if (span < 1) return MLA_ERR_SHAPE;
   const int splits = auto_splits(B, span, num_splits);
   Carver cv(ws);
-  float* part_o = cv.take<float>((size_t)B * splits * d->n_heads * d->kv_lora);
+  uint16_t* part_o = cv.take<uint16_t>((size_t)B * splits * d->n_heads * d->kv_lora);
   float* part_ml = cv.take<float>((size_t)B * splits * d->n_heads * 2);
   if (cv.off > ws_bytes) return MLA_ERR_WORKSPACE;
   DecodeAttnArgs a{};

@@ -34,6 +34,13 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
 }
 __device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+typedef _Float16 f16x2_ __attribute__((ext_vector_type(2)));
+// two floats -> packed fp16 pair, round to nearest even (lo in bits 0..15)
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_{lo, hi}, f16x2_));
+}
+__device__ __forceinline__ float lo_f16(uint32_t w) { return (float)__builtin_bit_cast(f16x2_, w).x; }
+__device__ __forceinline__ float hi_f16(uint32_t w) { return (float)__builtin_bit_cast(f16x2_, w).y; }
 
 // ---------------------------------------------------------------------------------------
 // MFMA (CDNA4 bf16, fp32 accumulate). Lane layouts (checked on the hardware):

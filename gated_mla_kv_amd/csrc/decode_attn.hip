@@ -15,7 +15,8 @@
 //   head l%32; max/sum need one xor-32 shuffle. P^T (bf16) and the rescale factors go to LDS.
 // * All four waves then accumulate O^T = Lat^T P^T for a quarter of the 512 latent output
 //   features, taking Lat^T straight from the row-major tile with ds_read_b64_tr_b16.
-// * Each split writes unnormalised O and (max, sum) per head; decode_merge combines splits.
+// * Each split writes (max, sum) per head and its output divided by the sum, in fp16 (a convex
+//   combination of latent rows, so bounded by the largest entry); decode_merge combines splits.
 // GATHER (sparse DSA): positions come from the selected list instead of a contiguous range.
 #include "common.h"
 #include "kernels.h"
@@ -189,13 +190,17 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeAttnArgs a) {
     __syncthreads();
   }
 
-  // ---- write this split's partial results ----
+  // ---- write this split's partial results: (max, sum) and O / sum in fp16 ----
   const size_t part = (size_t)b * a.n_splits + split;
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-  if (is_sw && head < C::H && g2 == 0) {
-    a.part_ml[(part * C::H + head) * 2 + 0] = m_run;  // base-2 scaled logits
-    a.part_ml[(part * C::H + head) * 2 + 1] = l_tot;
+  if (is_sw && g2 == 0) {
+    if (head < C::H) {
+      a.part_ml[(part * C::H + head) * 2 + 0] = m_run;  // base-2 scaled logits
+      a.part_ml[(part * C::H + head) * 2 + 1] = l_tot;
+    }
+    alpha_s[head] = l_tot > 0.f ? 1.0f / l_tot : 0.f;  // the loop's last barrier has passed
   }
+  __syncthreads();
 #pragma unroll
   for (int dt = 0; dt < C::DTW; ++dt) {
     const int ft = wave + 4 * dt;
@@ -204,49 +209,81 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeAttnArgs a) {
     for (int hs = 0; hs < C::NSW; ++hs) {
       const int hd = hs * 32 + l32;
       if (hd >= C::H) continue;
-      float* dst = a.part_o + (part * C::H + hd) * C::L;
+      const float inv = alpha_s[hd];
+      uint16_t* dst = a.part_o + (part * C::H + hd) * C::L;
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb) {
         const int f = ft * 32 + rb * 8 + g2 * 4;
         if (f < C::L)
-          *(f32x4*)(dst + f) = f32x4{o[dt][hs][rb * 4 + 0], o[dt][hs][rb * 4 + 1],
-                                     o[dt][hs][rb * 4 + 2], o[dt][hs][rb * 4 + 3]};
+          *(u32x2*)(dst + f) = u32x2{pack_f16x2(o[dt][hs][rb * 4 + 0] * inv, o[dt][hs][rb * 4 + 1] * inv),
+                                     pack_f16x2(o[dt][hs][rb * 4 + 2] * inv, o[dt][hs][rb * 4 + 3] * inv)};
       }
     }
   }
 }
 
-// Combine the splits of one (sequence, head): o = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.
-// One workgroup of 128 threads per (b, h); thread t owns latent features 4t .. 4t+3.
+// Combine the splits of one (sequence, head): with w_s = 2^(m_s - M) l_s over the splits s,
+// o = sum_s w_s O~_s / sum_s w_s, where O~_s is split s's output divided by its own sum l_s.
+// One workgroup of 256 threads per (b, h), b fastest (the XCD of the decode splits of b); wave w
+// takes splits w, w+4, ...; lane l owns latent features 8l .. 8l+7 (16 bytes of fp16 partial).
 template <class S>
-__global__ __launch_bounds__(128) void decode_merge_kernel(DecodeAttnArgs a) {
-  using C = DecodeCfg<S>;
-  static_assert(C::L % 4 == 0 && C::L <= 512, "features per thread");
-  const int bh = blockIdx.x;
-  const int b = bh / C::H, h = bh % C::H;
+__global__ __launch_bounds__(256) void decode_merge_kernel(DecodeAttnArgs a) {
+  constexpr int L = S::L, H = S::H;
+  static_assert(L % 8 == 0 && L <= 512, "eight features per lane, one wave per split");
+  __shared__ float red_m[4], red_d[4];
+  __shared__ f32x4 red_o[4][L / 4];
+  const int b = blockIdx.x % a.B, h = blockIdx.x / a.B;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int ns = a.n_splits;
-  const size_t base = (size_t)b * ns;
-  float M = -INFINITY;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, a.part_ml[((base + s) * C::H + h) * 2]);
+  const float* ml = a.part_ml + ((size_t)b * ns * H + h) * 2;  // split s at ml[s * H * 2]
+  float mx = -INFINITY;
+  for (int s = tid; s < ns; s += 256) mx = fmaxf(mx, ml[(size_t)s * H * 2]);
+  mx = wave_max(mx);
+  if (lane == 0) red_m[wave] = mx;
+  __syncthreads();
+  const float M = fmaxf(fmaxf(red_m[0], red_m[1]), fmaxf(red_m[2], red_m[3]));
+  const int f = lane * 8;
+  const bool own = f < L;
+  const uint16_t* po = a.part_o + ((size_t)b * ns * H + h) * L + f;  // split s at po[s * H * L]
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float den = 0.f;
-  for (int s = 0; s < ns; ++s) {
-    const float m = a.part_ml[((base + s) * C::H + h) * 2];
-    if (m != -INFINITY) den += fast_exp2(m - M) * a.part_ml[((base + s) * C::H + h) * 2 + 1];
-  }
-  const float inv = den > 0.f ? 1.0f / den : 0.f;  // no visible position: zeros
-  const int f = threadIdx.x * 4;
-  if (f < C::L) {
-    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < ns; ++s) {
-      const float m = a.part_ml[((base + s) * C::H + h) * 2];
-      if (m == -INFINITY) continue;
-      const float wgt = fast_exp2(m - M);
-      const f32x4 v = *(const f32x4*)(a.part_o + ((base + s) * C::H + h) * C::L + f);
-      acc += wgt * v;
+  constexpr int U = 4;  // splits in flight per wave
+  for (int s0 = wave; s0 < ns; s0 += 4 * U) {
+    u32x4 v[U];
+    float wgt[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int s = s0 + 4 * u;
+      const bool ok = s < ns;
+      const float m = ok ? ml[(size_t)s * H * 2] : -INFINITY;
+      const float l = ok ? ml[(size_t)s * H * 2 + 1] : 0.f;
+      wgt[u] = m == -INFINITY ? 0.f : fast_exp2(m - M) * l;
+      v[u] = (ok && own) ? ld16(po + (size_t)s * H * L) : zero16();
     }
-    *(f32x4*)(a.o_latent + ((size_t)b * C::H + h) * C::L + f) = acc * inv;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      den += wgt[u];
+      const uint32_t w4[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[2 * e] += wgt[u] * lo_f16(w4[e]);
+        acc[2 * e + 1] += wgt[u] * hi_f16(w4[e]);
+      }
+    }
   }
-  if (threadIdx.x == 0 && a.lse) a.lse[(size_t)b * C::H + h] = (M + __log2f(den)) * 0.6931471805599453f;
+  if (own) {
+    red_o[wave][lane * 2] = f32x4{acc[0], acc[1], acc[2], acc[3]};
+    red_o[wave][lane * 2 + 1] = f32x4{acc[4], acc[5], acc[6], acc[7]};
+  }
+  if (lane == 0) red_d[wave] = den;
+  __syncthreads();
+  const float dtot = red_d[0] + red_d[1] + red_d[2] + red_d[3];
+  const float inv = dtot > 0.f ? 1.0f / dtot : 0.f;  // no visible position: zeros
+  if (tid < L / 4) {
+    const f32x4 o = (red_o[0][tid] + red_o[1][tid] + red_o[2][tid] + red_o[3][tid]) * inv;
+    *(f32x4*)(a.o_latent + ((size_t)b * H + h) * L + tid * 4) = o;
+  }
+  if (tid == 0 && a.lse) a.lse[(size_t)b * H + h] = (M + __log2f(dtot)) * 0.6931471805599453f;
 }
 
 // q~[b,h,:L] = W^K_h^T q_nope[b,h], q~[b,h,L:] = q_shared[b,h]  (fp32 accumulate, bf16 out).
@@ -357,7 +394,7 @@ static hipError_t launch_decode_t(const DecodeAttnArgs& a, bool gather, hipStrea
   } else {
     decode_attn_kernel<S, false><<<grid, 256, 0, st>>>(a);
   }
-  decode_merge_kernel<S><<<a.B * S::H, 128, 0, st>>>(a);
+  decode_merge_kernel<S><<<a.B * S::H, 256, 0, st>>>(a);
   return hipGetLastError();
 }
 

@@ -22,6 +22,9 @@
 // * The running max is only moved when it grows by more than 8 (base 2): otherwise the old
 //   max stays and the rescale factor is exactly 1, so the accumulators are rarely rescaled.
 //   The result is the same softmax; only the reference point of the exponentials differs.
+// * Each split writes its output divided by its own softmax sum, in fp16: a convex combination
+//   of cached rows, so bounded by the largest latent entry, at half the bytes of fp32 partials
+//   (11-bit significand; the merge weights them by 2^(m - M) * l in fp32).
 #include "common.h"
 #include "kernels.h"
 
@@ -69,7 +72,9 @@ __global__ __launch_bounds__(k3dec::NTHREADS) void decode_attn_k3_kernel(DecodeA
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g2 = lane >> 5, l32 = lane & 31;
-  const int b = blockIdx.x / a.n_splits, split = blockIdx.x % a.n_splits;
+  // consecutive workgroups take different sequences, so that (with B a multiple of 8) all splits of
+  // a sequence run on one XCD and share its L2 for q~ and, in the merge, for the partials
+  const int b = blockIdx.x % a.B, split = blockIdx.x / a.B;
   const int n_vis = GATHER ? min(a.sel_cnt[b], a.sel_stride) : min(a.n_vis[b] + a.vis_offset, a.T_cap);
   const int p0 = split * a.chunk;
   const int p1 = min(p0 + a.chunk, n_vis);
@@ -177,7 +182,9 @@ __global__ __launch_bounds__(k3dec::NTHREADS) void decode_attn_k3_kernel(DecodeA
     if (g2 == 0) {
       a.part_ml[(part * H + head) * 2 + 0] = m_run;
       a.part_ml[(part * H + head) * 2 + 1] = l_tot;
+      alpha_s[0][head] = l_tot > 0.f ? 1.0f / l_tot : 0.f;  // no longer read as a rescale factor
     }
+    __syncthreads();  // 1/l of every head is in LDS
   } else {
     // ---------------- P.V waves: latent features [pw*128, pw*128 + 128) ----------------
     const int pw = wave - 3;
@@ -269,16 +276,19 @@ __global__ __launch_bounds__(k3dec::NTHREADS) void decode_attn_k3_kernel(DecodeA
       if (t + 2 < n_tiles) wait_for(t + 2, issued);  // the score waves read it in the next step
       __syncthreads();
     }
+    __syncthreads();  // 1/l of every head is in LDS
 #pragma unroll
     for (int hs = 0; hs < 3; ++hs) {
-      float* dst = a.part_o + (part * H + hs * 32 + l32) * L;
+      const float inv = alpha_s[0][hs * 32 + l32];
+      uint16_t* dst = a.part_o + (part * H + hs * 32 + l32) * L;
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
         for (int rb = 0; rb < 4; ++rb) {
           const int f = (pw * 4 + dt) * 32 + rb * 8 + g2 * 4;
-          *(f32x4*)(dst + f) = f32x4{o[dt][hs][rb * 4 + 0], o[dt][hs][rb * 4 + 1], o[dt][hs][rb * 4 + 2],
-                                     o[dt][hs][rb * 4 + 3]};
+          const f32x4 v = f32x4{o[dt][hs][rb * 4 + 0], o[dt][hs][rb * 4 + 1], o[dt][hs][rb * 4 + 2],
+                                o[dt][hs][rb * 4 + 3]} * inv;
+          *(u32x2*)(dst + f) = u32x2{pack_f16x2(v[0], v[1]), pack_f16x2(v[2], v[3])};
         }
     }
   }

@@ -54,7 +54,7 @@ struct DecodeAttnArgs {
   int sel_stride;
   int B, T_cap, n_splits, chunk;
   float scale;
-  float* part_o;    // [B, n_splits, H, L]
+  uint16_t* part_o; // [B, n_splits, H, L] fp16: each split's output divided by its own sum l
   float* part_ml;   // [B, n_splits, H, 2]
   float* o_latent;  // [B, H, L]
   float* lse;       // [B, H] or null

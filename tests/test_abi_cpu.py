@@ -57,7 +57,7 @@ def test_workspace_bytes():
     pre = gm.workspace_bytes(d, 1, 4096, 4096)
     assert pre > 4096 * 12288 * 2  # at least the gated head outputs
     dec = gm.workspace_bytes(d, 32, 1, 8193, gm.PATH_ABSORBED)
-    assert dec > 32 * 8 * 96 * 512 * 4  # split partials
+    assert dec > 32 * 8 * 96 * 512 * 2  # split partials (fp16)
     assert gm.workspace_bytes(d, 32, 1, 8193, gm.PATH_ABSORBED, 16) > dec
     assert gm.workspace_bytes(gm.make_dims(K3.replace(n_heads=8)), 1, 1, 10) == 0
 
