@@ -69,30 +69,33 @@ __device__ __forceinline__ float k3_max_xor32(float x) {
 
 template <int V> using ic = std::integral_constant<int, V>;
 
+// Key tiles of the job (bh, qt): tiles [0, n) of keys [0, kv_end), kv_end = min(n_keys, last row's
+// position + 1).
+__device__ __forceinline__ int k3_job_tiles(const PrefillAttnArgs& a, int bh, int qt, int* n_keys_out) {
+  using namespace k3pre;
+  const int start = a.start[bh / H];
+  const int n_keys = min(start + a.T, a.T_cap);
+  *n_keys_out = n_keys;
+  return cdiv(min(n_keys, start + min(a.T, qt * BQ + BQ)), BKV);
+}
+
+// One (b*H + h, query tile) job of a workgroup; `ring` is the workgroup's K/V ring. Every LDS
+// read of a job happens before its last barrier, so jobs can follow each other without one.
+// With `ahead` the job's first three K/V tiles are already in flight (issued by the previous job
+// of this workgroup); with next_bh >= 0 this job issues the first tiles of job (next_bh, next_qt)
+// into the free ring right after its last barrier, ahead of its own epilogue.
 template <int QB>
-__global__ __launch_bounds__(k3pre::Cfg<QB>::NT) void prefill_attn_k3_kernel(PrefillAttnArgs a) {
+__device__ __forceinline__ void prefill_k3_job(const PrefillAttnArgs& a, uint8_t* ring, const int bh,
+                                               const int qt, const bool ahead, const int next_bh,
+                                               const int next_qt) {
   using namespace k3pre;
   using C = Cfg<QB>;
   constexpr int NW = C::NW, WROWS = C::WROWS, NLOAD_W = C::NLOAD_W, NKOFS = C::NKOFS;
   (void)NW;
-  __shared__ __attribute__((aligned(1024))) uint8_t ring[NSLOT * SLOT];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g2 = lane >> 5, l32 = lane & 31;
-
-  // ---- workgroup -> (b, h, query tile) ----
-  const int nqt = cdiv(a.T, BQ);
-  const int BH = a.B * H;
-  int bh, qt;
-  if (BH % 8 == 0) {
-    const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
-    bh = (local / nqt) * 8 + xcd;
-    qt = nqt - 1 - (local % nqt);
-  } else {
-    bh = blockIdx.x % BH;
-    qt = nqt - 1 - blockIdx.x / BH;
-  }
   const int b = bh / H, h = bh % H;
   const int start = a.start[b];
   const int n_keys = min(start + a.T, a.T_cap);
@@ -132,13 +135,15 @@ __global__ __launch_bounds__(k3pre::Cfg<QB>::NT) void prefill_attn_k3_kernel(Pre
   }
   const uint32_t vofs = (uint32_t)v_src(lane);
   const uint32_t ring_lds = lds_addr(ring) + wave * NLOAD_W * 1024;
-  auto issue = [&](int t) __attribute__((always_inline)) {
-    if (t >= n_tiles) return;
+  // tile t of the job whose K/V rows start at kbase_/vbase_ (n_keys_ keys, n_tiles_ tiles)
+  auto issue_for = [&](const uint16_t* kbase_, const uint16_t* vbase_, int n_keys_, int n_tiles_,
+                       int t) __attribute__((always_inline)) {
+    if (t >= n_tiles_) return;
     const uint32_t sa = ring_lds + (t % NSLOT) * SLOT;
     const int j0 = t * BKV;
-    const uint8_t* kb = (const uint8_t*)(kbase + (size_t)j0 * DQK);
-    const uint8_t* vb = (const uint8_t*)(vbase + (size_t)j0 * DV);
-    if (j0 + BKV <= n_keys) {
+    const uint8_t* kb = (const uint8_t*)(kbase_ + (size_t)j0 * DQK);
+    const uint8_t* vb = (const uint8_t*)(vbase_ + (size_t)j0 * DV);
+    if (j0 + BKV <= n_keys_) {
 #pragma unroll
       for (int k = 0; k < NLOAD_W; ++k) {
         const int i = wave * NLOAD_W + k;
@@ -148,7 +153,7 @@ __global__ __launch_bounds__(k3pre::Cfg<QB>::NT) void prefill_attn_k3_kernel(Pre
           lds_dma16_sbase(vofs, vb + (i - NLOAD_K) * 1024, sa + k * 1024);
       }
     } else {  // last tile: rows past the end re-read the last key (masked later)
-      const int rmax = n_keys - 1 - j0;
+      const int rmax = n_keys_ - 1 - j0;
 #pragma unroll 1
       for (int k = 0; k < NLOAD_W; ++k) {
         const int i = wave * NLOAD_W + k;
@@ -161,6 +166,7 @@ __global__ __launch_bounds__(k3pre::Cfg<QB>::NT) void prefill_attn_k3_kernel(Pre
       }
     }
   };
+  auto issue = [&](int t) __attribute__((always_inline)) { issue_for(kbase, vbase, n_keys, n_tiles, t); };
 
   // ---- q fragments (B operand): query rows wrow0 + 32 qb + l32, features 16 s + 8 g2 .. +8 ----
   u32x4 qf[QB][KS];
@@ -171,9 +177,11 @@ __global__ __launch_bounds__(k3pre::Cfg<QB>::NT) void prefill_attn_k3_kernel(Pre
 #pragma unroll
     for (int s = 0; s < KS; ++s) qf[qb][s] = ld16(qrow + s * 16);
   }
-  issue(0);
-  issue(1);
-  issue(2);
+  if (!ahead) {
+    issue(0);
+    issue(1);
+    issue(2);
+  }
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
@@ -322,7 +330,10 @@ __global__ __launch_bounds__(k3pre::Cfg<QB>::NT) void prefill_attn_k3_kernel(Pre
   };
 
   // ---- prologue: tile 0 -> scores of sub-tiles 0 and 1, softmax of 0 ----
-  if (n_tiles >= 3)
+  // (tiles issued ahead precede this job's q loads in the wave's memory queue: wait for all)
+  if (ahead)
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  else if (n_tiles >= 3)
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * NLOAD_W) : "memory");
   else if (n_tiles == 2)
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NLOAD_W) : "memory");
@@ -333,7 +344,9 @@ __global__ __launch_bounds__(k3pre::Cfg<QB>::NT) void prefill_attn_k3_kernel(Pre
   scores(1, ic<1>{});
   if (mv == 0) apply_mask(0, ic<0>{});
   softmax(0, ic<0>{});  // alpha = 0 here, on accumulators that are still 0
-  if (n_tiles >= 3)
+  if (ahead)
+    ;
+  else if (n_tiles >= 3)
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NLOAD_W) : "memory");
   else
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -348,6 +361,17 @@ __global__ __launch_bounds__(k3pre::Cfg<QB>::NT) void prefill_attn_k3_kernel(Pre
     issue(t + 3);
   }
 
+  // ---- the next job's first tiles: the ring is free once every wave has passed the barrier ----
+  if (next_bh >= 0) {
+    int nk;
+    const int nt = k3_job_tiles(a, next_bh, next_qt, &nk);
+    const uint16_t* kb = a.k + (size_t)next_bh * a.T_cap * DQK;
+    const uint16_t* vb = a.v + (size_t)next_bh * a.T_cap * DV;
+    issue_for(kb, vb, nk, nt, 0);
+    issue_for(kb, vb, nk, nt, 1);
+    issue_for(kb, vb, nk, nt, 2);
+  }
+
   // ---- epilogue: normalise, gate, store ----
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
@@ -358,6 +382,14 @@ __global__ __launch_bounds__(k3pre::Cfg<QB>::NT) void prefill_attn_k3_kernel(Pre
     if (a.lse && g2 == 0)
       a.lse[((size_t)b * H + h) * a.T + qi] = (m_run[qb] + __log2f(l_tot)) * 0.6931471805599453f;
     const size_t urow = ((size_t)b * a.T + qi) * (H * DV) + (size_t)h * DV;
+    // all gate loads first (16 per lane), so their latencies overlap
+    f32x4 gv[4][4];
+    if (a.g_pre) {
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) gv[d][rb] = *(const f32x4*)(a.g_pre + urow + d * 32 + rb * 8 + g2 * 4);
+    }
 #pragma unroll
     for (int d = 0; d < 4; ++d)
 #pragma unroll
@@ -367,9 +399,8 @@ __global__ __launch_bounds__(k3pre::Cfg<QB>::NT) void prefill_attn_k3_kernel(Pre
 #pragma unroll
         for (int i = 0; i < 4; ++i) z[i] = o[d][qb][rb * 4 + i] * inv_l;
         if (a.g_pre) {
-          const f32x4 gv = *(const f32x4*)(a.g_pre + urow + dv);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) z[i] *= sigmoidf_(gv[i]);
+          for (int i = 0; i < 4; ++i) z[i] *= sigmoidf_(gv[d][rb][i]);
         }
         if (a.u_f32)
           *(f32x4*)((float*)a.u + urow + dv) = f32x4{z[0], z[1], z[2], z[3]};
@@ -379,11 +410,73 @@ __global__ __launch_bounds__(k3pre::Cfg<QB>::NT) void prefill_attn_k3_kernel(Pre
   }
 }
 
+// Work distribution. A query tile qt costs qt + 1 key tiles, so the tiles of one (b, h) pair up
+// as (nqt-1-j, j) at nqt + 1 each. With n_wg > 0 the grid is n_wg persistent workgroups (a
+// multiple of 8, about one per CU) that take pairs p = blockIdx.x, blockIdx.x + n_wg, ...: every
+// workgroup gets the same number of equal pairs. Pair p serves b*H + h = 8*(p/8 / (nqt/2)) + p%8,
+// so a workgroup (on XCD blockIdx.x % 8) only meets the heads of its own XCD, four at a time,
+// whose K/V rows stay in that XCD's L2. With n_wg == 0 (odd nqt or B*H not a multiple of 8)
+// there is one workgroup per query tile, ordered so each XCD walks one head at a time, longest
+// query tiles first.
+template <int QB>
+__global__ __launch_bounds__(k3pre::Cfg<QB>::NT) void prefill_attn_k3_kernel(PrefillAttnArgs a, int n_wg) {
+  using namespace k3pre;
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[NSLOT * SLOT];
+  const int nqt = cdiv(a.T, BQ);
+  const int BH = a.B * H;
+  if (n_wg > 0) {
+    const int half = nqt / 2, n_pairs = BH * half;
+    for (int p = blockIdx.x; p < n_pairs; p += n_wg) {
+      const int xcd = p & 7, local = p >> 3;
+      const int bh = (local / half) * 8 + xcd, j = local % half;
+#pragma unroll 1
+      for (int k = 0; k < 2; ++k) {
+        // the job after this one: the pair's second tile, else the first tile of the next pair
+        int nbh = bh, nq = j;
+        if (k == 1) {
+          const int pn = p + n_wg;
+          nbh = -1;
+          if (pn < n_pairs) {
+            const int ln = pn >> 3;
+            nbh = (ln / half) * 8 + (pn & 7);
+            nq = nqt - 1 - ln % half;
+          }
+        }
+        prefill_k3_job<QB>(a, ring, bh, k == 0 ? nqt - 1 - j : j, !(p == (int)blockIdx.x && k == 0), nbh, nq);
+      }
+    }
+    return;
+  }
+  int bh, qt;
+  if (BH % 8 == 0) {
+    const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
+    bh = (local / nqt) * 8 + xcd;
+    qt = nqt - 1 - (local % nqt);
+  } else {
+    bh = blockIdx.x % BH;
+    qt = nqt - 1 - blockIdx.x / BH;
+  }
+  prefill_k3_job<QB>(a, ring, bh, qt, false, -1, 0);
+}
+
 hipError_t launch_prefill_attention_k3(const PrefillAttnArgs& a, hipStream_t st) {
-  const int nqt = cdiv(a.T, k3pre::BQ);
+  using namespace k3pre;
+  const int nqt = cdiv(a.T, BQ);
+  const int BH = a.B * H;
+  int dev = 0, n_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n_cu < 8)
+    n_cu = 8;
   // one 32-row block per wave, two waves per SIMD: the second wave's MFMAs cover this wave's
   // softmax (the one-wave-per-SIMD form needs more than 512 registers per lane at 64 rows)
-  prefill_attn_k3_kernel<1><<<a.B * k3pre::H * nqt, k3pre::Cfg<1>::NT, 0, st>>>(a);
+  if (nqt % 2 == 0 && BH % 8 == 0) {
+    const int n_pairs = BH * (nqt / 2);
+    int n_wg = n_cu / 8 * 8;
+    if (n_wg > n_pairs) n_wg = n_pairs;  // n_pairs is a multiple of 8
+    prefill_attn_k3_kernel<1><<<n_wg, Cfg<1>::NT, 0, st>>>(a, n_wg);
+  } else {
+    prefill_attn_k3_kernel<1><<<BH * nqt, Cfg<1>::NT, 0, st>>>(a, 0);
+  }
   return hipGetLastError();
 }
 
