@@ -84,6 +84,7 @@ struct Ws {
   float* scores;   // [M, max_len]
   int32_t* sel;    // [M, topk]
   int32_t* cnt;    // [M]
+  int32_t* topk_scratch;  // index_topk_scratch_words(M, max_len)
   void* gemm_ws;
   size_t gemm_ws_bytes;
   size_t total;
@@ -118,6 +119,7 @@ Ws carve(const mla_dims* d, int M, bool decode, int max_len, int path, int split
       w.scores = cv.take<float>((size_t)M * max_len);
       w.sel = cv.take<int32_t>((size_t)M * d->topk);
       w.cnt = cv.take<int32_t>((size_t)M);
+      w.topk_scratch = cv.take<int32_t>(index_topk_scratch_words(M, max_len));
     }
   }
   // split-K partials of the small-M GEMMs (the largest of the layer's GEMMs)
@@ -490,14 +492,16 @@ int dsa_index_topk(const mla_dims* d, const void* q_idx, const float* w_idx, con
   if (B == 0) return MLA_OK;
   if (!q_idx || !w_idx || !idx_k_cache || !n_visible || !out_idx || !out_cnt) return MLA_ERR_NULL;
   if (max_visible > T_cap) return MLA_ERR_CAPACITY;
+  if (!ws) return MLA_ERR_NULL;
+  Carver cv(ws);
   float* scores = out_scores;
   int stride = T_cap;
   if (!scores) {
-    if (!ws) return MLA_ERR_NULL;
-    if (ws_bytes < (size_t)B * max_visible * sizeof(float)) return MLA_ERR_WORKSPACE;
-    scores = (float*)ws;
-    stride = max_visible;
+    stride = max_visible > 0 ? max_visible : 1;
+    scores = cv.take<float>((size_t)B * stride);
   }
+  int32_t* scratch = cv.take<int32_t>(index_topk_scratch_words(B, stride));
+  if (cv.off > ws_bytes) return MLA_ERR_WORKSPACE;
   IndexScoreArgs sa{};
   sa.q_idx = (const uint16_t*)q_idx;
   sa.w_idx = w_idx;
@@ -508,7 +512,6 @@ int dsa_index_topk(const mla_dims* d, const void* q_idx, const float* w_idx, con
   sa.scale = 1.0f / sqrtf((float)(d->n_idx_heads * d->d_idx));
   sa.scores = scores;
   sa.score_stride = stride;
-  CHECK_HIP(launch_index_scores(sa, max_visible, stream));
   TopkArgs ta{};
   ta.scores = scores;
   ta.score_stride = stride;
@@ -518,7 +521,7 @@ int dsa_index_topk(const mla_dims* d, const void* q_idx, const float* w_idx, con
   ta.out_idx = out_idx;
   ta.out_stride = d->topk;
   ta.out_cnt = out_cnt;
-  CHECK_HIP(launch_topk(ta, stream));
+  CHECK_HIP(launch_index_topk(sa, max_visible, ta, scratch, stream));
   return MLA_OK;
 }
 
@@ -720,7 +723,6 @@ int mla_decode(const mla_dims* d, const mla_weights* w, const mla_cache* cache, 
       sa.scale = 1.0f / sqrtf((float)(d->n_idx_heads * d->d_idx));
       sa.scores = wsp.scores;
       sa.score_stride = max_len;
-      CHECK_HIP(launch_index_scores(sa, max_len, stream));
       TopkArgs ta{};
       ta.scores = wsp.scores;
       ta.score_stride = max_len;
@@ -731,7 +733,7 @@ int mla_decode(const mla_dims* d, const mla_weights* w, const mla_cache* cache, 
       ta.out_idx = sel;
       ta.out_stride = d->topk;
       ta.out_cnt = cnt;
-      CHECK_HIP(launch_topk(ta, stream));
+      CHECK_HIP(launch_index_topk(sa, max_len, ta, wsp.topk_scratch, stream));
     }
     CHECK_HIP(launch_absorb_q(s, wsp.q, H * dqk, (const uint16_t*)w->w_kv_b, B, wsp.qt, stream));
     DecodeAttnArgs a{};

@@ -8,14 +8,18 @@
 // head-weighted ReLU sum is in-lane plus one xor-32 shuffle. 1/sqrt(32*128) = 1/64 is folded
 // into a exactly.
 //
-// topk_kernel (eq. (6)): S = the min(k, t) largest I, ties to the lower position, -0 == +0,
-// written in ascending position order. One workgroup per query row. A radix select over
-// order-preserving 32-bit keys with 12-, 12- and 8-bit digits (the row's keys held in registers,
-// LDS histograms) narrows the
-// k-th largest key down until a whole bin is taken or the key tau is exact. The compaction gives
-// each wave a contiguous run of positions: a counting pass, a scan of the 16 wave counts, and a
-// writing pass with ballot prefix counts, so the output is ascending by construction and the
-// copies of tau kept are the lowest-position ones.
+// Top-k (eq. (6)): S = the min(k, t) largest I, ties to the lower position, -0 == +0, written
+// in ascending position order, over order-preserving 32-bit keys of the fp32 scores.
+// * index_scores_kernel also counts the top 12-bit digit of every key into the row's histogram.
+// * topk_select_kernel (one workgroup per row) takes the bin where the count from the top reaches
+//   k, sorts that bin's keys (with their positions) in LDS, and fixes the threshold key and the
+//   last kept position among its copies; it scans the per-2048-position-chunk kept counts into
+//   output offsets.
+// * topk_compact_kernel (one workgroup per chunk) writes each chunk's kept positions in order.
+// * A row whose boundary bin exceeds the LDS candidate buffer (e.g. thousands of equal scores)
+//   runs the whole selection in its select workgroup instead: a radix select over 12-, 12- and
+//   8-bit digits with the row's keys in registers, and an ordered compaction in which every
+//   wave owns a contiguous run of positions.
 //
 // expanded_attn_kernel: one query per (b, h) against the expanded cache k [B,H,T_cap,192],
 // v [B,H,T_cap,128] (KV cache card): 61,440 bytes per position, HBM bound at ~1 flop per byte,
@@ -31,14 +35,19 @@ namespace gmla {
 // ------------------------------------------------------------------------------------------
 constexpr int kScorePosPerWG = 256;
 
+__device__ __forceinline__ uint32_t order_key(float f);
+constexpr int kHistBins = 4096;  // first radix digit: the top 12 bits of the order key
+
 __global__ __launch_bounds__(256) void index_scores_kernel(IndexScoreArgs a) {
   constexpr int NIH = 32, DI = 128, KS = DI / 16;
+  __shared__ int lhist[kHistBins];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g2 = lane >> 5, l32 = lane & 31;
   const int b = blockIdx.y;
   const int t = min(min(a.n_vis[b] + a.vis_offset, a.T_cap), a.score_stride);
   const int base = blockIdx.x * kScorePosPerWG;
   if (base >= t) return;
+  for (int i = threadIdx.x; i < kHistBins; i += 256) lhist[i] = 0;
   const int end = min(base + kScorePosPerWG, t);
   const uint16_t* kb = a.idx_k + (size_t)b * a.T_cap * DI;
   // keys of this wave's positions p0 + l32 (two 32-position steps per wave), both loads in flight
@@ -69,10 +78,26 @@ __global__ __launch_bounds__(256) void index_scores_kernel(IndexScoreArgs a) {
     for (int r = 0; r < 16; ++r) sc += wgt[r] * fmaxf(acc[r], 0.f);
     sc += __shfl_xor(sc, 32, 64);
     const int pos = p0 + l32;
-    if (pos < end && g2 == 0) a.scores[(size_t)b * a.score_stride + pos] = sc;
+    if (pos < end && g2 == 0) {
+      a.scores[(size_t)b * a.score_stride + pos] = sc;
+      atomicAdd(&lhist[order_key(sc) >> 20], 1);
+    }
   };
+  __syncthreads();  // histogram cleared
   if (p0a < end) score(p0a, kfa);
   if (p0b < end) score(p0b, kfb);
+  __syncthreads();
+  // the row's histogram gathers the workgroup's nonzero bins
+  int* gh = a.hist + (size_t)b * kHistBins;
+  for (int i = threadIdx.x; i < kHistBins; i += 256) {
+    const int c = lhist[i];
+    if (c) atomicAdd(&gh[i], c);
+  }
+}
+
+__global__ void zero_words_kernel(int32_t* p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0;
 }
 
 // ------------------------------------------------------------------------------------------
@@ -128,13 +153,16 @@ constexpr int kHistPitch = 4097;   // replica stride in words (not a multiple of
 // Positions past the row hold key 0. A real score never maps to a key below 2^20 (those are NaN
 // bit patterns), so key 0 sits in digit-0 bin 0, under any threshold, and no pass needs a
 // bounds test.
-__global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
-  __shared__ int hist[kHistRep * kHistPitch];
-  __shared__ int scan_tmp[kTopkThreads / 64 + 1];
-  __shared__ int sh_bin, sh_above, sh_cnt;
-  __shared__ int wcnt[2][kTopkWaves];
+// The whole selection of row b inside one workgroup: the general path, for rows whose boundary
+// bin holds more candidates than the chunked path keeps in LDS, or longer than it covers.
+// hist: kHistRep * kHistPitch ints of LDS; scan_tmp: kTopkWaves + 1; shv: 3; wcnt: 2 * kTopkWaves.
+__device__ __forceinline__ void topk_full_row(const TopkArgs& a, const int b, int* hist, int* scan_tmp,
+                                           int* shv, int* wcnt_flat) {
+  int& sh_bin = shv[0];
+  int& sh_above = shv[1];
+  int& sh_cnt = shv[2];
+  int(*wcnt)[kTopkWaves] = (int(*)[kTopkWaves])wcnt_flat;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int b = blockIdx.x;
   const int t = min(a.n_vis[b] + a.vis_offset, a.score_stride);
   const int k = min(a.k, t);
   int32_t* out = a.out_idx + (size_t)b * a.out_stride;
@@ -277,6 +305,261 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
   if (tid == 0) a.out_cnt[b] = k;
 }
 
+
+// ---- chunked path ----
+// The score kernel leaves each row's histogram of the 12-bit top digit. topk_select_kernel (one
+// workgroup per row) finds the bin b0 where the count from the top reaches k, collects the keys
+// of that bin (with their positions) in LDS, and radix-selects among them the threshold key thr
+// (the krem-th largest, krem = k minus the count above b0) and, when only some of its copies
+// are kept, the last kept position p_lim (the copies' positions radix-selected in turn).
+// A position is kept iff key > thr, or key == thr and position <= p_lim.
+// It also counts the kept positions of every 2048-position chunk and writes their exclusive scan.
+// topk_compact_kernel (one workgroup per chunk) then writes its chunk's kept positions in order
+// at that offset, so the output is ascending.
+constexpr int kChunk = 2048;        // positions per compaction workgroup
+constexpr int kMaxChunks = 1024;    // the chunked path covers rows of up to 2,097,152 positions
+constexpr int kCandCap = 8192;      // boundary-bin keys held in LDS
+enum { kSelDone = 0, kSelChunked = 1 };
+constexpr int kSelLds = kHistRep * kHistPitch * 4 > kCandCap * 12 + kHistBins * 4
+                            ? kHistRep * kHistPitch * 4 : kCandCap * 12 + kHistBins * 4;
+
+// The r-th largest (1 <= r <= n) of the 32-bit values vals[0, n) in LDS, for the whole
+// workgroup: three radix levels (12, 12 and 8 bits from the top) over an LDS histogram of 4096
+// ints. *n_gt receives the count of values above it, *n_eq the count equal to it.
+__device__ __forceinline__ uint32_t block_select_desc(const uint32_t* vals, int n, int r, int* hist,
+                                                      int* scan_tmp, int* shv, int* n_gt, int* n_eq) {
+  const int tid = threadIdx.x;
+  uint32_t prefix = 0, pmask = 0;
+  int gt = 0, eq = 0;
+#pragma unroll 1
+  for (int level = 0; level < 3; ++level) {
+    const int shift = level == 0 ? 20 : (level == 1 ? 8 : 0);
+    const int nbins = level == 2 ? 256 : 4096;
+    for (int i = tid; i < kHistBins; i += kTopkThreads) hist[i] = 0;
+    __syncthreads();
+    for (int i = tid; i < n; i += kTopkThreads) {
+      const uint32_t v = vals[i];
+      if ((v & pmask) == prefix) atomicAdd(&hist[(v >> shift) & (uint32_t)(nbins - 1)], 1);
+    }
+    __syncthreads();
+    constexpr int PER = kHistBins / kTopkThreads;
+    const int top = nbins - 1 - PER * tid;
+    int cntb[PER];
+    int local = 0;
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      cntb[q] = top - q >= 0 ? hist[top - q] : 0;
+      local += cntb[q];
+    }
+    int total;
+    const int before = block_exclusive_scan<kTopkThreads>(local, scan_tmp, total);
+    const int rr = r - gt;
+    if (before < rr && before + local >= rr) {
+      int cum = before;
+#pragma unroll
+      for (int q = 0; q < PER; ++q) {
+        if (cum < rr && cum + cntb[q] >= rr) {
+          shv[0] = top - q;
+          shv[1] = cum;
+          shv[2] = cntb[q];
+        }
+        cum += cntb[q];
+      }
+    }
+    __syncthreads();
+    prefix |= (uint32_t)shv[0] << shift;
+    pmask |= (uint32_t)(nbins - 1) << shift;
+    gt += shv[1];
+    eq = shv[2];
+    __syncthreads();
+  }
+  *n_gt = gt;
+  *n_eq = eq;
+  return prefix;
+}
+
+__global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(TopkArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t big[kSelLds];  // full-row histograms | candidates
+  __shared__ int scan_tmp[kTopkWaves + 1];
+  __shared__ int shv[4];
+  __shared__ int wcnt[2 * kTopkWaves];
+  __shared__ int ccnt[kMaxChunks];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int b = blockIdx.x;
+  const int t = min(a.n_vis[b] + a.vis_offset, a.score_stride);
+  const int k = min(a.k, t);
+  int32_t* sel = a.sel + (size_t)b * 4;
+  int32_t* out = a.out_idx + (size_t)b * a.out_stride;
+  const float* sc = a.scores + (size_t)b * a.score_stride;
+  if (t <= a.k) {  // short history: every visible position is kept
+    for (int i = tid; i < a.k; i += kTopkThreads) out[i] = (i < t) ? i : -1;
+    if (tid == 0) {
+      a.out_cnt[b] = t;
+      sel[0] = kSelDone;
+    }
+    return;
+  }
+  const int nch = cdiv(t, kChunk);
+  // ---- the bin where the count from the top reaches k: thread j owns bins 4095-4j .. -3 ----
+  const int* gh = a.hist + (size_t)b * kHistBins;
+  constexpr int PER = kHistBins / kTopkThreads;
+  const int top = kHistBins - 1 - PER * tid;
+  int cntb[PER];
+  int local = 0;
+#pragma unroll
+  for (int q = 0; q < PER; ++q) {
+    cntb[q] = gh[top - q];
+    local += cntb[q];
+  }
+  int total;
+  const int before = block_exclusive_scan<kTopkThreads>(local, scan_tmp, total);
+  if (before < k && before + local >= k) {
+    int cum = before;
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      if (cum < k && cum + cntb[q] >= k) {
+        shv[0] = top - q;
+        shv[1] = cum;
+        shv[2] = cntb[q];
+      }
+      cum += cntb[q];
+    }
+  }
+  if (tid == 0) shv[3] = 0;
+  __syncthreads();
+  const uint32_t b0 = (uint32_t)shv[0];
+  const int krem = k - shv[1];
+  const int c0 = shv[2];
+  if (c0 > kCandCap || nch > kMaxChunks) {
+    __syncthreads();
+    topk_full_row(a, b, (int*)big, scan_tmp, shv, wcnt);
+    if (tid == 0) sel[0] = kSelDone;
+    return;
+  }
+  // ---- one pass over the row: chunk counts above b0, and the keys of bin b0 with their
+  // positions. Wave w owns the chunks w, w + 16, ...: it counts each alone, then reserves room
+  // for its candidates with one LDS atomic ----
+  uint32_t* ckey = (uint32_t*)big;         // [kCandCap]
+  int* cpos = (int*)(ckey + kCandCap);     // [kCandCap]
+  int* lh = cpos + kCandCap;               // [kHistBins] histogram of the candidate selections
+  uint32_t* tv = (uint32_t*)(lh + kHistBins);  // [kCandCap] ~position of each copy of thr
+  const int wave = tid >> 6;
+  constexpr int R = kChunk / 64;  // 32 loads per lane per chunk, all in flight
+  for (int c = wave; c < nch; c += kTopkWaves) {
+    const int p0 = c * kChunk;
+    uint32_t kv[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int p = p0 + r * 64 + lane;
+      kv[r] = __float_as_uint(sc[min(p, t - 1)]);
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) kv[r] = p0 + r * 64 + lane < t ? order_key(__uint_as_float(kv[r])) : 0u;
+    int above = 0, nc = 0;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      above += (int)__popcll(__ballot((kv[r] >> 20) > b0));
+      nc += (int)__popcll(__ballot((kv[r] >> 20) == b0));
+    }
+    if (lane == 0) ccnt[c] = above;
+    if (nc) {
+      int cb = 0;
+      if (lane == 0) cb = atomicAdd(&shv[3], nc);
+      cb = __shfl(cb, 0, 64);
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const bool is_c = (kv[r] >> 20) == b0;
+        const uint64_t cm = __ballot(is_c);
+        const int ci = cb + lanes_below(cm);
+        if (is_c && ci < kCandCap) {
+          ckey[ci] = kv[r];
+          cpos[ci] = p0 + r * 64 + lane;
+        }
+        cb += (int)__popcll(cm);
+      }
+    }
+  }
+  __syncthreads();
+  const int n = min(shv[3], kCandCap);
+  // ---- thr = the krem-th largest candidate key; of its e copies the keep lowest positions stay ----
+  int n_gt, e;
+  const uint32_t thr = block_select_desc(ckey, n, krem, lh, scan_tmp, shv, &n_gt, &e);
+  const int keep = krem - n_gt;  // 1 <= keep <= e
+  int p_lim = 0x7FFFFFFF;
+  if (keep < e) {
+    if (tid == 0) shv[3] = 0;
+    __syncthreads();
+    for (int i0 = 0; i0 < n; i0 += kTopkThreads) {
+      const int i = i0 + tid;
+      const bool is_t = i < n && ckey[i] == thr;
+      const uint64_t m = __ballot(is_t);
+      if (m) {
+        int cb = 0;
+        if (lane == 0) cb = atomicAdd(&shv[3], (int)__popcll(m));
+        cb = __shfl(cb, 0, 64);
+        if (is_t) tv[cb + lanes_below(m)] = ~(uint32_t)cpos[i];
+      }
+    }
+    __syncthreads();
+    int g2, e2;
+    p_lim = (int)~block_select_desc(tv, min(shv[3], kCandCap), keep, lh, scan_tmp, shv, &g2, &e2);
+  }
+  // ---- kept candidates per chunk, then the chunks' output offsets ----
+  for (int i = tid; i < n; i += kTopkThreads) {
+    const uint32_t key = ckey[i];
+    if (key > thr || (key == thr && cpos[i] <= p_lim)) atomicAdd(&ccnt[cpos[i] / kChunk], 1);
+  }
+  __syncthreads();
+  int tot;
+  const int ex = block_exclusive_scan<kTopkThreads>(tid < nch ? ccnt[tid] : 0, scan_tmp, tot);
+  if (tid < nch) a.off[(size_t)b * a.off_stride + tid] = ex;
+  for (int i = k + tid; i < a.k; i += kTopkThreads) out[i] = -1;
+  if (tid == 0) {
+    a.out_cnt[b] = k;
+    sel[1] = (int32_t)thr;
+    sel[2] = p_lim;
+    sel[3] = nch;
+    sel[0] = kSelChunked;
+  }
+}
+
+// grid (chunks, B), 256 threads: wave w writes the kept positions of chunk positions
+// [512 w, 512 w + 512) in order, after those of the waves before it
+__global__ __launch_bounds__(256) void topk_compact_kernel(TopkArgs a) {
+  __shared__ int wc[4];
+  const int b = blockIdx.y, c = blockIdx.x;
+  const int32_t* sel = a.sel + (size_t)b * 4;
+  if (sel[0] != kSelChunked || c >= sel[3]) return;
+  const uint32_t thr = (uint32_t)sel[1];
+  const int p_lim = sel[2];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t = min(a.n_vis[b] + a.vis_offset, a.score_stride);
+  const float* sc = a.scores + (size_t)b * a.score_stride;
+  const int base = c * kChunk + wave * (kChunk / 4);
+  constexpr int R = kChunk / 4 / 64;
+  uint64_t km[R];
+  int n = 0;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int p = base + r * 64 + lane;
+    const uint32_t key = p < t ? order_key(sc[p]) : 0u;
+    km[r] = __ballot(key > thr || (key == thr && p <= p_lim));
+    n += (int)__popcll(km[r]);
+  }
+  if (lane == 0) wc[wave] = n;
+  __syncthreads();
+  int w = a.off[(size_t)b * a.off_stride + c];
+  for (int i = 0; i < wave; ++i) w += wc[i];
+  int32_t* out = a.out_idx + (size_t)b * a.out_stride;
+  const int kk = min(a.k, t);  // the kept total (guards the writes should the counts disagree)
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int o = w + lanes_below(km[r]);
+    if (((km[r] >> lane) & 1) && o < kk) out[o] = base + r * 64 + lane;
+    w += (int)__popcll(km[r]);
+  }
+}
+
 // ------------------------------------------------------------------------------------------
 // Expanded-cache decode attention
 // ------------------------------------------------------------------------------------------
@@ -394,15 +677,23 @@ __global__ void gate_mul_kernel(const float* z, const float* g_pre, int n, void*
     ((uint16_t*)u)[i] = f32_to_bf16_bits(v);
 }
 
-hipError_t launch_index_scores(const IndexScoreArgs& a, int max_visible, hipStream_t st) {
-  if (a.B <= 0 || max_visible <= 0) return hipSuccess;
-  index_scores_kernel<<<dim3(cdiv(max_visible, kScorePosPerWG), a.B), 256, 0, st>>>(a);
-  return hipGetLastError();
+size_t index_topk_scratch_words(int B, int score_stride) {
+  return (size_t)B * (kHistBins + 4 + cdiv(score_stride, kChunk));
 }
 
-hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
-  if (a.B <= 0) return hipSuccess;
-  topk_kernel<<<a.B, kTopkThreads, 0, st>>>(a);
+hipError_t launch_index_topk(IndexScoreArgs sa, int max_visible, TopkArgs ta, int32_t* scratch,
+                             hipStream_t st) {
+  if (sa.B <= 0) return hipSuccess;
+  const int B = sa.B;
+  sa.hist = ta.hist = scratch;
+  ta.sel = scratch + (size_t)B * kHistBins;
+  ta.off = ta.sel + (size_t)B * 4;
+  ta.off_stride = cdiv(ta.score_stride, kChunk);
+  zero_words_kernel<<<cdiv(B * kHistBins, 256), 256, 0, st>>>(sa.hist, B * kHistBins);
+  if (max_visible > 0)
+    index_scores_kernel<<<dim3(cdiv(max_visible, kScorePosPerWG), B), 256, 0, st>>>(sa);
+  topk_select_kernel<<<B, kTopkThreads, 0, st>>>(ta);
+  topk_compact_kernel<<<dim3(ta.off_stride, B), 256, 0, st>>>(ta);
   return hipGetLastError();
 }
 

@@ -75,8 +75,8 @@ struct IndexScoreArgs {
   float scale;            // 1/sqrt(n_idx * d_idx)
   float* scores;          // [B, score_stride]
   int score_stride;
+  int32_t* hist;          // [B, 4096] counts of the scores' top-12-bit order-key digit (zeroed first)
 };
-hipError_t launch_index_scores(const IndexScoreArgs& a, int max_visible, hipStream_t st);
 
 struct TopkArgs {
   const float* scores;  // [B, score_stride]
@@ -87,8 +87,16 @@ struct TopkArgs {
   int32_t* out_idx;  // [B, out_stride]
   int out_stride;
   int32_t* out_cnt;  // [B]
+  int32_t* hist;     // [B, 4096] from the score kernel
+  int32_t* sel;      // [B, 4]: path, threshold key, last kept tie position, chunk count
+  int32_t* off;      // [B, off_stride]: output offset of each 2048-position chunk
+  int off_stride;
 };
-hipError_t launch_topk(const TopkArgs& a, hipStream_t st);
+// int32 scratch words of the index-score + top-k launches for B rows of score_stride scores
+size_t index_topk_scratch_words(int B, int score_stride);
+// index scores, then the top-k selection; scratch: index_topk_scratch_words(a.B, score_stride)
+hipError_t launch_index_topk(IndexScoreArgs sa, int max_visible, TopkArgs ta, int32_t* scratch,
+                             hipStream_t st);
 
 struct ExpandedAttnArgs {
   const uint16_t* q;  // [B, H, DQK]

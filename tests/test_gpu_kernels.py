@@ -271,8 +271,9 @@ def test_index_scores_and_topk(topk, t_vis):
     out_idx = torch.empty((B, topk), dtype=torch.int32, device="cuda")
     out_cnt = torch.empty((B,), dtype=torch.int32, device="cuda")
     scores = torch.full((B, T_cap), float("nan"), dtype=torch.float32, device="cuda")
+    ws = torch.empty(gm.workspace_bytes(dims_c, B, 1, T_cap, gm.PATH_SPARSE), dtype=torch.uint8, device="cuda")
     gm.dsa_index_topk(dims_c, dev_bf16(qi), torch.tensor(a, device="cuda"), dev_bf16(keys), T_cap, i32(t_vis),
-                      max(t_vis), B, out_idx, out_cnt, scores)
+                      max(t_vis), B, out_idx, out_cnt, scores, ws)
     _sync()
     sel = out_idx.cpu().numpy()
     cnt = out_cnt.cpu().numpy()
@@ -305,8 +306,45 @@ def test_topk_ties_take_lowest_positions():
     keys = rand_bf16((B, T_cap, d.d_idx), 81)
     out_idx = torch.empty((B, 16), dtype=torch.int32, device="cuda")
     out_cnt = torch.empty((B,), dtype=torch.int32, device="cuda")
-    ws = torch.empty(B * T_cap * 4, dtype=torch.uint8, device="cuda")
+    ws = torch.empty(gm.workspace_bytes(gm.make_dims(d), B, 1, t, gm.PATH_SPARSE), dtype=torch.uint8, device="cuda")
     gm.dsa_index_topk(gm.make_dims(d), dev_bf16(qi), torch.tensor(a, device="cuda"), dev_bf16(keys), T_cap,
                       i32([t, t]), t, B, out_idx, out_cnt, None, ws)
     _sync()
     np.testing.assert_array_equal(out_idx.cpu().numpy(), np.tile(np.arange(16, dtype=np.int32), (B, 1)))
+
+
+@pytest.mark.parametrize("t,n_pos", [(20000, 0), (9000, 1000), (70000, 600)])
+def test_topk_many_equal_scores(t, n_pos):
+    """Rows where the k-th score is shared by thousands of positions: the zero score of every
+    position whose index key is zero, with n_pos scattered positions scoring above it. The kept
+    copies of the tie are the lowest positions (some rows straddle several 2048-position chunks;
+    (20000, 0) has more tied positions than the selection keeps in LDS, which takes the one-row
+    path)."""
+    d = K3.replace(topk=2048)
+    print(f"topk ties t={t} n_pos={n_pos}", flush=True)
+    B, T_cap = 2, t + 5
+    rng = np.random.default_rng(90 + n_pos)
+    qi = rand_bf16((B, d.n_idx_heads, d.d_idx), 91, std=0.1)
+    a = np.abs(rng.standard_normal((B, d.n_idx_heads))).astype(np.float32) + 0.1  # positive weights
+    keys = rand_bf16((B, T_cap, d.d_idx), 92)
+    keys_z = keys.copy()
+    for b in range(B):
+        live = rng.choice(t, n_pos, replace=False) if n_pos else np.zeros(0, np.int64)
+        mask = np.ones(T_cap, bool)
+        mask[live] = False
+        keys_z[b, mask] = 0  # q . 0 = 0 for every head: the score is exactly 0
+    dims_c = gm.make_dims(d)
+    out_idx = torch.empty((B, 2048), dtype=torch.int32, device="cuda")
+    out_cnt = torch.empty((B,), dtype=torch.int32, device="cuda")
+    scores = torch.full((B, T_cap), float("nan"), dtype=torch.float32, device="cuda")
+    ws = torch.empty(gm.workspace_bytes(dims_c, B, 1, T_cap, gm.PATH_SPARSE), dtype=torch.uint8, device="cuda")
+    gm.dsa_index_topk(dims_c, dev_bf16(qi), torch.tensor(a, device="cuda"), dev_bf16(keys_z), T_cap,
+                      i32([t, t]), t, B, out_idx, out_cnt, scores, ws)
+    _sync()
+    sel = out_idx.cpu().numpy()
+    sc_gpu = scores.cpu().numpy()
+    for b in range(B):
+        assert out_cnt[b].item() == 2048
+        np.testing.assert_array_equal(sel[b], O.select_topk(sc_gpu[b, :t].astype(np.float64), 2048))
+        n_zero_kept = int((sc_gpu[b, sel[b]] == 0).sum())
+        assert n_zero_kept >= 2048 - n_pos
