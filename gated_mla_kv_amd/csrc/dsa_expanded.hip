@@ -4,16 +4,18 @@
 //   I[b, s] = (1/sqrt(n_idx d_idx)) sum_h a[b,h] ReLU(q^I[b,h] . k^I[b,s]),  s < t
 // The dot products are a [32 heads x 128] . [128 x 32 positions] bf16 MFMA per wave, with the
 // index keys loaded from HBM straight into the B operand (one 16-byte load per lane and k-step,
-// 256 bytes per position, each read once). Lane l ends with position l%32 and 16 heads, so the
+// 256 bytes per position, each read once; two 32-position tiles in flight per wave, eight waves
+// per 2048-position workgroup). Lane l ends with position l%32 and 16 heads, so the
 // head-weighted ReLU sum is in-lane plus one xor-32 shuffle. 1/sqrt(32*128) = 1/64 is folded
 // into a exactly.
 //
 // Top-k (eq. (6)): S = the min(k, t) largest I, ties to the lower position, -0 == +0, written
 // in ascending position order, over order-preserving 32-bit keys of the fp32 scores.
 // * index_scores_kernel also counts the top 12-bit digit of every key into the row's histogram.
-// * topk_select_kernel (one workgroup per row) takes the bin where the count from the top reaches
-//   k, sorts that bin's keys (with their positions) in LDS, and fixes the threshold key and the
-//   last kept position among its copies; it scans the per-2048-position-chunk kept counts into
+// * topk_count_kernel (one workgroup per 2048-position chunk) finds the bin where the count from
+//   the top reaches k, counts the chunk's keys above it and lists the keys inside it.
+// * topk_select_kernel (one workgroup per row) radix-selects among the listed keys the threshold
+//   key and the last kept position among its copies, and scans the per-chunk kept counts into
 //   output offsets.
 // * topk_compact_kernel (one workgroup per chunk) writes each chunk's kept positions in order.
 // * A row whose boundary bin exceeds the LDS candidate buffer (e.g. thousands of equal scores)
@@ -33,33 +35,37 @@ namespace gmla {
 // ------------------------------------------------------------------------------------------
 // Index scores (K3 indexer: 32 heads x 128)
 // ------------------------------------------------------------------------------------------
-constexpr int kScorePosPerWG = 256;
-
 __device__ __forceinline__ uint32_t order_key(float f);
-constexpr int kHistBins = 4096;  // first radix digit: the top 12 bits of the order key
+constexpr int kHistBins = 4096;      // first radix digit: the top 12 bits of the order key
+constexpr int kScoreChunk = 2048;    // positions per workgroup
+constexpr int kScoreWaves = 8;
 
-__global__ __launch_bounds__(256) void index_scores_kernel(IndexScoreArgs a) {
+// One workgroup per (2048-position chunk, row); wave w scores the 32-position tiles w, w+8, ... of
+// the chunk with the keys of the next tile already in flight, and every score's top digit goes
+// into an LDS histogram that is added to the row's histogram at the end.
+__global__ __launch_bounds__(kScoreWaves * 64) void index_scores_kernel(IndexScoreArgs a) {
   constexpr int NIH = 32, DI = 128, KS = DI / 16;
   __shared__ int lhist[kHistBins];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g2 = lane >> 5, l32 = lane & 31;
   const int b = blockIdx.y;
   const int t = min(min(a.n_vis[b] + a.vis_offset, a.T_cap), a.score_stride);
-  const int base = blockIdx.x * kScorePosPerWG;
+  const int base = blockIdx.x * kScoreChunk;
   if (base >= t) return;
-  for (int i = threadIdx.x; i < kHistBins; i += 256) lhist[i] = 0;
-  const int end = min(base + kScorePosPerWG, t);
+  const int end = min(base + kScoreChunk, t);
+  for (int i = threadIdx.x; i < kHistBins; i += kScoreWaves * 64) lhist[i] = 0;
   const uint16_t* kb = a.idx_k + (size_t)b * a.T_cap * DI;
-  // keys of this wave's positions p0 + l32 (two 32-position steps per wave), both loads in flight
-  auto load_keys = [&](int p0, u32x4* kf) __attribute__((always_inline)) {
-    const int pos = min(p0 + l32, end - 1);  // rows past the end re-read a valid row (not stored)
+  const int n_tiles = cdiv(end - base, 32);
+  const int nt_w = wave < n_tiles ? cdiv(n_tiles - wave, kScoreWaves) : 0;  // this wave's tiles
+  // keys of this wave's j-th tile (positions p0 + l32): the B operand, one 16-byte load per k-step
+  auto load_keys = [&](int j, u32x4* kf) __attribute__((always_inline)) {
+    const int pos = min(base + (wave + kScoreWaves * j) * 32 + l32, end - 1);  // past the end: not stored
 #pragma unroll
     for (int s = 0; s < KS; ++s) kf[s] = ld16(kb + (size_t)pos * DI + s * 16 + g2 * 8);
   };
-  const int p0a = base + wave * 32, p0b = p0a + 4 * 32;
-  u32x4 kfa[KS], kfb[KS];
-  load_keys(p0a, kfa);
-  if (p0b < end) load_keys(p0b, kfb);
+  u32x4 kf0[KS], kf1[KS];
+  if (nt_w > 0) load_keys(0, kf0);
+  if (nt_w > 1) load_keys(1, kf1);
   // A operand: q^I rows (heads) for this lane's head l32
   u32x4 qa[KS];
   const uint16_t* qrow = a.q_idx + ((size_t)b * NIH + l32) * DI;
@@ -69,7 +75,8 @@ __global__ __launch_bounds__(256) void index_scores_kernel(IndexScoreArgs a) {
   float wgt[16];
 #pragma unroll
   for (int r = 0; r < 16; ++r) wgt[r] = a.w_idx[(size_t)b * NIH + (r >> 2) * 8 + g2 * 4 + (r & 3)] * a.scale;
-  auto score = [&](int p0, const u32x4* kf) __attribute__((always_inline)) {
+  __syncthreads();  // histogram cleared
+  auto score = [&](int j, const u32x4* kf) __attribute__((always_inline)) {
     f32x16 acc = f32x16{};
 #pragma unroll
     for (int s = 0; s < KS; ++s) acc = mfma32(qa[s], kf[s], acc);
@@ -77,19 +84,24 @@ __global__ __launch_bounds__(256) void index_scores_kernel(IndexScoreArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) sc += wgt[r] * fmaxf(acc[r], 0.f);
     sc += __shfl_xor(sc, 32, 64);
-    const int pos = p0 + l32;
+    const int pos = base + (wave + kScoreWaves * j) * 32 + l32;
     if (pos < end && g2 == 0) {
       a.scores[(size_t)b * a.score_stride + pos] = sc;
       atomicAdd(&lhist[order_key(sc) >> 20], 1);
     }
   };
-  __syncthreads();  // histogram cleared
-  if (p0a < end) score(p0a, kfa);
-  if (p0b < end) score(p0b, kfb);
+  for (int j = 0; j < nt_w; j += 2) {
+    score(j, kf0);
+    if (j + 2 < nt_w) load_keys(j + 2, kf0);
+    if (j + 1 < nt_w) {
+      score(j + 1, kf1);
+      if (j + 3 < nt_w) load_keys(j + 3, kf1);
+    }
+  }
   __syncthreads();
   // the row's histogram gathers the workgroup's nonzero bins
   int* gh = a.hist + (size_t)b * kHistBins;
-  for (int i = threadIdx.x; i < kHistBins; i += 256) {
+  for (int i = threadIdx.x; i < kHistBins; i += kScoreWaves * 64) {
     const int c = lhist[i];
     if (c) atomicAdd(&gh[i], c);
   }
@@ -111,6 +123,7 @@ __device__ __forceinline__ uint32_t order_key(float f) {
 
 template <int NT>
 __device__ int block_exclusive_scan(int v, int* tmp /* NT/64 + 1 ints */, int& total) {
+  constexpr int NW = NT / 64;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int x = v;
 #pragma unroll
@@ -120,18 +133,20 @@ __device__ int block_exclusive_scan(int v, int* tmp /* NT/64 + 1 ints */, int& t
   }
   if (lane == 63) tmp[wave] = x;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int run = 0;
-    for (int w = 0; w < NT / 64; ++w) {
-      const int c = tmp[w];
-      tmp[w] = run;
-      run += c;
+  if (wave == 0) {  // the wave totals, scanned by the first NW lanes of wave 0
+    const int c = lane < NW ? tmp[lane] : 0;
+    int y = c;
+#pragma unroll
+    for (int o = 1; o < NW; o <<= 1) {
+      const int z = __shfl_up(y, o, 64);
+      if (lane >= o) y += z;
     }
-    tmp[NT / 64] = run;
+    if (lane < NW) tmp[lane] = y - c;
+    if (lane == NW - 1) tmp[NW] = y;
   }
   __syncthreads();
   const int r = tmp[wave] + x - v;
-  total = tmp[NT / 64];
+  total = tmp[NW];
   __syncthreads();
   return r;
 }
@@ -307,9 +322,11 @@ __device__ __forceinline__ void topk_full_row(const TopkArgs& a, const int b, in
 
 
 // ---- chunked path ----
-// The score kernel leaves each row's histogram of the 12-bit top digit. topk_select_kernel (one
-// workgroup per row) finds the bin b0 where the count from the top reaches k, collects the keys
-// of that bin (with their positions) in LDS, and radix-selects among them the threshold key thr
+// The score kernel leaves each row's histogram of the 12-bit top digit. Every 2048-position
+// chunk (topk_count_kernel) finds the bin b0 where the count from the top reaches k, counts its
+// keys above b0 and appends the keys of b0 (with their positions) to the row's candidate list.
+// topk_select_kernel (one workgroup per row) radix-selects among the candidates in LDS the
+// threshold key thr
 // (the krem-th largest, krem = k minus the count above b0) and, when only some of its copies
 // are kept, the last kept position p_lim (the copies' positions radix-selected in turn).
 // A position is kept iff key > thr, or key == thr and position <= p_lim.
@@ -323,16 +340,37 @@ enum { kSelDone = 0, kSelChunked = 1 };
 constexpr int kSelLds = kHistRep * kHistPitch * 4 > kCandCap * 12 + kHistBins * 4
                             ? kHistRep * kHistPitch * 4 : kCandCap * 12 + kHistBins * 4;
 
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = min(v, (uint32_t)__shfl_xor((int)v, o, 64));
+  return v;
+}
+// sum over the workgroup (kTopkThreads); tmp: kTopkWaves ints of LDS, free on entry
+__device__ __forceinline__ int block_sum_int(int v, int* tmp) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  if ((threadIdx.x & 63) == 0) tmp[threadIdx.x >> 6] = v;
+  __syncthreads();
+  int s = 0;
+  for (int w = 0; w < kTopkWaves; ++w) s += tmp[w];
+  __syncthreads();
+  return s;
+}
+
 // The r-th largest (1 <= r <= n) of the 32-bit values vals[0, n) in LDS, for the whole
-// workgroup: three radix levels (12, 12 and 8 bits from the top) over an LDS histogram of 4096
-// ints. *n_gt receives the count of values above it, *n_eq the count equal to it.
+// workgroup: radix levels of 12, 12 and 8 bits from the top over an LDS histogram of 4096 ints,
+// ending early when the r-th lands on a bin that is taken whole (then the answer is that bin's
+// smallest value). *n_gt receives the count of values above it, *n_eq the count equal to it.
+// With first_level = 1 every value is known to have the top 12 bits top12, and level 0 is
+// skipped.
 __device__ __forceinline__ uint32_t block_select_desc(const uint32_t* vals, int n, int r, int* hist,
-                                                      int* scan_tmp, int* shv, int* n_gt, int* n_eq) {
+                                                      int* scan_tmp, int* shv, int* n_gt, int* n_eq,
+                                                      int first_level = 0, uint32_t top12 = 0) {
   const int tid = threadIdx.x;
-  uint32_t prefix = 0, pmask = 0;
-  int gt = 0, eq = 0;
+  uint32_t prefix = first_level ? top12 << 20 : 0u, pmask = first_level ? 0xFFF00000u : 0u;
+  int gt = 0, eq = n;
 #pragma unroll 1
-  for (int level = 0; level < 3; ++level) {
+  for (int level = first_level; level < 3; ++level) {
     const int shift = level == 0 ? 20 : (level == 1 ? 8 : 0);
     const int nbins = level == 2 ? 256 : 4096;
     for (int i = tid; i < kHistBins; i += kTopkThreads) hist[i] = 0;
@@ -371,11 +409,116 @@ __device__ __forceinline__ uint32_t block_select_desc(const uint32_t* vals, int 
     pmask |= (uint32_t)(nbins - 1) << shift;
     gt += shv[1];
     eq = shv[2];
+    const bool whole = rr - shv[1] == shv[2] && level < 2;  // the bin's values are all taken
     __syncthreads();
+    if (whole) {  // every value of the bin is taken: its smallest one is the answer
+      uint32_t lo = 0xFFFFFFFFu;
+      for (int i = tid; i < n; i += kTopkThreads) {
+        const uint32_t v = vals[i];
+        if ((v & pmask) == prefix) lo = min(lo, v);
+      }
+      lo = wave_min_u32(lo);
+      if ((tid & 63) == 0) scan_tmp[tid >> 6] = (int)lo;
+      __syncthreads();
+      lo = 0xFFFFFFFFu;
+      for (int w = 0; w < kTopkWaves; ++w) lo = min(lo, (uint32_t)scan_tmp[w]);
+      int c_lo = 0;  // copies of the bin's smallest value: it is taken entirely, so e == keep
+      for (int i = tid; i < n; i += kTopkThreads) c_lo += vals[i] == lo;
+      __syncthreads();
+      c_lo = block_sum_int(c_lo, scan_tmp);
+      *n_gt = gt + eq - c_lo;
+      *n_eq = c_lo;
+      return lo;
+    }
   }
   *n_gt = gt;
   *n_eq = eq;
   return prefix;
+}
+
+// The bin of the row histogram gh where the count from the top reaches k (k <= the row's
+// count): shv[0] = bin, shv[1] = count above it, shv[2] = its count. Thread j of NT owns bins
+// 4095 - PER j .. -PER+1. Ends with a barrier.
+template <int NT>
+__device__ __forceinline__ void boundary_bin(const int32_t* gh, int k, int* scan_tmp, int* shv) {
+  constexpr int PER = kHistBins / NT;
+  const int top = kHistBins - 1 - PER * (int)threadIdx.x;
+  int cntb[PER];
+  int local = 0;
+#pragma unroll
+  for (int q = 0; q < PER; ++q) {
+    cntb[q] = gh[top - q];
+    local += cntb[q];
+  }
+  int total;
+  const int before = block_exclusive_scan<NT>(local, scan_tmp, total);
+  if (before < k && before + local >= k) {
+    int cum = before;
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      if (cum < k && cum + cntb[q] >= k) {
+        shv[0] = top - q;
+        shv[1] = cum;
+        shv[2] = cntb[q];
+      }
+      cum += cntb[q];
+    }
+  }
+  __syncthreads();
+}
+
+// grid (chunks, B), 256 threads: per chunk, the count of keys above the boundary bin, and the
+// boundary bin's keys and positions (in position order) in the chunk's own candidate slot
+__global__ __launch_bounds__(256) void topk_count_kernel(TopkArgs a) {
+  __shared__ int scan_tmp[256 / 64 + 1];
+  __shared__ int shv[4];
+  __shared__ int wa[4], wn[4];
+  const int b = blockIdx.y, c = blockIdx.x;
+  const int t = min(a.n_vis[b] + a.vis_offset, a.score_stride);
+  if (t <= a.k || c * kChunk >= t) return;
+  boundary_bin<256>(a.hist + (size_t)b * kHistBins, a.k, scan_tmp, shv);
+  if (shv[2] > kCandCap) return;  // the select kernel takes the whole row
+  const uint32_t b0 = (uint32_t)shv[0];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const float* sc = a.scores + (size_t)b * a.score_stride;
+  const int base = c * kChunk + wave * (kChunk / 4);
+  constexpr int R = kChunk / 4 / 64;
+  uint32_t kv[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) kv[r] = __float_as_uint(sc[min(base + r * 64 + lane, t - 1)]);
+#pragma unroll
+  for (int r = 0; r < R; ++r) kv[r] = base + r * 64 + lane < t ? order_key(__uint_as_float(kv[r])) : 0u;
+  int above = 0, nc = 0;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    above += (int)__popcll(__ballot((kv[r] >> 20) > b0));
+    nc += (int)__popcll(__ballot((kv[r] >> 20) == b0));
+  }
+  if (lane == 0) {
+    wa[wave] = above;
+    wn[wave] = nc;
+  }
+  __syncthreads();
+  if (nc) {
+    int cb = 0;
+    for (int i = 0; i < wave; ++i) cb += wn[i];
+    uint32_t* ck = a.cand + ((size_t)b * a.off_stride + c) * 2 * kChunk;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const bool is_c = (kv[r] >> 20) == b0;
+      const uint64_t cm = __ballot(is_c);
+      const int ci = cb + lanes_below(cm);
+      if (is_c) {
+        ck[ci] = kv[r];
+        ck[kChunk + ci] = (uint32_t)(base + r * 64 + lane);
+      }
+      cb += (int)__popcll(cm);
+    }
+  }
+  if (threadIdx.x == 0) {
+    a.above[(size_t)b * a.off_stride + c] = wa[0] + wa[1] + wa[2] + wa[3];
+    a.ncand[(size_t)b * a.off_stride + c] = wn[0] + wn[1] + wn[2] + wn[3];
+  }
 }
 
 __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(TopkArgs a) {
@@ -390,7 +533,6 @@ __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(TopkArgs a) {
   const int k = min(a.k, t);
   int32_t* sel = a.sel + (size_t)b * 4;
   int32_t* out = a.out_idx + (size_t)b * a.out_stride;
-  const float* sc = a.scores + (size_t)b * a.score_stride;
   if (t <= a.k) {  // short history: every visible position is kept
     for (int i = tid; i < a.k; i += kTopkThreads) out[i] = (i < t) ? i : -1;
     if (tid == 0) {
@@ -400,33 +542,13 @@ __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(TopkArgs a) {
     return;
   }
   const int nch = cdiv(t, kChunk);
-  // ---- the bin where the count from the top reaches k: thread j owns bins 4095-4j .. -3 ----
-  const int* gh = a.hist + (size_t)b * kHistBins;
-  constexpr int PER = kHistBins / kTopkThreads;
-  const int top = kHistBins - 1 - PER * tid;
-  int cntb[PER];
-  int local = 0;
-#pragma unroll
-  for (int q = 0; q < PER; ++q) {
-    cntb[q] = gh[top - q];
-    local += cntb[q];
-  }
-  int total;
-  const int before = block_exclusive_scan<kTopkThreads>(local, scan_tmp, total);
-  if (before < k && before + local >= k) {
-    int cum = before;
-#pragma unroll
-    for (int q = 0; q < PER; ++q) {
-      if (cum < k && cum + cntb[q] >= k) {
-        shv[0] = top - q;
-        shv[1] = cum;
-        shv[2] = cntb[q];
-      }
-      cum += cntb[q];
-    }
-  }
-  if (tid == 0) shv[3] = 0;
-  __syncthreads();
+  // this thread's chunk counts (chunk tid; kMaxChunks == kTopkThreads), loaded alongside the
+  // histogram (rows on the one-workgroup path never use them)
+  static_assert(kMaxChunks == kTopkThreads, "one chunk per thread");
+  const bool own = tid < nch;
+  const int my_nc = own ? a.ncand[(size_t)b * a.off_stride + tid] : 0;
+  const int my_above = own ? a.above[(size_t)b * a.off_stride + tid] : 0;
+  boundary_bin<kTopkThreads>(a.hist + (size_t)b * kHistBins, k, scan_tmp, shv);
   const uint32_t b0 = (uint32_t)shv[0];
   const int krem = k - shv[1];
   const int c0 = shv[2];
@@ -436,54 +558,32 @@ __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(TopkArgs a) {
     if (tid == 0) sel[0] = kSelDone;
     return;
   }
-  // ---- one pass over the row: chunk counts above b0, and the keys of bin b0 with their
-  // positions. Wave w owns the chunks w, w + 16, ...: it counts each alone, then reserves room
-  // for its candidates with one LDS atomic ----
+  // ---- the boundary bin's keys and positions, and the chunk counts above it ----
   uint32_t* ckey = (uint32_t*)big;         // [kCandCap]
   int* cpos = (int*)(ckey + kCandCap);     // [kCandCap]
   int* lh = cpos + kCandCap;               // [kHistBins] histogram of the candidate selections
   uint32_t* tv = (uint32_t*)(lh + kHistBins);  // [kCandCap] ~position of each copy of thr
-  const int wave = tid >> 6;
-  constexpr int R = kChunk / 64;  // 32 loads per lane per chunk, all in flight
-  for (int c = wave; c < nch; c += kTopkWaves) {
-    const int p0 = c * kChunk;
-    uint32_t kv[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int p = p0 + r * 64 + lane;
-      kv[r] = __float_as_uint(sc[min(p, t - 1)]);
-    }
-#pragma unroll
-    for (int r = 0; r < R; ++r) kv[r] = p0 + r * 64 + lane < t ? order_key(__uint_as_float(kv[r])) : 0u;
-    int above = 0, nc = 0;
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      above += (int)__popcll(__ballot((kv[r] >> 20) > b0));
-      nc += (int)__popcll(__ballot((kv[r] >> 20) == b0));
-    }
-    if (lane == 0) ccnt[c] = above;
-    if (nc) {
-      int cb = 0;
-      if (lane == 0) cb = atomicAdd(&shv[3], nc);
-      cb = __shfl(cb, 0, 64);
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const bool is_c = (kv[r] >> 20) == b0;
-        const uint64_t cm = __ballot(is_c);
-        const int ci = cb + lanes_below(cm);
-        if (is_c && ci < kCandCap) {
-          ckey[ci] = kv[r];
-          cpos[ci] = p0 + r * 64 + lane;
-        }
-        cb += (int)__popcll(cm);
-      }
+  // the chunks' candidate counts, scanned into LDS offsets (ccnt holds them for the moment)
+  int ntot;
+  const int cpre = block_exclusive_scan<kTopkThreads>(my_nc, scan_tmp, ntot);
+  if (own) ccnt[tid] = cpre;
+  __syncthreads();
+  const int n = min(ntot, kCandCap);
+  for (int c = tid >> 6; c < nch; c += kTopkWaves) {  // wave w copies the chunks w, w + 16, ...
+    const int o = ccnt[c];
+    const int m = min((c + 1 < nch ? ccnt[c + 1] : ntot) - o, kCandCap - o);
+    const uint32_t* gk = a.cand + ((size_t)b * a.off_stride + c) * 2 * kChunk;
+    for (int i = lane; i < m; i += 64) {
+      ckey[o + i] = gk[i];
+      cpos[o + i] = (int)gk[kChunk + i];
     }
   }
   __syncthreads();
-  const int n = min(shv[3], kCandCap);
+  if (own) ccnt[tid] = my_above;
+  __syncthreads();
   // ---- thr = the krem-th largest candidate key; of its e copies the keep lowest positions stay ----
   int n_gt, e;
-  const uint32_t thr = block_select_desc(ckey, n, krem, lh, scan_tmp, shv, &n_gt, &e);
+  const uint32_t thr = block_select_desc(ckey, n, krem, lh, scan_tmp, shv, &n_gt, &e, 1, b0);
   const int keep = krem - n_gt;  // 1 <= keep <= e
   int p_lim = 0x7FFFFFFF;
   if (keep < e) {
@@ -678,22 +778,29 @@ __global__ void gate_mul_kernel(const float* z, const float* g_pre, int n, void*
 }
 
 size_t index_topk_scratch_words(int B, int score_stride) {
-  return (size_t)B * (kHistBins + 4 + cdiv(score_stride, kChunk));
+  const size_t S = cdiv(score_stride, kChunk);
+  return (size_t)B * (kHistBins + 4 + 3 * S + S * 2 * kChunk);
 }
 
 hipError_t launch_index_topk(IndexScoreArgs sa, int max_visible, TopkArgs ta, int32_t* scratch,
                              hipStream_t st) {
   if (sa.B <= 0) return hipSuccess;
   const int B = sa.B;
-  sa.hist = ta.hist = scratch;
+  const int S = cdiv(ta.score_stride, kChunk);
+  sa.hist = ta.hist = scratch;  // zeroed before the score kernel adds to it
   ta.sel = scratch + (size_t)B * kHistBins;
   ta.off = ta.sel + (size_t)B * 4;
-  ta.off_stride = cdiv(ta.score_stride, kChunk);
-  zero_words_kernel<<<cdiv(B * kHistBins, 256), 256, 0, st>>>(sa.hist, B * kHistBins);
+  ta.above = ta.off + (size_t)B * S;
+  ta.ncand = ta.above + (size_t)B * S;
+  ta.cand = (uint32_t*)(ta.ncand + (size_t)B * S);
+  ta.off_stride = S;
+  const int nz = B * kHistBins;
+  zero_words_kernel<<<cdiv(nz, 256), 256, 0, st>>>(scratch, nz);
   if (max_visible > 0)
-    index_scores_kernel<<<dim3(cdiv(max_visible, kScorePosPerWG), B), 256, 0, st>>>(sa);
+    index_scores_kernel<<<dim3(cdiv(max_visible, kScoreChunk), B), kScoreWaves * 64, 0, st>>>(sa);
+  topk_count_kernel<<<dim3(S, B), 256, 0, st>>>(ta);
   topk_select_kernel<<<B, kTopkThreads, 0, st>>>(ta);
-  topk_compact_kernel<<<dim3(ta.off_stride, B), 256, 0, st>>>(ta);
+  topk_compact_kernel<<<dim3(S, B), 256, 0, st>>>(ta);
   return hipGetLastError();
 }
 
