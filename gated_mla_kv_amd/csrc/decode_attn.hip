@@ -404,11 +404,136 @@ hipError_t launch_decode_attention(Shape s, const DecodeAttnArgs& a, bool gather
   return launch_decode_t<ShapeTiny>(a, gather, st);
 }
 
+// ---- K3 shape: the same two products on the matrix cores ----
+// absorb: Q~^T[n, tok] = (W^K_h)^T[n, k] Q_nope^T[k, tok] per head. W^K_h ([128 k][512 n], n
+// contiguous) is staged in LDS once per head (rows padded to 1,056 bytes) and read transposed
+// with ds_read_b64_tr_b16 as the A operand; q_nope rows are the B operand (k contiguous).
+// One workgroup per head; wave w computes latent features [128 w, 128 w + 128) for 32 tokens
+// at a time (4 x 8 v_mfma_f32_32x32x16_bf16).
+constexpr int kAbsPitch = 528;  // LDS row pitch of W^K_h in bf16 (conflict-free transposed reads)
+
+__global__ __launch_bounds__(256) void absorb_q_k3_kernel(const uint16_t* __restrict__ q, int ldq,
+                                                          const uint16_t* __restrict__ wkvb, int B,
+                                                          uint16_t* __restrict__ qt) {
+  using S = ShapeK3;
+  constexpr int H = S::H, DN = S::DN, DS = S::DS, DV = S::DV, L = S::L, DQK = DN + DS;
+  __shared__ __attribute__((aligned(16))) uint16_t wk_s[DN * kAbsPitch];
+  const int h = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint16_t* wk = wkvb + (size_t)h * (DN + DV) * L;
+  // W^K_h -> LDS: 128 rows x 64 chunks of 16 bytes, 32 per thread
+#pragma unroll 8
+  for (int i = 0; i < DN * (L / 8) / 256; ++i) {
+    const int ci = i * 256 + tid, r = ci / (L / 8), c = ci % (L / 8);
+    st16(&wk_s[r * kAbsPitch + c * 8], ld16(wk + (size_t)r * L + c * 8));
+  }
+  __syncthreads();
+  const int G = lane >> 4, jj = lane & 15, g2 = lane >> 5, l32 = lane & 31;
+  for (int t0 = 0; t0 < B; t0 += 32) {
+    const int tok = min(t0 + l32, B - 1);  // tokens past B: computed, not stored
+    const uint16_t* qrow = q + (size_t)tok * ldq + h * DQK + g2 * 8;
+    u32x4 qb[DN / 16];
+#pragma unroll
+    for (int ks = 0; ks < DN / 16; ++ks) qb[ks] = ld16(qrow + ks * 16);
+    f32x16 acc[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};
+#pragma unroll
+    for (int ks = 0; ks < DN / 16; ++ks) {
+      const int r0 = ks * 16 + 8 * (G >> 1) + (jj >> 2);
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        const int col = wave * 128 + dt * 32 + 16 * (G & 1) + 4 * (jj & 3);
+        const u32x2 lo = lds_read_tr16(&wk_s[r0 * kAbsPitch + col]);
+        const u32x2 hi = lds_read_tr16(&wk_s[(r0 + 4) * kAbsPitch + col]);
+        acc[dt] = mfma32(u32x4{lo.x, lo.y, hi.x, hi.y}, qb[ks], acc[dt]);
+      }
+    }
+    if (t0 + l32 < B) {
+      uint16_t* dst = qt + ((size_t)(t0 + l32) * H + h) * (L + DS);
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int jg = 0; jg < 4; ++jg) {
+          const int n = wave * 128 + dt * 32 + jg * 8 + g2 * 4;
+          *(u32x2*)(dst + n) = u32x2{pack_bf16x2(acc[dt][jg * 4], acc[dt][jg * 4 + 1]),
+                                     pack_bf16x2(acc[dt][jg * 4 + 2], acc[dt][jg * 4 + 3])};
+        }
+    }
+    // q~[.., L:] = q_shared (64 values = 8 chunks of 16 bytes per token)
+    for (int i = tid; i < 32 * (DS / 8); i += 256) {
+      const int tt = t0 + i / (DS / 8), c = i % (DS / 8);
+      if (tt < B) st16(qt + ((size_t)tt * H + h) * (L + DS) + L + c * 8, ld16(q + (size_t)tt * ldq + h * DQK + DN + c * 8));
+    }
+  }
+}
+
+// value up-projection and gate: Z^T[d, tok] = W^V_h[d, c] O~^T[c, tok]. W^V_h rows (c contiguous)
+// are the A operand straight from memory; o~ is fp32, split into bf16 hi + lo parts (two MFMAs,
+// products exact to ~2^-17 relative) as the B operand. One workgroup per head; wave w computes
+// value rows [32 w, 32 w + 32) for 32 tokens at a time; the epilogue multiplies by sigmoid(g_pre).
+__global__ __launch_bounds__(256) void vup_gate_k3_kernel(const float* __restrict__ o,
+                                                          const uint16_t* __restrict__ wkvb,
+                                                          const float* __restrict__ g_pre, int B,
+                                                          void* __restrict__ u, int u_f32) {
+  using S = ShapeK3;
+  constexpr int H = S::H, DN = S::DN, DV = S::DV, L = S::L;
+  const int h = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g2 = lane >> 5, l32 = lane & 31;
+  const uint16_t* wrow = wkvb + ((size_t)h * (DN + DV) + DN + wave * 32 + l32) * L + g2 * 8;
+  for (int t0 = 0; t0 < B; t0 += 32) {
+    const int tok = min(t0 + l32, B - 1);
+    const float* orow = o + ((size_t)tok * H + h) * L + g2 * 8;
+    f32x16 acc = f32x16{};
+    constexpr int U = 8;  // k-steps whose loads are in flight together
+#pragma unroll 1
+    for (int k0 = 0; k0 < L / 16; k0 += U) {
+      u32x4 wa[U];
+      f32x4 ov[U][2];
+#pragma unroll
+      for (int i = 0; i < U; ++i) {
+        wa[i] = ld16(wrow + (k0 + i) * 16);
+        ov[i][0] = *(const f32x4*)(orow + (k0 + i) * 16);
+        ov[i][1] = *(const f32x4*)(orow + (k0 + i) * 16 + 4);
+      }
+#pragma unroll
+      for (int i = 0; i < U; ++i) {
+        float x[8] = {ov[i][0][0], ov[i][0][1], ov[i][0][2], ov[i][0][3],
+                      ov[i][1][0], ov[i][1][1], ov[i][1][2], ov[i][1][3]};
+        uint32_t hi[4], lo[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          hi[e] = pack_bf16x2(x[2 * e], x[2 * e + 1]);
+          lo[e] = pack_bf16x2(x[2 * e] - lo_bf16(hi[e]), x[2 * e + 1] - hi_bf16(hi[e]));
+        }
+        acc = mfma32(wa[i], u32x4{hi[0], hi[1], hi[2], hi[3]}, acc);
+        acc = mfma32(wa[i], u32x4{lo[0], lo[1], lo[2], lo[3]}, acc);
+      }
+    }
+    if (t0 + l32 < B) {
+      const size_t ub = (size_t)(t0 + l32) * H * DV + (size_t)h * DV;
+#pragma unroll
+      for (int jg = 0; jg < 4; ++jg) {
+        const int d = wave * 32 + jg * 8 + g2 * 4;
+        float z[4] = {acc[jg * 4], acc[jg * 4 + 1], acc[jg * 4 + 2], acc[jg * 4 + 3]};
+        if (g_pre) {
+          const f32x4 gv = *(const f32x4*)(g_pre + ub + d);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) z[e] *= sigmoidf_(gv[e]);
+        }
+        if (u_f32)
+          *(f32x4*)((float*)u + ub + d) = f32x4{z[0], z[1], z[2], z[3]};
+        else
+          *(u32x2*)((uint16_t*)u + ub + d) = u32x2{pack_bf16x2(z[0], z[1]), pack_bf16x2(z[2], z[3])};
+      }
+    }
+  }
+}
+
 hipError_t launch_absorb_q(Shape s, const uint16_t* q, int ldq, const uint16_t* wkvb, int B,
                            uint16_t* qt, hipStream_t st) {
   if (B <= 0) return hipSuccess;
   if (s == Shape::K3)
-    absorb_q_kernel<ShapeK3><<<ShapeK3::H, 256, 0, st>>>(q, ldq, wkvb, B, qt);
+    absorb_q_k3_kernel<<<ShapeK3::H, 256, 0, st>>>(q, ldq, wkvb, B, qt);
   else
     absorb_q_kernel<ShapeTiny><<<ShapeTiny::H, 256, 0, st>>>(q, ldq, wkvb, B, qt);
   return hipGetLastError();
@@ -418,7 +543,7 @@ hipError_t launch_vup_gate(Shape s, const float* o, const uint16_t* wkvb, const 
                            int B, void* u, int u_f32, hipStream_t st) {
   if (B <= 0) return hipSuccess;
   if (s == Shape::K3)
-    vup_gate_kernel<ShapeK3><<<ShapeK3::H, 256, 0, st>>>(o, wkvb, g_pre, B, u, u_f32);
+    vup_gate_k3_kernel<<<ShapeK3::H, 256, 0, st>>>(o, wkvb, g_pre, B, u, u_f32);
   else
     vup_gate_kernel<ShapeTiny><<<ShapeTiny::H, 256, 0, st>>>(o, wkvb, g_pre, B, u, u_f32);
   return hipGetLastError();
