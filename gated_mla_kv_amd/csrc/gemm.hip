@@ -9,7 +9,8 @@
 //   double-buffered LDS tiles with a 144-byte row stride (conflict-free 16-byte reads over 16
 //   consecutive rows), workgroup ids remapped so that each XCD walks a contiguous, M-grouped
 //   range of tiles (operands reused from that XCD's L2).
-// * gemm_nt_skinny: M <= 32 (decode). Weight-bandwidth bound: each wave computes
+// * gemm_nt_skinny_lds: M <= 32 with K % 256 == 0 (decode at the K3 shape), see below.
+// * gemm_nt_skinny: other M <= 32 (decode). Weight-bandwidth bound: each wave computes
 //   W[32 rows] . X^T for all tokens, streaming weights straight from HBM into MFMA operands
 //   with eight 16-byte loads in flight per lane; four waves split K inside the workgroup and
 //   reduce through LDS; a grid-level split-K writes fp32 partials that gemm_reduce sums.
@@ -475,6 +476,72 @@ __global__ __launch_bounds__(256) void gemm_nt_skinny(GemmArgs g, float* partial
   }
 }
 
+// M <= 32 with K % 256 == 0: the decode projections at the K3 shape. Wave w of a workgroup takes
+// weight rows [128 x + 32 w, +32) over the k range [kr y, kr y + kr) (x, y = workgroup ids). The
+// activations are the MFMA B operand staged through LDS in 256-wide k chunks (double-buffered,
+// one barrier per chunk), so the global loads are weight rows only: with every wave loading its
+// own activation fragments too (the same rows in every workgroup) the weight stream ran at half
+// the rate. The next chunk's weight fragments (16 per lane) are in flight during the current
+// chunk's MFMAs.
+constexpr int kSkChunk = 256, kSkXPitch = kSkChunk + 8;  // LDS row pitch (bf16): no bank-aligned rows
+
+__global__ __launch_bounds__(256) void gemm_nt_skinny_lds(GemmArgs g, float* partial, int kr) {
+  __shared__ __attribute__((aligned(16))) uint16_t xs[2][32 * kSkXPitch];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5;
+  const int n0 = blockIdx.x * 128 + wave * 32;
+  const int k1 = blockIdx.y * kr;
+  // rows past N re-read the last row (computed, never stored)
+  const uint16_t* wr = wrow_ptr(g, min(n0 + (lane & 31), g.N - 1)) + k1 + half * 8;
+  // activation staging: thread t copies token t / 8, k [32 (t % 8), +32) of each chunk
+  const int tt = tid >> 3, part = tid & 7;
+  const bool xok = tt < g.M;
+  const uint16_t* xg = g.a + (size_t)(xok ? tt : 0) * g.lda + k1 + part * 32;
+  const int nch = kr / kSkChunk;
+  u32x4 xr[4], wa[16], wb[16];
+  auto load_x = [&](int ch) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) xr[i] = xok ? ld16(xg + ch * kSkChunk + i * 8) : zero16();
+  };
+  auto load_w = [&](int ch, u32x4* v) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < 16; ++u) v[u] = ld16(wr + ch * kSkChunk + u * 16);
+  };
+  f32x16 acc = f32x16{};
+  auto step = [&](int ch, const u32x4* wcur, u32x4* wnext) __attribute__((always_inline)) {
+    uint16_t* xb = xs[ch & 1];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) st16(xb + tt * kSkXPitch + part * 32 + i * 8, xr[i]);
+    if (ch + 1 < nch) {
+      load_x(ch + 1);
+      load_w(ch + 1, wnext);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const u32x4 xv = *(const u32x4*)(xb + (lane & 31) * kSkXPitch + u * 16 + half * 8);
+      acc = mfma32(wcur[u], xv, acc);
+    }
+  };
+  load_x(0);
+  load_w(0, wa);
+  for (int ch = 0; ch < nch; ch += 2) {
+    step(ch, wa, wb);
+    if (ch + 1 < nch) step(ch + 1, wb, wa);
+  }
+  // acc[r] = out(m = lane % 32, n = n0 + 8 (r / 4) + 4 half + r % 4)
+  const int m = lane & 31;
+  if (m >= g.M) return;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int n = n0 + (r >> 2) * 8 + half * 4 + (r & 3);
+    if (n >= g.N) continue;
+    if (partial)
+      partial[((size_t)blockIdx.y * g.M + m) * g.N + n] = acc[r];
+    else
+      store_out(out_col(g, n), m, acc[r]);
+  }
+}
+
 __global__ void gemm_reduce(GemmArgs g, const float* partial, int ksplit) {
   const int idx = blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= g.M * g.N) return;
@@ -487,7 +554,16 @@ __global__ void gemm_reduce(GemmArgs g, const float* partial, int ksplit) {
 // ----------------------------------------------------------------------------------------
 // Host launchers
 // ----------------------------------------------------------------------------------------
+static bool skinny_lds_ok(int M, int K) { return M <= 32 && K % kSkChunk == 0; }
+
 static int skinny_ksplit(int M, int N, int K) {
+  if (skinny_lds_ok(M, K)) {
+    // about two 128-row workgroups per CU, each k range a whole number of chunks
+    const int groups = cdiv(N, 128), nch = K / kSkChunk;
+    int ks = 1;
+    while (groups * ks * 2 <= 512 && nch % (ks * 2) == 0) ks *= 2;
+    return ks;
+  }
   const int ntiles = cdiv(N, 32);
   int ks = 1;
   // aim for >= 512 workgroups while every wave keeps >= 16 k steps
@@ -512,7 +588,10 @@ hipError_t launch_gemm(const GemmArgs& g, void* ws, size_t ws_bytes, hipStream_t
       if (ws_bytes < (size_t)ks * g.M * g.N * sizeof(float)) return hipErrorInvalidValue;
       partial = (float*)ws;
     }
-    gemm_nt_skinny<<<dim3(cdiv(g.N, 32), ks), 256, 0, stream>>>(g, partial, spw);
+    if (skinny_lds_ok(g.M, g.K))
+      gemm_nt_skinny_lds<<<dim3(cdiv(g.N, 128), ks), 256, 0, stream>>>(g, partial, g.K / ks);
+    else
+      gemm_nt_skinny<<<dim3(cdiv(g.N, 32), ks), 256, 0, stream>>>(g, partial, spw);
     if (ks > 1) {
       const int total = g.M * g.N;
       gemm_reduce<<<cdiv(total, 256), 256, 0, stream>>>(g, partial, ks);
