@@ -268,7 +268,7 @@ def decode_benches(args, d, lw, log):
     t_dsa = median(time_events(dsa_fn, it, flush=flush))
     b_idx = B5 * nv5 * dd.d_idx * 2
     b_sel = B5 * dd.topk * dd.d_latent * 2
-    r5 = roof_hbm("index_scores_kernel+topk_kernel+decode_attn_k3_kernel<gather>+decode_merge_kernel",
+    r5 = roof_hbm("index_scores_kernel+topk_count_kernel+topk_select_kernel+topk_compact_kernel+decode_attn_k3_kernel<gather>+decode_merge_kernel",
                   b_idx + b_sel, t_dsa * 1e3, "dsa:B8_T65536")
     log(f"[bench] DSA decode: index+top-k {t_topk * 1e3:.1f} us, sparse {t_sparse * 1e3:.1f} us, "
         f"together {t_dsa * 1e3:.1f} us, {r5['achieved']:.0f} GB/s")
