@@ -280,26 +280,6 @@ __device__ __forceinline__ void prefill_k3_job(const PrefillAttnArgs& a, uint8_t
       l_run[qb] = l_run[qb] * alpha[qb] + ls;
     }
   };
-  // P.V MFMAs of sub-tile u (parity P): O^T += V^T P^T
-  auto pv = [&](int u, auto P) __attribute__((always_inline)) {
-    constexpr int p = decltype(P)::value;
-    const uint32_t so = ((u >> 1) % NSLOT) * SLOT;
-    uint32_t vb[4];
-#pragma unroll
-    for (int d = 0; d < 4; ++d) vb[d] = vaddr[d] + so;
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const uint32_t ad = vb[d] + (2 * p + ks) * 16 * VROWB;
-        const u32x2 lo = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((GMLA_LDS i16x4*)(ad)));
-        const u32x2 hi = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((GMLA_LDS i16x4*)(ad + 4 * VROWB)));
-        const u32x4 vf = u32x4{lo.x, lo.y, hi.x, hi.y};
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) o[d][qb] = mfma32(vf, pb[p][ks][qb], o[d][qb]);
-      }
-    }
-  };
   // O^T *= alpha before the next P.V (the factor is exactly 1 unless the max moved)
   auto rescale = [&]() __attribute__((always_inline)) {
     bool any = false;
@@ -320,11 +300,47 @@ __device__ __forceinline__ void prefill_k3_job(const PrefillAttnArgs& a, uint8_t
   // One pipeline step: S(u+2) and P.V(u) on the matrix cores, softmax(u+1) on the VALU. Every
   // wave runs every sub-tile of the workgroup's key range (keys after a row's position get
   // probability 0), so the waves stay in step between barriers.
+  // The LDS fragments of both products are read ahead of their MFMAs (K: KPF k-steps, V^T: two
+  // fragments).
   auto step = [&](int u, auto P) __attribute__((always_inline)) {
     constexpr int p = decltype(P)::value;
+    static_assert(QB == 1, "one query block per wave");
     if (u + 1 >= mv) apply_mask(u + 1, ic<1 - p>{});
-    scores(u + 2, ic<p>{});
-    pv(u, ic<p>{});
+    const uint32_t so = (((u + 2) >> 1) % NSLOT) * SLOT + p * 32 * KROWB;
+    uint32_t kb[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) kb[m] = kaddr[m] + so;
+    auto kread = [&](int s) __attribute__((always_inline)) {
+      return *(GMLA_LDS const u32x4*)(kb[s & 3] + 128 * (s >> 2));
+    };
+    const uint32_t sv = ((u >> 1) % NSLOT) * SLOT;
+    uint32_t vb[4];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) vb[d] = vaddr[d] + sv;
+    auto vread = [&](int i) __attribute__((always_inline)) {  // i = 4 ks + d
+      const uint32_t ad = vb[i & 3] + (2 * p + (i >> 2)) * 16 * VROWB;
+      const u32x2 lo = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((GMLA_LDS i16x4*)(ad)));
+      const u32x2 hi = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((GMLA_LDS i16x4*)(ad + 4 * VROWB)));
+      return u32x4{lo.x, lo.y, hi.x, hi.y};
+    };
+    constexpr int KPF = 4;
+    u32x4 kf[KPF], vf[2];
+#pragma unroll
+    for (int s = 0; s < KPF; ++s) kf[s] = kread(s);
+    sacc[p][0] = f32x16{};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const u32x4 cur = kf[s % KPF];
+      if (s + KPF < KS) kf[s % KPF] = kread(s + KPF);
+      else if (s + KPF - KS < 2) vf[s + KPF - KS] = vread(s + KPF - KS);
+      sacc[p][0] = mfma32(cur, qf[0][s], sacc[p][0]);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const u32x4 cur = vf[i & 1];
+      if (i + 2 < 8) vf[i & 1] = vread(i + 2);
+      o[i & 3][0] = mfma32(cur, pb[p][i >> 2][0], o[i & 3][0]);
+    }
     softmax(u + 1, ic<1 - p>{});
     rescale();
   };
