@@ -39,7 +39,7 @@ __all__ = [
     "Cache", "query_path", "kv_down_path", "kv_up", "expand_keys", "attention_expanded",
     "absorbed_query", "attention_absorbed", "value_up", "gate_output", "layer_forward",
     "index_projections", "index_scores", "select_topk", "attention_absorbed_subset",
-    "dsa_decode_step", "cache_values_per_position",
+    "dsa_decode_step", "dsa_prefill", "cache_values_per_position",
 ]
 
 F64 = np.float64
@@ -422,3 +422,46 @@ def dsa_decode_step(x, w, cache: Cache, dims, index_query_bf16: bool = True):
     u, y = gate_output(z, x, w, dims)
     return y, {"cq": cq, "q_idx": qi, "k_idx": ki, "a": a, "scores": scores, "selected": sel,
                "q_tilde": qt, "z": z, "u": u, "lse": np.stack(lse)}
+
+
+def dsa_prefill(x, w, cache: Cache, dims, index_query_bf16: bool = True):
+    """T new tokens per sequence through the Gated DSA layer (eq. (6) applied at every t).
+
+    x [B, T, hidden]. The main latent, the index keys (and the expanded K/V when the cache
+    keeps them) of all T tokens are appended first; token i then sits at absolute position
+    P + i (P = positions cached before the call) and, with t = P + i + 1 visible positions,
+    scores the index keys 0..P+i (eq. (5)), keeps S = TopK(I, min(k, t)) (eq. (6)) and
+    attends over S only in the absorbed form (eq. (9) over S), followed by the gate and
+    o_proj. Appending all T keys before scoring is the per-query pseudocode's order for every
+    token, since token i only reads positions up to its own. ``index_query_bf16`` as in
+    ``dsa_decode_step``. Returns (y [B, T, hidden], extras).
+    """
+    x = np.asarray(x, dtype=F64)
+    B, T = x.shape[:2]
+    P = cache.length
+    cq, q_nope, q_shared = query_path(x, w, dims)
+    c, r = kv_down_path(x, w, dims)
+    if index_query_bf16:
+        qi, ki, a = index_projections(x, round_to_bf16(cq), w, dims)
+        qi = round_to_bf16(qi)
+    else:
+        qi, ki, a = index_projections(x, cq, w, dims)
+    if cache.expanded:
+        k_nope, v = kv_up(cache._store(c), w, dims)
+        cache.append(c, r, expand_keys(k_nope, cache._store(r)), v.transpose(0, 2, 1, 3), ki)
+    else:
+        cache.append(c, r, idx_k=ki)
+    qt = absorbed_query(q_nope, q_shared, w, dims)        # [B, T, H, L+S]
+    scale = softmax_scale(dims)
+    z = np.zeros((B, T, dims.n_heads, dims.d_v))
+    sel = [[None] * T for _ in range(B)]
+    for b in range(B):
+        for i in range(T):
+            t = P + i + 1
+            I = index_scores(qi[b, i], a[b, i], cache.idx[b], t)
+            S = select_topk(I, dims.topk)
+            o, _ = attention_absorbed_subset(qt[b, i], cache.latent[b], S, scale, dims)
+            z[b, i] = value_up(o, w, dims)
+            sel[b][i] = S
+    u, y = gate_output(z, x, w, dims)
+    return y, {"q_idx": qi, "k_idx": ki, "a": a, "selected": sel, "q_tilde": qt, "z": z, "u": u}

@@ -304,6 +304,40 @@ def test_dsa_step_with_k_at_least_t_equals_dense_decode():
     np.testing.assert_allclose(y_sparse, y_dense[:, 0], rtol=1e-11, atol=1e-13)
 
 
+def test_dsa_prefill_equals_successive_decode_steps():
+    """DSA prefill of T tokens = T DSA decode steps, each appending its token first: token i's
+    scores, selection and output only involve positions up to its own (eq. (6) at every t).
+    k = 6 is below the visible length for most tokens, so the selections are real."""
+    d = TINY_DSA.replace(topk=6)
+    w = _weights_f64(make_layer_weights(d, seed=16, dist="fan_in", perturb_norms=True))
+    x = _x(d, 2, 12, seed=16)
+    a_cache = O.Cache(d, 2, expanded=False)
+    O.dsa_prefill(x[:, :5], w, a_cache, d)
+    b_cache = O.Cache(d, 2, expanded=False)
+    b_cache.latent, b_cache.idx = a_cache.latent.copy(), a_cache.idx.copy()
+    y_pre, ex = O.dsa_prefill(x[:, 5:], w, a_cache, d)
+    for i in range(7):
+        y_dec, ex_d = O.dsa_decode_step(x[:, 5 + i], w, b_cache, d)
+        np.testing.assert_allclose(y_pre[:, i], y_dec, rtol=1e-11, atol=1e-13)
+        for b in range(2):
+            np.testing.assert_array_equal(ex["selected"][b][i], ex_d["selected"][b])
+    assert any(len(S) == 6 and S[-1] > 6 for S in ex["selected"][0])  # some rows do select
+    np.testing.assert_array_equal(a_cache.latent, b_cache.latent)
+    np.testing.assert_array_equal(a_cache.idx, b_cache.idx)
+
+
+def test_dsa_prefill_with_k_at_least_t_equals_dense_prefill():
+    """k >= every visible length keeps every position, so DSA prefill is the dense layer."""
+    d = TINY_DSA.replace(topk=64)
+    w = _weights_f64(make_layer_weights(d, seed=17, dist="fan_in", perturb_norms=True))
+    x = _x(d, 2, 11, seed=17)
+    y_dense, _ = O.layer_forward(x, w, O.Cache(d, 2), d, form="absorbed")
+    y_sparse, ex = O.dsa_prefill(x, w, O.Cache(d, 2, expanded=False), d)
+    for i in range(11):
+        np.testing.assert_array_equal(ex["selected"][1][i], np.arange(i + 1))
+    np.testing.assert_allclose(y_sparse, y_dense, rtol=1e-11, atol=1e-13)
+
+
 def test_dsa_step_selects_by_index_score():
     d = TINY_DSA
     w = _weights_f64(make_layer_weights(d, seed=15, dist="fan_in", perturb_norms=True))
