@@ -528,6 +528,61 @@ int dsa_index_topk(const mla_dims* d, const void* q_idx, const float* w_idx, con
 // ------------------------------------------------------------------------------------------
 // Whole-layer calls
 // ------------------------------------------------------------------------------------------
+// The projections of T new tokens per sequence and their append to every cache present
+// (everything before attention): x-GEMM, the two RMSNorms, q_b (with the index query segment
+// when idx_query), kv_b when the expanded cache is kept, the index-key LayerNorm, kv_append.
+static int prefill_front(const mla_dims* d, const mla_weights* w, const mla_cache* cache,
+                         const int32_t* start_pos, const void* x, int B, int T, const Ws& wsp, bool with_idx,
+                         bool idx_query, hipStream_t stream) {
+  const int M = B * T, H = d->n_heads, dqk = d->d_nope + d->d_shared;
+  const bool expanded_cache = cache->k && cache->v;
+  int rc = run_x_gemm(d, w, x, M, wsp, with_idx, stream);
+  if (rc) return rc;
+  CHECK_HIP(launch_rmsnorm(wsp.xq, d->q_lora, (const uint16_t*)w->g_q_a, M, d->q_lora, d->rms_eps, wsp.cq,
+                           d->q_lora, stream));
+  CHECK_HIP(launch_rmsnorm(wsp.xc, d->kv_lora, (const uint16_t*)w->g_kv_a, M, d->kv_lora, d->rms_eps, wsp.c,
+                           d->kv_lora, stream));
+  {
+    GemmArgs g = gemm_args(wsp.cq, d->q_lora, M, d->q_lora);
+    int n = 0;
+    push(g, seg(w->w_q_b, H * dqk, wsp.q, H * dqk, false, n));
+    if (idx_query) push(g, seg(w->w_idx_q, d->n_idx_heads * d->d_idx, wsp.qidx, d->n_idx_heads * d->d_idx, false, n));
+    CHECK_HIP(launch_gemm(g, wsp.gemm_ws, wsp.gemm_ws_bytes, stream));
+  }
+  if (expanded_cache) {
+    GemmArgs g = gemm_args(wsp.c, d->kv_lora, M, d->kv_lora);
+    int n = 0;
+    push(g, seg(w->w_kv_b, H * (d->d_nope + d->d_v), wsp.kv, H * (d->d_nope + d->d_v), false, n));
+    CHECK_HIP(launch_gemm(g, wsp.gemm_ws, wsp.gemm_ws_bytes, stream));
+  }
+  if (with_idx)
+    CHECK_HIP(launch_layernorm(wsp.kpre, d->d_idx, (const uint16_t*)w->g_idx_k, (const uint16_t*)w->b_idx_k, M,
+                               d->d_idx, d->ln_eps, wsp.kidx, d->d_idx, stream));
+  KvAppendArgs a = append_args(d, cache, start_pos, B, T);
+  a.c = wsp.c;
+  a.ld_c = d->kv_lora;
+  a.r = wsp.r;
+  a.ld_r = d->d_shared;
+  a.latent = (uint16_t*)cache->latent;
+  if (expanded_cache) {
+    a.k_nope = wsp.kv;
+    a.ld_k_tok = H * (d->d_nope + d->d_v);
+    a.ld_k_head = d->d_nope + d->d_v;
+    a.v_new = wsp.kv + d->d_nope;
+    a.ld_v_tok = H * (d->d_nope + d->d_v);
+    a.ld_v_head = d->d_nope + d->d_v;
+    a.k = (uint16_t*)cache->k;
+    a.v = (uint16_t*)cache->v;
+  }
+  if (with_idx) {
+    a.idx_new = wsp.kidx;
+    a.ld_idx = d->d_idx;
+    a.idx = (uint16_t*)cache->idx_k;
+  }
+  CHECK_HIP(launch_kv_append(a, stream));
+  return MLA_OK;
+}
+
 int mla_prefill(const mla_dims* d, const mla_weights* w, const mla_cache* cache, const int32_t* start_pos,
                 int32_t max_end, const void* x, int32_t B, int32_t T, void* y, int32_t out_dtype,
                 float* lse, void* ws, size_t ws_bytes, hipStream_t stream) {
@@ -549,49 +604,8 @@ int mla_prefill(const mla_dims* d, const mla_weights* w, const mla_cache* cache,
   const Ws wsp = carve(d, M, false, max_end, 0, 1, ws);
   if (wsp.total > ws_bytes) return MLA_ERR_WORKSPACE;
 
-  rc = run_x_gemm(d, w, x, M, wsp, with_idx, stream);
+  rc = prefill_front(d, w, cache, start_pos, x, B, T, wsp, with_idx, false, stream);
   if (rc) return rc;
-  CHECK_HIP(launch_rmsnorm(wsp.xq, d->q_lora, (const uint16_t*)w->g_q_a, M, d->q_lora, d->rms_eps, wsp.cq,
-                           d->q_lora, stream));
-  CHECK_HIP(launch_rmsnorm(wsp.xc, d->kv_lora, (const uint16_t*)w->g_kv_a, M, d->kv_lora, d->rms_eps, wsp.c,
-                           d->kv_lora, stream));
-  {
-    GemmArgs g = gemm_args(wsp.cq, d->q_lora, M, d->q_lora);
-    int n = 0;
-    push(g, seg(w->w_q_b, H * dqk, wsp.q, H * dqk, false, n));
-    CHECK_HIP(launch_gemm(g, wsp.gemm_ws, wsp.gemm_ws_bytes, stream));
-  }
-  {
-    GemmArgs g = gemm_args(wsp.c, d->kv_lora, M, d->kv_lora);
-    int n = 0;
-    push(g, seg(w->w_kv_b, H * (d->d_nope + d->d_v), wsp.kv, H * (d->d_nope + d->d_v), false, n));
-    CHECK_HIP(launch_gemm(g, wsp.gemm_ws, wsp.gemm_ws_bytes, stream));
-  }
-  if (with_idx)
-    CHECK_HIP(launch_layernorm(wsp.kpre, d->d_idx, (const uint16_t*)w->g_idx_k, (const uint16_t*)w->b_idx_k, M,
-                               d->d_idx, d->ln_eps, wsp.kidx, d->d_idx, stream));
-  {
-    KvAppendArgs a = append_args(d, cache, start_pos, B, T);
-    a.c = wsp.c;
-    a.ld_c = d->kv_lora;
-    a.r = wsp.r;
-    a.ld_r = d->d_shared;
-    a.k_nope = wsp.kv;
-    a.ld_k_tok = H * (d->d_nope + d->d_v);
-    a.ld_k_head = d->d_nope + d->d_v;
-    a.v_new = wsp.kv + d->d_nope;
-    a.ld_v_tok = H * (d->d_nope + d->d_v);
-    a.ld_v_head = d->d_nope + d->d_v;
-    a.latent = (uint16_t*)cache->latent;
-    a.k = (uint16_t*)cache->k;
-    a.v = (uint16_t*)cache->v;
-    if (with_idx) {
-      a.idx_new = wsp.kidx;
-      a.ld_idx = d->d_idx;
-      a.idx = (uint16_t*)cache->idx_k;
-    }
-    CHECK_HIP(launch_kv_append(a, stream));
-  }
   {
     PrefillAttnArgs a{};
     a.q = wsp.q;
@@ -607,6 +621,134 @@ int mla_prefill(const mla_dims* d, const mla_weights* w, const mla_cache* cache,
     a.T_cap = cache->T_cap;
     a.scale = d->softmax_scale;
     CHECK_HIP(launch_prefill_attention(s, a, stream));
+  }
+  {
+    GemmArgs g = gemm_args(wsp.u, H * d->d_v, M, H * d->d_v);
+    int n = 0;
+    push(g, seg(w->w_o, d->hidden, y, d->hidden, out_dtype == MLA_OUT_F32, n));
+    CHECK_HIP(launch_gemm(g, wsp.gemm_ws, wsp.gemm_ws_bytes, stream));
+  }
+  return MLA_OK;
+}
+
+// ---- Gated DSA prefill ----
+// Rows (tokens) are processed in chunks of kSparseRows: absorbed queries, index scores + top-k,
+// gathered latent attention (one split per row), merge, value up-projection and gate; then one
+// o_proj GEMM over all rows.
+constexpr int kSparseRows = 512;
+
+struct SparseWs {
+  uint16_t* qt;      // [R, H, kv_lora + d_shared]
+  float* scores;     // [R, max_end]
+  int32_t* sel;      // [R, topk]
+  int32_t* cnt;      // [R]
+  int32_t* scratch;  // index_topk_scratch_words(R, max_end)
+  uint16_t* part_o;  // [R, H, kv_lora] fp16
+  float* part_ml;    // [R, H, 2]
+  float* olat;       // [R, H, kv_lora]
+  size_t total;
+};
+
+static SparseWs carve_sparse(const mla_dims* d, int R, int max_end, char* base) {
+  Carver cv(base);
+  SparseWs w{};
+  const int H = d->n_heads;
+  w.qt = cv.take<uint16_t>((size_t)R * H * (d->kv_lora + d->d_shared));
+  w.scores = cv.take<float>((size_t)R * max_end);
+  w.sel = cv.take<int32_t>((size_t)R * d->topk);
+  w.cnt = cv.take<int32_t>((size_t)R);
+  w.scratch = cv.take<int32_t>(index_topk_scratch_words(R, max_end));
+  w.part_o = cv.take<uint16_t>((size_t)R * H * d->kv_lora);
+  w.part_ml = cv.take<float>((size_t)R * H * 2);
+  w.olat = cv.take<float>((size_t)R * H * d->kv_lora);
+  w.total = cv.off;
+  return w;
+}
+
+size_t mla_workspace_bytes_prefill_sparse(const mla_dims* d, int32_t B, int32_t T, int32_t max_end) {
+  Shape s;
+  if (!d || !shape_of(d, &s) || !has_dsa(d) || B <= 0 || T <= 0 || max_end < T) return 0;
+  const int M = B * T, R = M < kSparseRows ? M : kSparseRows;
+  return carve(d, M, false, max_end, 0, 1, nullptr).total + carve_sparse(d, R, max_end, nullptr).total;
+}
+
+int mla_prefill_sparse(const mla_dims* d, const mla_weights* w, const mla_cache* cache, const int32_t* start_pos,
+                       int32_t max_end, const void* x, int32_t B, int32_t T, void* y, int32_t out_dtype,
+                       int32_t* sel_idx, int32_t* sel_cnt, void* ws, size_t ws_bytes, hipStream_t stream) {
+  Shape s;
+  if (!d) return MLA_ERR_NULL;
+  if (!shape_of(d, &s)) return MLA_ERR_UNSUPPORTED;
+  if (!has_dsa(d)) return MLA_ERR_UNSUPPORTED;
+  if (B < 0 || T < 0) return MLA_ERR_SHAPE;
+  if (B == 0 || T == 0) return MLA_OK;
+  int rc = check_weights(d, w);
+  if (rc) return rc;
+  if (!idx_weights(w) || !w->w_idx_q) return MLA_ERR_NULL;
+  if (!start_pos || !x || !y || !ws) return MLA_ERR_NULL;
+  rc = check_cache(cache, B, max_end);
+  if (rc) return rc;
+  if (!cache->idx_k) return MLA_ERR_NULL;
+  if (max_end < T) return MLA_ERR_SHAPE;
+  if (out_dtype != MLA_OUT_BF16 && out_dtype != MLA_OUT_F32) return MLA_ERR_UNSUPPORTED;
+  const int M = B * T, H = d->n_heads, dqk = d->d_nope + d->d_shared, R = M < kSparseRows ? M : kSparseRows;
+  const Ws wsp = carve(d, M, false, max_end, 0, 1, ws);
+  const SparseWs sw = carve_sparse(d, R, max_end, (char*)ws + wsp.total);
+  if (wsp.total + sw.total > ws_bytes) return MLA_ERR_WORKSPACE;
+
+  rc = prefill_front(d, w, cache, start_pos, x, B, T, wsp, true, true, stream);
+  if (rc) return rc;
+  for (int r0 = 0; r0 < M; r0 += R) {
+    const int n = M - r0 < R ? M - r0 : R;  // rows r0 .. r0 + n - 1; row r is token r % T of sequence r / T
+    int32_t* sel = sel_idx ? sel_idx + (size_t)r0 * d->topk : sw.sel;
+    int32_t* cnt = sel_cnt ? sel_cnt + r0 : sw.cnt;
+    CHECK_HIP(launch_absorb_q(s, wsp.q + (size_t)r0 * H * dqk, H * dqk, (const uint16_t*)w->w_kv_b, n, sw.qt, stream));
+    IndexScoreArgs sa{};
+    sa.q_idx = wsp.qidx + (size_t)r0 * d->n_idx_heads * d->d_idx;
+    sa.w_idx = wsp.aw + (size_t)r0 * d->n_idx_heads;
+    sa.idx_k = (const uint16_t*)cache->idx_k;
+    sa.n_vis = start_pos;
+    sa.vis_offset = 1;
+    sa.B = n;
+    sa.T_cap = cache->T_cap;
+    sa.scale = 1.0f / sqrtf((float)(d->n_idx_heads * d->d_idx));
+    sa.scores = sw.scores;
+    sa.score_stride = max_end;
+    sa.row0 = r0;
+    sa.rows_per_seq = T;
+    TopkArgs ta{};
+    ta.scores = sw.scores;
+    ta.score_stride = max_end;
+    ta.n_vis = start_pos;
+    ta.vis_offset = 1;
+    ta.B = n;
+    ta.k = d->topk;
+    ta.out_idx = sel;
+    ta.out_stride = d->topk;
+    ta.out_cnt = cnt;
+    ta.row0 = r0;
+    ta.rows_per_seq = T;
+    CHECK_HIP(launch_index_topk(sa, max_end, ta, sw.scratch, stream));
+    DecodeAttnArgs a{};
+    a.q_tilde = sw.qt;
+    a.latent = (const uint16_t*)cache->latent;
+    a.sel_idx = sel;
+    a.sel_cnt = cnt;
+    a.sel_stride = d->topk;
+    a.B = n;
+    a.T_cap = cache->T_cap;
+    a.n_splits = 1;
+    a.chunk = split_chunk(d->topk, 1);
+    a.scale = d->softmax_scale;
+    a.part_o = sw.part_o;
+    a.part_ml = sw.part_ml;
+    a.o_latent = sw.olat;
+    a.lse = nullptr;
+    a.row0 = r0;
+    a.rows_per_seq = T;
+    CHECK_HIP(launch_decode_attention(s, a, true, stream));
+    CHECK_HIP(launch_vup_gate(s, sw.olat, (const uint16_t*)w->w_kv_b,
+                              d->use_gate ? wsp.gpre + (size_t)r0 * H * d->d_v : nullptr, n,
+                              wsp.u + (size_t)r0 * H * d->d_v, 0, stream));
   }
   {
     GemmArgs g = gemm_args(wsp.u, H * d->d_v, M, H * d->d_v);

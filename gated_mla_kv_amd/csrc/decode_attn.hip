@@ -61,7 +61,7 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeAttnArgs a) {
   const int p1 = min(p0 + a.chunk, n_vis);
   const int n_pos = max(p1 - p0, 0);
   const int n_tiles = cdiv(n_pos, C::BT);
-  const uint16_t* lat = a.latent + (size_t)b * a.T_cap * C::DL;
+  const uint16_t* lat = a.latent + (size_t)row_map(a.row0, a.rows_per_seq, b).seq * a.T_cap * C::DL;
   const int32_t* sel = GATHER ? a.sel_idx + (size_t)b * a.sel_stride : nullptr;
 
   // ---- score waves: q~ for heads wave*32 + l32 ----

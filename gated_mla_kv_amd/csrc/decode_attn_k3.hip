@@ -80,7 +80,7 @@ __global__ __launch_bounds__(k3dec::NTHREADS) void decode_attn_k3_kernel(DecodeA
   const int p1 = min(p0 + a.chunk, n_vis);
   const int n_pos = GATHER ? min(max(p1 - p0, 0), MAX_SEL) : max(p1 - p0, 0);
   const int n_tiles = (n_pos + BT - 1) / BT;
-  const uint16_t* lat = a.latent + (size_t)b * a.T_cap * DL;
+  const uint16_t* lat = a.latent + (size_t)row_map(a.row0, a.rows_per_seq, b).seq * a.T_cap * DL;
 
   if (GATHER) {  // this split's selected positions, clamped into the cache
     const int32_t* sel = a.sel_idx + (size_t)b * a.sel_stride;

@@ -49,12 +49,13 @@ __global__ __launch_bounds__(kScoreWaves * 64) void index_scores_kernel(IndexSco
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g2 = lane >> 5, l32 = lane & 31;
   const int b = blockIdx.y;
-  const int t = min(min(a.n_vis[b] + a.vis_offset, a.T_cap), a.score_stride);
+  const RowMap rm = row_map(a.row0, a.rows_per_seq, b);
+  const int t = min(min(a.n_vis[rm.seq] + a.vis_offset + rm.extra, a.T_cap), a.score_stride);
   const int base = blockIdx.x * kScoreChunk;
   if (base >= t) return;
   const int end = min(base + kScoreChunk, t);
   for (int i = threadIdx.x; i < kHistBins; i += kScoreWaves * 64) lhist[i] = 0;
-  const uint16_t* kb = a.idx_k + (size_t)b * a.T_cap * DI;
+  const uint16_t* kb = a.idx_k + (size_t)rm.seq * a.T_cap * DI;
   const int n_tiles = cdiv(end - base, 32);
   const int nt_w = wave < n_tiles ? cdiv(n_tiles - wave, kScoreWaves) : 0;  // this wave's tiles
   // keys of this wave's j-th tile (positions p0 + l32): the B operand, one 16-byte load per k-step
@@ -178,7 +179,8 @@ __device__ __forceinline__ void topk_full_row(const TopkArgs& a, const int b, in
   int& sh_cnt = shv[2];
   int(*wcnt)[kTopkWaves] = (int(*)[kTopkWaves])wcnt_flat;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int t = min(a.n_vis[b] + a.vis_offset, a.score_stride);
+  const RowMap rm = row_map(a.row0, a.rows_per_seq, b);
+  const int t = min(a.n_vis[rm.seq] + a.vis_offset + rm.extra, a.score_stride);
   const int k = min(a.k, t);
   int32_t* out = a.out_idx + (size_t)b * a.out_stride;
   const float* sc = a.scores + (size_t)b * a.score_stride;
@@ -474,7 +476,8 @@ __global__ __launch_bounds__(256) void topk_count_kernel(TopkArgs a) {
   __shared__ int shv[4];
   __shared__ int wa[4], wn[4];
   const int b = blockIdx.y, c = blockIdx.x;
-  const int t = min(a.n_vis[b] + a.vis_offset, a.score_stride);
+  const RowMap rm = row_map(a.row0, a.rows_per_seq, b);
+  const int t = min(a.n_vis[rm.seq] + a.vis_offset + rm.extra, a.score_stride);
   if (t <= a.k || c * kChunk >= t) return;
   boundary_bin<256>(a.hist + (size_t)b * kHistBins, a.k, scan_tmp, shv);
   if (shv[2] > kCandCap) return;  // the select kernel takes the whole row
@@ -529,7 +532,8 @@ __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(TopkArgs a) {
   __shared__ int ccnt[kMaxChunks];
   const int tid = threadIdx.x, lane = tid & 63;
   const int b = blockIdx.x;
-  const int t = min(a.n_vis[b] + a.vis_offset, a.score_stride);
+  const RowMap rm = row_map(a.row0, a.rows_per_seq, b);
+  const int t = min(a.n_vis[rm.seq] + a.vis_offset + rm.extra, a.score_stride);
   const int k = min(a.k, t);
   int32_t* sel = a.sel + (size_t)b * 4;
   int32_t* out = a.out_idx + (size_t)b * a.out_stride;
@@ -633,7 +637,8 @@ __global__ __launch_bounds__(256) void topk_compact_kernel(TopkArgs a) {
   const uint32_t thr = (uint32_t)sel[1];
   const int p_lim = sel[2];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int t = min(a.n_vis[b] + a.vis_offset, a.score_stride);
+  const RowMap rm = row_map(a.row0, a.rows_per_seq, b);
+  const int t = min(a.n_vis[rm.seq] + a.vis_offset + rm.extra, a.score_stride);
   const float* sc = a.scores + (size_t)b * a.score_stride;
   const int base = c * kChunk + wave * (kChunk / 4);
   constexpr int R = kChunk / 4 / 64;

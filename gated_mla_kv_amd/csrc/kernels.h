@@ -58,12 +58,25 @@ struct DecodeAttnArgs {
   float* part_ml;   // [B, n_splits, H, 2]
   float* o_latent;  // [B, H, L]
   float* lse;       // [B, H] or null
+  int row0, rows_per_seq;  // see row_map (latent rows of sequence row_map(..).seq)
 };
 hipError_t launch_decode_attention(Shape s, const DecodeAttnArgs& a, bool gather, hipStream_t st);
 hipError_t launch_absorb_q(Shape s, const uint16_t* q, int ldq, const uint16_t* wkvb, int B,
                            uint16_t* qt, hipStream_t st);
 hipError_t launch_vup_gate(Shape s, const float* o, const uint16_t* wkvb, const float* g_pre,
                            int B, void* u, int u_f32, hipStream_t st);
+
+// Row b of a launch over B rows is row row0 + b of the call. rows_per_seq consecutive rows of the
+// call (1 when 0) belong to one sequence: the new tokens of a prefill, each seeing one more
+// position than the one before it. The sequence indexes the caches and n_vis; the visible length
+// of the row is n_vis[seq] + vis_offset + (its rank in the sequence).
+struct RowMap {
+  int seq, extra;
+};
+__device__ __forceinline__ RowMap row_map(int row0, int rows_per_seq, int b) {
+  const int g = row0 + b, r = rows_per_seq > 0 ? rows_per_seq : 1;
+  return RowMap{g / r, g % r};
+}
 
 struct IndexScoreArgs {
   const uint16_t* q_idx;  // [B, 32, 128]
@@ -76,6 +89,7 @@ struct IndexScoreArgs {
   float* scores;          // [B, score_stride]
   int score_stride;
   int32_t* hist;          // [B, 4096] counts of the scores' top-12-bit order-key digit (zeroed first)
+  int row0, rows_per_seq; // see row_map
 };
 
 struct TopkArgs {
@@ -94,6 +108,7 @@ struct TopkArgs {
   int32_t* ncand;    // [B, off_stride]: per chunk, keys inside the boundary bin
   uint32_t* cand;    // [B, off_stride, 2, 2048]: per chunk, those keys, then their positions
   int off_stride;
+  int row0, rows_per_seq;  // see row_map
 };
 // int32 scratch words of the index-score + top-k launches for B rows of score_stride scores
 size_t index_topk_scratch_words(int B, int score_stride);

@@ -8,7 +8,7 @@ import numpy as np
 import torch
 
 from . import (MlaCache, MlaWeights, OUT_BF16, PATH_ABSORBED, make_dims, mla_decode, mla_prefill,
-               workspace_bytes)
+               workspace_bytes, mla_prefill_sparse, workspace_bytes_prefill_sparse)
 
 _WEIGHT_NAMES = ("w_q_a", "g_q_a", "w_q_b", "w_kv_a", "g_kv_a", "w_kv_b", "w_g", "w_o",
                  "w_idx_q", "w_idx_k", "g_idx_k", "b_idx_k", "w_idx_w")
@@ -49,6 +49,18 @@ class LayerBuffers:
                         dtype=torch.bfloat16 if out_dtype == OUT_BF16 else torch.float32)
         ws = ws if ws is not None else self.workspace(B, T, max_end)
         mla_prefill(self.dims, self.cw, cache.c, start_pos, max_end, x, B, T, y, out_dtype, lse, ws)
+        return y
+
+    def prefill_sparse(self, cache: "CacheBuffers", x: torch.Tensor, start_pos: torch.Tensor, max_end: int,
+                       out_dtype=OUT_BF16, sel_idx=None, sel_cnt=None, ws=None):
+        B, T, _ = x.shape
+        y = torch.empty((B, T, self.shape.hidden), device=self.device,
+                        dtype=torch.bfloat16 if out_dtype == OUT_BF16 else torch.float32)
+        if ws is None:
+            ws = torch.empty(workspace_bytes_prefill_sparse(self.dims, B, T, max_end), dtype=torch.uint8,
+                             device=self.device)
+        mla_prefill_sparse(self.dims, self.cw, cache.c, start_pos, max_end, x, B, T, y, out_dtype, sel_idx, sel_cnt,
+                           ws)
         return y
 
     def decode(self, cache: "CacheBuffers", x: torch.Tensor, seq_len: torch.Tensor, max_len: int,

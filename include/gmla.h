@@ -136,6 +136,25 @@ int mla_prefill(const mla_dims* dims, const mla_weights* w, const mla_cache* cac
                 void* y, int32_t out_dtype, float* lse, void* ws, size_t ws_bytes,
                 hipStream_t stream);
 
+/* Gated DSA prefill ([DSA] eq. (6) at every position, eq. (9) over S_t): T new tokens of each
+ * of B sequences with the indexer's selection applied to every token.
+ *   Arguments as mla_prefill. Requires the indexer (dims->n_idx_heads > 0, every w_idx_* weight)
+ *   and cache->idx_k; cache->k / cache->v are appended to when set (not read).
+ *   The latent rows and index keys of all T tokens are appended first. Token i of sequence b
+ *   (position p = start_pos[b]+i, t = p+1 visible positions) then scores index keys 0..p
+ *   (eq. (5)), keeps S = the min(topk, t) largest (eq. (6), ties to the lower position),
+ *   attends over S only in the absorbed form, and goes through the gate and o_proj.
+ *   sel_idx [B,T,topk] i32 (ascending, -1 padded) and sel_cnt [B,T] i32, or NULL, receive S.
+ *   ws: device workspace of at least mla_workspace_bytes_prefill_sparse(dims, B, T, max_end)
+ *   bytes. Errors as mla_prefill; MLA_ERR_UNSUPPORTED without the indexer. */
+int mla_prefill_sparse(const mla_dims* dims, const mla_weights* w, const mla_cache* cache,
+                       const int32_t* start_pos, int32_t max_end, const void* x, int32_t B,
+                       int32_t T, void* y, int32_t out_dtype, int32_t* sel_idx, int32_t* sel_cnt,
+                       void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* [host] Workspace bytes of mla_prefill_sparse; 0 on bad input or without the indexer. */
+size_t mla_workspace_bytes_prefill_sparse(const mla_dims* dims, int32_t B, int32_t T, int32_t max_end);
+
 /* Decode: one new token per sequence ([ATT] forward with one position; [DSA] pseudocode).
  *   seq_len [B] i32: positions cached before this token; the token is written at position
  *   seq_len[b] and sees seq_len[b]+1 positions. max_len [host]: >= max_b seq_len[b]+1, and

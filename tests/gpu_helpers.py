@@ -74,3 +74,30 @@ def check_scores(got, ref, what, tol=SCORE_TOL):
 
 def i32(a):
     return torch.tensor(np.asarray(a, np.int32), device="cuda")
+
+
+def index_score_ulp_bound(qi, a, keys):
+    """Per position s, how far the index score I_s (eq. (5)) can move when every element of the
+    bf16 index query sits one bf16 ulp (<= 2^-7 |q|) from the oracle's: scale * sum_h |a_h|
+    sum_d 2^-7 |q_hd| |k_sd| (ReLU is 1-Lipschitz). End to end, the GPU rounds q^I to bf16 from
+    its own fp32 c^Q and the oracle from its float64 one, so single elements may round apart."""
+    q = np.abs(np.asarray(qi, np.float64))
+    k = np.abs(np.asarray(keys, np.float64))
+    scale = 1.0 / np.sqrt(q.shape[0] * q.shape[1])
+    return scale * 2.0 ** -7 * (np.abs(np.asarray(a, np.float64)) @ (q @ k.T))
+
+
+def check_selection_end_to_end(got, I, k, bound):
+    """The GPU's top-k set against the oracle's scores I: equal to select_topk(I, k) except for
+    swapped positions whose scores lie within 1e-4 plus their ulp bounds of the k-th largest.
+    Kernel-boundary tests (identical index inputs) use the plain 1e-4 rule instead."""
+    import oracle as O
+    exp = O.select_topk(I, k)
+    order = np.argsort(-I, kind="stable")
+    tau_pos = order[k - 1]
+    tau = I[tau_pos]
+    extra, missing = np.setdiff1d(got, exp), np.setdiff1d(exp, got)
+    assert len(extra) == len(missing), (extra, missing)
+    for s_ in np.concatenate([extra, missing]):
+        assert abs(I[s_] - tau) < 1e-4 + bound[s_] + bound[tau_pos], (s_, I[s_], tau, bound[s_], bound[tau_pos])
+    return exp

@@ -144,3 +144,20 @@ def test_dsa_and_stage_validation():
                                   16, None) == ERR_WORKSPACE
     assert L.mla_expanded_attention(ctypes.byref(d), FAKE, ctypes.byref(_cache(v=None)), FAKE, 10, 2, FAKE,
                                     None, None) == ERR_NULL
+
+
+def test_prefill_sparse_validation():
+    L = gm.lib()
+    d = gm.make_dims(K3)
+    w = gm.MlaWeights(*([FAKE] * 13))
+    call = lambda dims=d, c=None, ws_bytes=1 << 40, B=2, T=10, max_end=50, ww=w: L.mla_prefill_sparse(  # noqa: E731
+        ctypes.byref(dims), ctypes.byref(ww), ctypes.byref(c or _cache(idx=FAKE)), FAKE, max_end, FAKE, B, T, FAKE,
+        0, None, None, FAKE, ws_bytes, None)
+    assert call(dims=gm.make_dims(K3.replace(n_idx_heads=0))) == ERR_UNSUPPORTED   # needs the indexer
+    assert call(c=_cache(idx=None)) == ERR_NULL
+    assert call(ww=_weights()) == ERR_NULL                                            # no index weights
+    assert call(c=_cache(idx=FAKE, T_cap=40)) == ERR_CAPACITY
+    assert call(ws_bytes=100) == ERR_WORKSPACE
+    assert call(B=0) == OK
+    assert gm.workspace_bytes_prefill_sparse(d, 2, 10, 50) > gm.workspace_bytes(d, 2, 10, 50)
+    assert gm.workspace_bytes_prefill_sparse(gm.make_dims(K3.replace(n_idx_heads=0)), 2, 10, 50) == 0

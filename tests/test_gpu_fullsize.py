@@ -17,7 +17,7 @@ import torch
 import gated_mla_kv_amd as gm
 import oracle as O
 from gated_mla_kv_amd.layer import LayerBuffers, bf16_bits, bf16_tensor
-from gpu_helpers import check_rows, check_scores, dev_bf16, to_np
+from gpu_helpers import check_rows, check_scores, check_selection_end_to_end, dev_bf16, index_score_ulp_bound, to_np
 from workloads import K3, bf16_bits_to_f32, device_normal_bf16, make_layer_weights, make_tokens, normal_bf16
 
 pytestmark = pytest.mark.gpu
@@ -210,7 +210,8 @@ def test_decode_step_full_size(k3_weights, path):
             y_ref, ex = O.dsa_decode_step(xb, w64, oc, d)
             got = sel.cpu().numpy()[b]
             assert cnt.cpu().numpy()[b] == d.topk
-            _boundary_rule(got, ex["scores"][0], d.topk)
+            check_selection_end_to_end(got, ex["scores"][0], d.topk,
+                                       index_score_ulp_bound(ex["q_idx"][0], ex["a"][0], oc.idx[0, :Tc + 1]))
             if not np.array_equal(got, ex["selected"][0]):
                 # a boundary swap: the oracle's layer output over the set the GPU selected
                 o, _ = O.attention_absorbed_subset(ex["q_tilde"][0], oc.latent[0], got, O.softmax_scale(d), d)
