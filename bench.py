@@ -13,6 +13,7 @@ Also reported on the same JSON line:
   Cache flushed between iterations; the whole mla_decode step; the expanded-cache path at the
   same shape; long-context decode (B=4, T=131072); Gated DSA decode (B=8, T=65536, top-2048);
   and the attainable HBM bandwidth of a plain device copy;
+* dsa_prefill: the Gated DSA prefill (every token's own top-2048 selection) at B=1, T=4096;
 * cpu_baseline: the oracle (float64 NumPy) timed on the host on a bounded sample of the same
   prefill workload.
 All inputs are seeded synthetic data (workloads module); no trained weights are involved.
@@ -283,6 +284,44 @@ def decode_benches(args, d, lw, log):
     return out
 
 
+def dsa_prefill_bench(args, lw, log):
+    """Gated DSA prefill (mla_prefill_sparse) of B=1, T tokens with the K3.1 indexer (top-2048):
+    the whole call timed with events; its algorithmic flops counted per token (projections
+    without kv_b, index projections, index scores over t positions, the sparse core over
+    min(k, t) positions, query absorption and value up-projection)."""
+    import torch
+
+    import gated_mla_kv_amd as gm
+    from gated_mla_kv_amd.layer import LayerBuffers, bf16_tensor
+    from workloads import K3, make_tokens
+
+    d, T, H = K3, args.T, K3.n_heads
+    L = LayerBuffers(d, lw.w, "cuda")
+    x = bf16_tensor(make_tokens(d, 1, T, seed=0), "cuda")
+    cache = L.new_cache(1, T, expanded=False, index=True)
+    start = torch.zeros(1, dtype=torch.int32, device="cuda")
+    y = torch.empty((1, T, d.hidden), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(gm.workspace_bytes_prefill_sparse(L.dims, 1, T, T), dtype=torch.uint8, device="cuda")
+
+    def run():
+        gm.mla_prefill_sparse(L.dims, L.cw, cache.c, start, T, x, 1, T, y, gm.OUT_BF16, None, None, ws)
+
+    run()
+    torch.cuda.synchronize()
+    ms = median(time_events(run, max(3, args.steps // 4)))
+    tok = 2 * T * (d.hidden * (d.q_lora + d.kv_lora + d.d_shared + H * d.d_v + d.d_idx + d.n_idx_heads)
+                   + d.q_lora * (H * d.d_qk + d.n_idx_heads * d.d_idx)
+                   + H * d.d_v * d.hidden
+                   + 2 * H * d.d_nope * d.kv_lora)                       # absorb + value up
+    pos = sum(range(1, T + 1))
+    sel = sum(min(d.topk, t) for t in range(1, T + 1))
+    fl = tok + 2 * d.n_idx_heads * d.d_idx * pos + 2 * H * (d.d_latent + d.kv_lora) * sel
+    tf = fl / (ms * 1e-3) / 1e12
+    log(f"[bench] DSA prefill (B=1, T={T}, top-{d.topk}): {ms:.3f} ms, {tf:.1f} TFLOP/s algorithmic")
+    return {"workload": f"K3.1 Gated DSA prefill, B=1, T={T} causal, top-{d.topk}, bf16", "ms": round(ms, 4),
+            "flops": fl, "tflops": round(tf, 1)}
+
+
 def counter_pass(log):
     """--counters: each measured kernel launched twice at the bench's shapes, and a plain device
     copy of 256 MiB (reads 256 MiB, writes 256 MiB) that calibrates rocprofv3's FETCH_SIZE and
@@ -479,6 +518,10 @@ def main():
         del cache
         torch.cuda.empty_cache()
         decode = decode_benches(args, d, lw, log)
+    dsa_prefill = None
+    if not args.no_decode:
+        torch.cuda.empty_cache()
+        dsa_prefill = dsa_prefill_bench(args, lw, log)
     # ---- CPU baseline: the oracle on a bounded sample of the prefill workload ----
     cpu = None
     if not args.no_cpu_baseline:
@@ -513,6 +556,7 @@ def main():
         "cpu_baseline": cpu,
         "kernels": kernels,
         "decode": decode,
+        "dsa_prefill": dsa_prefill,
     }
     print(json.dumps(line), flush=True)
 

@@ -7,7 +7,9 @@ the oracle computes one by one (sampled rows, heads and sequences):
   expanded-cache attention per sampled (sequence, head), and whole mla_decode steps;
 * long-context decode, B=4, cache T=131072: absorbed attention (split-K + merge) per sequence;
 * Gated DSA decode, B=8, cache T=65536: index scores, top-2048 (boundary rule), sparse attention,
-  and the whole sparse mla_decode step for sampled sequences.
+  and the whole sparse mla_decode step for sampled sequences;
+* Gated DSA prefill, B=1, T=4096, top-2048: sampled rows past 2048 (where the selection drops
+  positions) against the oracle's DSA steps over the first 2,100 tokens.
 Large inputs are drawn on the device (workloads.device_normal_bf16); the oracle gets the rows
 copied back."""
 import numpy as np
@@ -77,6 +79,47 @@ def test_prefill_layer_T4096_first_rows(k3_weights):
     y_ref, _ = O.layer_forward(bf16_bits_to_f32(x_bits[:, :R]).astype(np.float64), w64, O.Cache(DD, 1), DD)
     rows = [0, 3, 255, 256, 300]
     check_rows(to_np(y[0, rows]), y_ref[0, rows], "prefill y rows", bf16_out=True)
+
+
+def test_dsa_prefill_T4096_selecting_rows(k3_weights):
+    """mla_prefill_sparse at B=1, T=4096, top-2048: rows 2048.. are the first whose visible
+    length exceeds k, so their selection drops positions. Sampled rows there are compared with
+    the oracle's DSA steps (eqs. (5)-(6), (9) over S_t) computed from the first 2,100 tokens."""
+    lw, w64 = k3_weights
+    T, R = 4096, 2100
+    rows = [2047, 2048, 2060, 2099]
+    print("mla_prefill_sparse B=1 T=4096 (sampled rows >= 2047)", flush=True)
+    L = LayerBuffers(D, lw.w)
+    x_bits = make_tokens(D, 1, T, seed=7)
+    cache = L.new_cache(1, T, expanded=False, index=True)
+    sel = torch.empty((1, T, D.topk), dtype=torch.int32, device="cuda")
+    cnt = torch.empty((1, T), dtype=torch.int32, device="cuda")
+    y = L.prefill_sparse(cache, dev_bf16(x_bits), torch.zeros(1, dtype=torch.int32, device="cuda"), T,
+                         out_dtype=gm.OUT_F32, sel_idx=sel, sel_cnt=cnt)
+    torch.cuda.synchronize()
+    sel_h, cnt_h, y_h = sel.cpu().numpy()[0], cnt.cpu().numpy()[0], to_np(y[0])
+    # the oracle's caches and per-token quantities for the first R tokens (the same steps as
+    # O.dsa_prefill, evaluated only at the sampled rows)
+    x = bf16_bits_to_f32(x_bits[:, :R]).astype(np.float64)
+    cq, q_nope, q_shared = O.query_path(x, w64, D)
+    c, r = O.kv_down_path(x, w64, D)
+    qi, ki, a = O.index_projections(x, O.round_to_bf16(cq), w64, D)
+    qi = O.round_to_bf16(qi)
+    oc = O.Cache(D, 1, expanded=False)
+    oc.append(c, r, idx_k=ki)
+    qt = O.absorbed_query(q_nope, q_shared, w64, D)
+    for i in rows:
+        t = i + 1
+        I = O.index_scores(qi[0, i], a[0, i], oc.idx[0], t)
+        k = min(D.topk, t)
+        assert cnt_h[i] == k
+        got = sel_h[i, :k]
+        S = check_selection_end_to_end(got, I, k, index_score_ulp_bound(qi[0, i], a[0, i], oc.idx[0, :t]))
+        if t > D.topk:
+            assert len(S) == D.topk
+        o, _ = O.attention_absorbed_subset(qt[0, i], oc.latent[0], got, O.softmax_scale(D), D)
+        _, y_ref = O.gate_output(O.value_up(o, w64, D)[None], x[0, i][None], w64, D)
+        check_rows(y_h[i], y_ref[0], f"dsa prefill y row {i}")
 
 
 def test_absorbed_decode_B32_T8192():
