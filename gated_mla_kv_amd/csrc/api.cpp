@@ -632,10 +632,9 @@ int mla_prefill(const mla_dims* d, const mla_weights* w, const mla_cache* cache,
 }
 
 // ---- Gated DSA prefill ----
-// Rows (tokens) are processed in chunks of kSparseRows: absorbed queries, index scores + top-k,
-// gathered latent attention (one split per row), merge, value up-projection and gate; then one
-// o_proj GEMM over all rows.
-constexpr int kSparseRows = 512;
+// Rows (tokens) are processed in chunks of sparse_rows(): absorbed queries, index scores + top-k,
+// gathered latent attention (one split per row), value up-projection and gate; then one o_proj
+// GEMM over all rows.
 
 struct SparseWs {
   uint16_t* qt;      // [R, H, kv_lora + d_shared]
@@ -665,10 +664,18 @@ static SparseWs carve_sparse(const mla_dims* d, int R, int max_end, char* base) 
   return w;
 }
 
+// Rows per chunk: the largest of 2048, 1024, 512, 256 whose per-chunk buffers fit in 1 GiB (256
+// at least), and never more than the call's rows.
+static int sparse_rows(const mla_dims* d, int M, int max_end) {
+  int R = 2048;
+  while (R > 256 && carve_sparse(d, R, max_end, nullptr).total > (size_t(1) << 30)) R /= 2;
+  return M < R ? M : R;
+}
+
 size_t mla_workspace_bytes_prefill_sparse(const mla_dims* d, int32_t B, int32_t T, int32_t max_end) {
   Shape s;
   if (!d || !shape_of(d, &s) || !has_dsa(d) || B <= 0 || T <= 0 || max_end < T) return 0;
-  const int M = B * T, R = M < kSparseRows ? M : kSparseRows;
+  const int M = B * T, R = sparse_rows(d, M, max_end);
   return carve(d, M, false, max_end, 0, 1, nullptr).total + carve_sparse(d, R, max_end, nullptr).total;
 }
 
@@ -690,7 +697,7 @@ int mla_prefill_sparse(const mla_dims* d, const mla_weights* w, const mla_cache*
   if (!cache->idx_k) return MLA_ERR_NULL;
   if (max_end < T) return MLA_ERR_SHAPE;
   if (out_dtype != MLA_OUT_BF16 && out_dtype != MLA_OUT_F32) return MLA_ERR_UNSUPPORTED;
-  const int M = B * T, H = d->n_heads, dqk = d->d_nope + d->d_shared, R = M < kSparseRows ? M : kSparseRows;
+  const int M = B * T, H = d->n_heads, dqk = d->d_nope + d->d_shared, R = sparse_rows(d, M, max_end);
   const Ws wsp = carve(d, M, false, max_end, 0, 1, ws);
   const SparseWs sw = carve_sparse(d, R, max_end, (char*)ws + wsp.total);
   if (wsp.total + sw.total > ws_bytes) return MLA_ERR_WORKSPACE;

@@ -388,7 +388,7 @@ static hipError_t launch_decode_t(const DecodeAttnArgs& a, bool gather, hipStrea
   const int grid = a.B * a.n_splits;
   if constexpr (S::H == ShapeK3::H) {
     const hipError_t e = launch_decode_attention_k3(a, gather, st);
-    if (e != hipSuccess) return e;
+    if (e != hipSuccess || (a.n_splits == 1 && !a.lse)) return e;  // wrote o_latent itself
   } else if (gather) {
     decode_attn_kernel<S, true><<<grid, 256, 0, st>>>(a);
   } else {
@@ -405,11 +405,22 @@ hipError_t launch_decode_attention(Shape s, const DecodeAttnArgs& a, bool gather
 }
 
 // ---- K3 shape: the same two products on the matrix cores ----
+// Rows of 512 bf16 (1,024 bytes: one wave-wide LDS DMA each) from `src` (row stride 512) into LDS
+// at row pitch `pitch` elements; wave w of four takes rows w, w + 4, ...; returns after the
+// workgroup's barrier, with every row in LDS.
+__device__ __forceinline__ void stage_rows_512(uint16_t* dst, int pitch, const uint16_t* __restrict__ src,
+                                               int rows, int wave, int lane) {
+  const uint32_t base = lds_addr(dst);
+  for (int r = wave; r < rows; r += 4) lds_dma16(src + (size_t)r * 512 + lane * 8, base + r * pitch * 2);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+}
+
 // absorb: Q~^T[n, tok] = (W^K_h)^T[n, k] Q_nope^T[k, tok] per head. W^K_h ([128 k][512 n], n
 // contiguous) is staged in LDS once per head (rows padded to 1,056 bytes) and read transposed
 // with ds_read_b64_tr_b16 as the A operand; q_nope rows are the B operand (k contiguous).
-// One workgroup per head; wave w computes latent features [128 w, 128 w + 128) for 32 tokens
-// at a time (4 x 8 v_mfma_f32_32x32x16_bf16).
+// Workgroup (h, y) takes head h and the token blocks y, y + gridDim.y, ... of 32 tokens; wave w
+// computes latent features [128 w, 128 w + 128) of a block (4 x 8 v_mfma_f32_32x32x16_bf16).
 constexpr int kAbsPitch = 528;  // LDS row pitch of W^K_h in bf16 (conflict-free transposed reads)
 
 __global__ __launch_bounds__(256) void absorb_q_k3_kernel(const uint16_t* __restrict__ q, int ldq,
@@ -420,16 +431,11 @@ __global__ __launch_bounds__(256) void absorb_q_k3_kernel(const uint16_t* __rest
   __shared__ __attribute__((aligned(16))) uint16_t wk_s[DN * kAbsPitch];
   const int h = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const uint16_t* wk = wkvb + (size_t)h * (DN + DV) * L;
-  // W^K_h -> LDS: 128 rows x 64 chunks of 16 bytes, 32 per thread
-#pragma unroll 8
-  for (int i = 0; i < DN * (L / 8) / 256; ++i) {
-    const int ci = i * 256 + tid, r = ci / (L / 8), c = ci % (L / 8);
-    st16(&wk_s[r * kAbsPitch + c * 8], ld16(wk + (size_t)r * L + c * 8));
-  }
-  __syncthreads();
+  // token blocks of 32: this workgroup takes blocks blockIdx.y, + gridDim.y, ...
+  if ((int)blockIdx.y * 32 >= B) return;
+  stage_rows_512(wk_s, kAbsPitch, wkvb + (size_t)h * (DN + DV) * L, DN, wave, lane);  // W^K_h
   const int G = lane >> 4, jj = lane & 15, g2 = lane >> 5, l32 = lane & 31;
-  for (int t0 = 0; t0 < B; t0 += 32) {
+  for (int t0 = blockIdx.y * 32; t0 < B; t0 += gridDim.y * 32) {
     const int tok = min(t0 + l32, B - 1);  // tokens past B: computed, not stored
     const uint16_t* qrow = q + (size_t)tok * ldq + h * DQK + g2 * 8;
     u32x4 qb[DN / 16];
@@ -468,8 +474,9 @@ __global__ __launch_bounds__(256) void absorb_q_k3_kernel(const uint16_t* __rest
 
 // value up-projection and gate: Z^T[d, tok] = W^V_h[d, c] O~^T[c, tok]. W^V_h rows (c contiguous)
 // are the A operand straight from memory; o~ is fp32, split into bf16 hi + lo parts (two MFMAs,
-// products exact to ~2^-17 relative) as the B operand. One workgroup per head; wave w computes
-// value rows [32 w, 32 w + 32) for 32 tokens at a time; the epilogue multiplies by sigmoid(g_pre).
+// products exact to ~2^-17 relative) as the B operand. Workgroup (h, y) takes head h and the
+// token blocks y, y + gridDim.y, ... of 32 tokens; wave w computes value rows [32 w, 32 w + 32)
+// of a block; the epilogue multiplies by sigmoid(g_pre).
 __global__ __launch_bounds__(256) void vup_gate_k3_kernel(const float* __restrict__ o,
                                                           const uint16_t* __restrict__ wkvb,
                                                           const float* __restrict__ g_pre, int B,
@@ -480,7 +487,7 @@ __global__ __launch_bounds__(256) void vup_gate_k3_kernel(const float* __restric
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g2 = lane >> 5, l32 = lane & 31;
   const uint16_t* wrow = wkvb + ((size_t)h * (DN + DV) + DN + wave * 32 + l32) * L + g2 * 8;
-  for (int t0 = 0; t0 < B; t0 += 32) {
+  for (int t0 = blockIdx.y * 32; t0 < B; t0 += gridDim.y * 32) {  // token blocks of this workgroup
     const int tok = min(t0 + l32, B - 1);
     const float* orow = o + ((size_t)tok * H + h) * L + g2 * 8;
     f32x16 acc = f32x16{};
@@ -529,11 +536,93 @@ __global__ __launch_bounds__(256) void vup_gate_k3_kernel(const float* __restric
   }
 }
 
+// The same product for many tokens: W^V_h is staged in LDS (rows padded to 1,040 bytes) and read
+// as the A operand; workgroup (h, y) takes head h and the four 32-token blocks 4y .. 4y + 3, one
+// per wave, each wave computing all 128 value rows of its block.
+constexpr int kVupPitch = 520;  // LDS row pitch of W^V_h in bf16 (16-byte reads conflict-free)
+
+__global__ __launch_bounds__(256) void vup_gate_k3_lds_kernel(const float* __restrict__ o,
+                                                              const uint16_t* __restrict__ wkvb,
+                                                              const float* __restrict__ g_pre, int B,
+                                                              void* __restrict__ u, int u_f32) {
+  using S = ShapeK3;
+  constexpr int H = S::H, DN = S::DN, DV = S::DV, L = S::L;
+  __shared__ __attribute__((aligned(16))) uint16_t wv_s[DV * kVupPitch];
+  const int h = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g2 = lane >> 5, l32 = lane & 31;
+  stage_rows_512(wv_s, kVupPitch, wkvb + ((size_t)h * (DN + DV) + DN) * L, DV, wave, lane);
+  const int t0 = (blockIdx.y * 4 + wave) * 32;
+  if (t0 >= B) return;  // after the workgroup's only barrier
+  const int tok = min(t0 + l32, B - 1);
+  const float* orow = o + ((size_t)tok * H + h) * L + g2 * 8;
+  const uint16_t* arow = wv_s + l32 * kVupPitch + g2 * 8;
+  f32x16 acc[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};
+  constexpr int U = 8;  // k-steps of o~ loaded together
+  f32x4 ov[U][2];
+#pragma unroll
+  for (int i = 0; i < U; ++i) {
+    ov[i][0] = *(const f32x4*)(orow + i * 16);
+    ov[i][1] = *(const f32x4*)(orow + i * 16 + 4);
+  }
+#pragma unroll 1
+  for (int k0 = 0; k0 < L / 16; k0 += U) {
+    u32x4 bh[U], bl[U];
+#pragma unroll
+    for (int i = 0; i < U; ++i) {
+      const float x[8] = {ov[i][0][0], ov[i][0][1], ov[i][0][2], ov[i][0][3],
+                          ov[i][1][0], ov[i][1][1], ov[i][1][2], ov[i][1][3]};
+      uint32_t hi[4], lo[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        hi[e] = pack_bf16x2(x[2 * e], x[2 * e + 1]);
+        lo[e] = pack_bf16x2(x[2 * e] - lo_bf16(hi[e]), x[2 * e + 1] - hi_bf16(hi[e]));
+      }
+      bh[i] = u32x4{hi[0], hi[1], hi[2], hi[3]};
+      bl[i] = u32x4{lo[0], lo[1], lo[2], lo[3]};
+    }
+    if (k0 + U < L / 16) {  // the next U k-steps of o~ while these run
+#pragma unroll
+      for (int i = 0; i < U; ++i) {
+        ov[i][0] = *(const f32x4*)(orow + (k0 + U + i) * 16);
+        ov[i][1] = *(const f32x4*)(orow + (k0 + U + i) * 16 + 4);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < U; ++i)
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        const u32x4 wa = *(const u32x4*)(arow + dt * 32 * kVupPitch + (k0 + i) * 16);
+        acc[dt] = mfma32(wa, bh[i], acc[dt]);
+        acc[dt] = mfma32(wa, bl[i], acc[dt]);
+      }
+  }
+  if (t0 + l32 < B) {
+    const size_t ub = (size_t)(t0 + l32) * H * DV + (size_t)h * DV;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int jg = 0; jg < 4; ++jg) {
+        const int d = dt * 32 + jg * 8 + g2 * 4;
+        float z[4] = {acc[dt][jg * 4], acc[dt][jg * 4 + 1], acc[dt][jg * 4 + 2], acc[dt][jg * 4 + 3]};
+        if (g_pre) {
+          const f32x4 gv = *(const f32x4*)(g_pre + ub + d);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) z[e] *= sigmoidf_(gv[e]);
+        }
+        if (u_f32)
+          *(f32x4*)((float*)u + ub + d) = f32x4{z[0], z[1], z[2], z[3]};
+        else
+          *(u32x2*)((uint16_t*)u + ub + d) = u32x2{pack_bf16x2(z[0], z[1]), pack_bf16x2(z[2], z[3])};
+      }
+  }
+}
+
 hipError_t launch_absorb_q(Shape s, const uint16_t* q, int ldq, const uint16_t* wkvb, int B,
                            uint16_t* qt, hipStream_t st) {
   if (B <= 0) return hipSuccess;
-  if (s == Shape::K3)
-    absorb_q_k3_kernel<<<ShapeK3::H, 256, 0, st>>>(q, ldq, wkvb, B, qt);
+  if (s == Shape::K3)  // up to four token blocks per workgroup (W^K_h is staged once per workgroup)
+    absorb_q_k3_kernel<<<dim3(ShapeK3::H, cdiv(B, 128)), 256, 0, st>>>(q, ldq, wkvb, B, qt);
   else
     absorb_q_kernel<ShapeTiny><<<ShapeTiny::H, 256, 0, st>>>(q, ldq, wkvb, B, qt);
   return hipGetLastError();
@@ -542,8 +631,10 @@ hipError_t launch_absorb_q(Shape s, const uint16_t* q, int ldq, const uint16_t* 
 hipError_t launch_vup_gate(Shape s, const float* o, const uint16_t* wkvb, const float* g_pre,
                            int B, void* u, int u_f32, hipStream_t st) {
   if (B <= 0) return hipSuccess;
-  if (s == Shape::K3)
-    vup_gate_k3_kernel<<<ShapeK3::H, 256, 0, st>>>(o, wkvb, g_pre, B, u, u_f32);
+  if (s == Shape::K3 && B > 32)  // many tokens: W^V_h staged once per 128 tokens
+    vup_gate_k3_lds_kernel<<<dim3(ShapeK3::H, cdiv(B, 128)), 256, 0, st>>>(o, wkvb, g_pre, B, u, u_f32);
+  else if (s == Shape::K3)
+    vup_gate_k3_kernel<<<dim3(ShapeK3::H, cdiv(B, 32)), 256, 0, st>>>(o, wkvb, g_pre, B, u, u_f32);
   else
     vup_gate_kernel<ShapeTiny><<<ShapeTiny::H, 256, 0, st>>>(o, wkvb, g_pre, B, u, u_f32);
   return hipGetLastError();

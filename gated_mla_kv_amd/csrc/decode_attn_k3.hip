@@ -277,6 +277,22 @@ __global__ __launch_bounds__(k3dec::NTHREADS) void decode_attn_k3_kernel(DecodeA
       __syncthreads();
     }
     __syncthreads();  // 1/l of every head is in LDS
+    if (a.n_splits == 1 && !a.lse) {  // one split: its normalised output is the result
+#pragma unroll
+      for (int hs = 0; hs < 3; ++hs) {
+        const float inv = alpha_s[0][hs * 32 + l32];
+        float* dst = a.o_latent + ((size_t)b * H + hs * 32 + l32) * L;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+          for (int rb = 0; rb < 4; ++rb) {
+            const int f = (pw * 4 + dt) * 32 + rb * 8 + g2 * 4;
+            *(f32x4*)(dst + f) = f32x4{o[dt][hs][rb * 4 + 0], o[dt][hs][rb * 4 + 1], o[dt][hs][rb * 4 + 2],
+                                       o[dt][hs][rb * 4 + 3]} * inv;
+          }
+      }
+      return;
+    }
 #pragma unroll
     for (int hs = 0; hs < 3; ++hs) {
       const float inv = alpha_s[0][hs * 32 + l32];

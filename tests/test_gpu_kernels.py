@@ -228,7 +228,7 @@ def test_expanded_attention(dims, n_vis):
         check_scores(to_np(lse[b]), lse_ref[0, :, 0], f"expanded lse b={b}")
 
 
-@pytest.mark.parametrize("dims,B", [(K3, 5), (K3, 33), (TINY, 3)])
+@pytest.mark.parametrize("dims,B", [(K3, 5), (K3, 33), (K3, 300), (TINY, 3)])
 def test_absorb_query_and_value_up(dims, B):
     d = dims
     H = d.n_heads
