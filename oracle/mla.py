@@ -34,6 +34,8 @@ from __future__ import annotations
 
 import numpy as np
 
+from . import fp8
+
 __all__ = [
     "round_to_bf16", "rms_norm", "layer_norm", "linear", "sigmoid", "softmax_scale",
     "Cache", "query_path", "kv_down_path", "kv_up", "expand_keys", "attention_expanded",
@@ -114,13 +116,25 @@ class Cache:
     ``store_bf16`` the stored values are rounded to bfloat16, the cache type the pages give.
     With ``expanded=False`` only the latent and index caches are kept (the absorbed and the
     sparse paths read nothing else).
+
+    With ``fp8_latent`` / ``fp8_index`` the latent c_s / the index keys are held in the FP8
+    formats of the [DSA] cache section (``oracle.fp8``): the bf16 value is quantized, and
+    ``latent`` / ``idx`` hold what the cache reads back (decode(code) * scale); the codes and
+    scales are kept in ``latent_codes``, ``latent_scales``, ``idx_codes``, ``idx_scales``.
     """
 
-    def __init__(self, dims, B: int, store_bf16: bool = True, expanded: bool = True):
+    def __init__(self, dims, B: int, store_bf16: bool = True, expanded: bool = True,
+                 fp8_latent: bool = False, fp8_index: bool = False):
         H = dims.n_heads
         self.dims = dims
         self.store_bf16 = store_bf16
         self.expanded = expanded
+        self.fp8_latent = fp8_latent
+        self.fp8_index = fp8_index
+        self.latent_codes = np.zeros((B, 0, dims.kv_lora), np.uint8)
+        self.latent_scales = np.zeros((B, 0, dims.kv_lora // fp8.latent_block(dims)), np.float32)
+        self.idx_codes = np.zeros((B, 0, max(dims.d_idx, 0)), np.uint8)
+        self.idx_scales = np.zeros((B, 0, 1), np.float32)
         self.k = np.zeros((B, H, 0, dims.d_nope + dims.d_shared), F64)
         self.v = np.zeros((B, H, 0, dims.d_v), F64)
         self.latent = np.zeros((B, 0, dims.kv_lora + dims.d_shared), F64)
@@ -137,18 +151,41 @@ class Cache:
     def append(self, c, r, k=None, v=None, idx_k=None):
         """Append T new positions: c [B,T,kv_lora], r [B,T,d_shared], k [B,H,T,d_qk],
         v [B,H,T,d_v] (ignored without the expanded cache), idx_k [B,T,d_idx] or None."""
-        self.latent = np.concatenate([self.latent, self._store(np.concatenate([c, r], -1))], 1)
+        c = self._store(c)
+        if self.fp8_latent:
+            codes, scales = fp8.quantize_latent(c, self.dims)
+            self.latent_codes = np.concatenate([self.latent_codes, codes], 1)
+            self.latent_scales = np.concatenate([self.latent_scales, scales], 1)
+            c = fp8.dequantize_latent(codes, scales)
+        self.latent = np.concatenate([self.latent, np.concatenate([c, self._store(r)], -1)], 1)
         if self.expanded:
             self.k = np.concatenate([self.k, self._store(k)], 2)
             self.v = np.concatenate([self.v, self._store(v)], 2)
         if idx_k is not None:
-            self.idx = np.concatenate([self.idx, self._store(idx_k)], 1)
+            ik = self._store(idx_k)
+            if self.fp8_index:
+                codes, scales = fp8.quantize_index_keys(ik)
+                self.idx_codes = np.concatenate([self.idx_codes, codes], 1)
+                self.idx_scales = np.concatenate([self.idx_scales, scales], 1)
+                ik = fp8.dequantize_index_keys(codes, scales)
+            self.idx = np.concatenate([self.idx, ik], 1)
 
     def set_prefix(self, latent, idx=None):
-        """Start from given latent rows (already in the cache type) with no expanded rows."""
-        self.latent = np.asarray(latent, dtype=F64)
+        """Start from given latent rows (already in the cache type) with no expanded rows.
+        With the FP8 formats the rows are given as bf16 values and quantized here."""
+        latent = np.asarray(latent, dtype=F64)
+        if self.fp8_latent:
+            L = self.dims.kv_lora
+            self.latent_codes, self.latent_scales = fp8.quantize_latent(latent[..., :L], self.dims)
+            latent = np.concatenate([fp8.dequantize_latent(self.latent_codes, self.latent_scales),
+                                     latent[..., L:]], -1)
+        self.latent = latent
         if idx is not None:
-            self.idx = np.asarray(idx, dtype=F64)
+            idx = np.asarray(idx, dtype=F64)
+            if self.fp8_index:
+                self.idx_codes, self.idx_scales = fp8.quantize_index_keys(idx)
+                idx = fp8.dequantize_index_keys(self.idx_codes, self.idx_scales)
+            self.idx = idx
 
 
 def cache_values_per_position(dims) -> dict:
