@@ -18,8 +18,10 @@ Readings where the page is silent (listed with their support in the design notes
   rounded to the nearest E4M3 value, ties to even, with the sign copied (a block of zeros has
   scale 0 and codes +-0). Encoding saturates at 448: v / scale can exceed 448 by the FP32
   rounding of the scale, never by half an E4M3 step.
-* A cached value reads back as decode(code) * scale, exact in float64; the layer then runs on
-  those values exactly as on a BF16 cache.
+* A cached index key reads back as decode(code) * scale, exact in float64. A cached latent
+  value reads back in the layer's compute type: decode(code) * scale formed in FP32 and rounded
+  once to BF16 (the page's deployed path feeds the main cache to BF16 attention kernels; the
+  shared key is BF16 already). The layer then runs on those values exactly as on a BF16 cache.
 """
 from __future__ import annotations
 
@@ -27,7 +29,7 @@ import numpy as np
 
 __all__ = ["E4M3_MAX", "e4m3_decode", "e4m3_encode", "quantize_blocks", "dequantize_blocks",
            "latent_block", "latent_row_bytes", "index_key_bytes", "quantize_latent", "quantize_index_keys",
-           "dequantize_latent", "dequantize_index_keys"]
+           "dequantize_latent", "latent_read_back", "dequantize_index_keys"]
 
 F64 = np.float64
 E4M3_MAX = 448.0
@@ -111,6 +113,17 @@ def quantize_latent(c, dims):
 def dequantize_latent(codes, scales) -> np.ndarray:
     codes = np.asarray(codes)
     return dequantize_blocks(codes, scales, codes.shape[-1] // np.shape(scales)[-1])
+
+
+def latent_read_back(codes, scales) -> np.ndarray:
+    """What an FP8 latent value reads back as: bf16(fp32(decode(code) * scale)), as float64."""
+    from .mla import round_to_bf16
+    codes = np.asarray(codes, dtype=np.uint8)
+    n = codes.shape[-1]
+    block = n // np.shape(scales)[-1]
+    vals = e4m3_decode(codes).astype(np.float32).reshape(codes.shape[:-1] + (n // block, block))
+    prod = (vals * np.asarray(scales, dtype=np.float32)[..., None]).astype(np.float32)   # fp32 product
+    return round_to_bf16(prod.astype(F64)).reshape(codes.shape)
 
 
 def quantize_index_keys(k):

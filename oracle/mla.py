@@ -119,7 +119,8 @@ class Cache:
 
     With ``fp8_latent`` / ``fp8_index`` the latent c_s / the index keys are held in the FP8
     formats of the [DSA] cache section (``oracle.fp8``): the bf16 value is quantized, and
-    ``latent`` / ``idx`` hold what the cache reads back (decode(code) * scale); the codes and
+    ``latent`` / ``idx`` hold what the cache reads back (``fp8.latent_read_back``,
+    ``fp8.dequantize_index_keys``); the codes and
     scales are kept in ``latent_codes``, ``latent_scales``, ``idx_codes``, ``idx_scales``.
     """
 
@@ -156,7 +157,7 @@ class Cache:
             codes, scales = fp8.quantize_latent(c, self.dims)
             self.latent_codes = np.concatenate([self.latent_codes, codes], 1)
             self.latent_scales = np.concatenate([self.latent_scales, scales], 1)
-            c = fp8.dequantize_latent(codes, scales)
+            c = fp8.latent_read_back(codes, scales)
         self.latent = np.concatenate([self.latent, np.concatenate([c, self._store(r)], -1)], 1)
         if self.expanded:
             self.k = np.concatenate([self.k, self._store(k)], 2)
@@ -177,7 +178,7 @@ class Cache:
         if self.fp8_latent:
             L = self.dims.kv_lora
             self.latent_codes, self.latent_scales = fp8.quantize_latent(latent[..., :L], self.dims)
-            latent = np.concatenate([fp8.dequantize_latent(self.latent_codes, self.latent_scales),
+            latent = np.concatenate([fp8.latent_read_back(self.latent_codes, self.latent_scales),
                                      latent[..., L:]], -1)
         self.latent = latent
         if idx is not None:

@@ -109,7 +109,7 @@ def test_cache_reads_back_dequantized_values():
     oc.append(c, r, idx_k=ik)
     cb = O.round_to_bf16(c)
     assert np.array_equal(oc.latent[..., d.kv_lora:], O.round_to_bf16(r))
-    assert np.array_equal(oc.latent[..., :d.kv_lora], F.dequantize_latent(*F.quantize_latent(cb, d)))
+    assert np.array_equal(oc.latent[..., :d.kv_lora], F.latent_read_back(*F.quantize_latent(cb, d)))
     assert np.array_equal(oc.idx, F.dequantize_index_keys(*F.quantize_index_keys(O.round_to_bf16(ik))))
     assert oc.idx_scales.shape == (B, T, 1) and oc.latent_scales.shape == (B, T, d.kv_lora // F.latent_block(d))
 
@@ -150,3 +150,19 @@ class _Preset:
         n = self.ref.length
         self.ref.latent = np.concatenate([self.ref.latent, self.q8.latent[:, n:n + 1]], 1)
         self.ref.idx = np.concatenate([self.ref.idx, self.q8.idx[:, n:n + 1]], 1)
+
+
+def test_latent_read_back_matches_torch():
+    """A latent value reads back as decode(code) * scale in fp32, rounded once to bf16: torch's
+    float8_e4m3fn -> float32 product -> bfloat16 casts give the same values."""
+    rng = np.random.default_rng(9)
+    codes = rng.integers(0, 256, (50, 512)).astype(np.uint8)
+    codes[(codes & 0x7F) == 0x7F] ^= 1
+    scales = (np.abs(rng.standard_normal((50, 4))) / 448).astype(np.float32)
+    got = F.latent_read_back(codes, scales)
+    vals = torch.from_numpy(codes).view(torch.float8_e4m3fn).float().reshape(50, 4, 128)
+    ref = (vals * torch.from_numpy(scales)[..., None]).to(torch.bfloat16).double().reshape(50, 512).numpy()
+    assert np.array_equal(got, ref)
+    # within one bf16 rounding (2^-8 relative) of the exact read-back value
+    exact = F.dequantize_latent(codes, scales)
+    assert np.all(np.abs(got - exact) <= 2.0 ** -8 * np.abs(exact) * (1 + 2.0 ** -20))
