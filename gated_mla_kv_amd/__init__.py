@@ -23,6 +23,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgmla.so"
 
 OUT_BF16, OUT_F32 = 0, 1
 PATH_ABSORBED, PATH_EXPANDED, PATH_SPARSE = 0, 1, 2
+CACHE_BF16, CACHE_FP8 = 0, 1
+FP8_LATENT_ROW_BYTES = 656  # 512 E4M3 codes, four fp32 scales, 64 bf16 shared-key values
 
 
 class GmlaError(RuntimeError):
@@ -47,7 +49,8 @@ class MlaWeights(ctypes.Structure):
 
 class MlaCache(ctypes.Structure):
     _fields_ = [("latent", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
-                ("idx_k", ctypes.c_void_p), ("batch", ctypes.c_int32), ("T_cap", ctypes.c_int32)]
+                ("idx_k", ctypes.c_void_p), ("batch", ctypes.c_int32), ("T_cap", ctypes.c_int32),
+                ("latent_format", ctypes.c_int32), ("idx_format", ctypes.c_int32)]
 
 
 _lib = None
@@ -66,6 +69,7 @@ _SIGS = {
     "mla_decode": (ctypes.c_int, [_P, _P, _P, _P, _I, _P, _I, _I, _I, _P, _P, _P, _I, _P, _SZ, _P]),
     "kv_append": (ctypes.c_int, [_P, _P, _P, _I, _I, _I, _P, _P, _P, _P, _P, _P]),
     "dsa_index_topk": (ctypes.c_int, [_P, _P, _P, _P, _I, _P, _I, _I, _P, _P, _P, _P, _SZ, _P]),
+    "dsa_index_topk_fp8": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _P, _I, _I, _P, _P, _P, _P, _SZ, _P]),
     "mla_gemm": (ctypes.c_int, [_P, _I, _P, _I, _I, _I, _P, _I, _I, _P]),
     "mla_rmsnorm": (ctypes.c_int, [_P, _I, _P, _I, _I, _F, _P, _I, _P]),
     "mla_layernorm": (ctypes.c_int, [_P, _I, _P, _P, _I, _I, _F, _P, _I, _P]),
@@ -187,6 +191,14 @@ def dsa_index_topk(dims, q_idx, w_idx, idx_k_cache, T_cap, n_visible, max_visibl
     _check(lib().dsa_index_topk(ctypes.byref(dims), _p(q_idx), _p(w_idx), _p(idx_k_cache), T_cap,
                                 _p(n_visible), max_visible, B, _p(out_idx), _p(out_cnt), _p(out_scores),
                                 wp, wn, _stream(stream)), "dsa_index_topk")
+
+
+def dsa_index_topk_fp8(dims, q_idx, w_idx, idx_codes, idx_scales, T_cap, n_visible, max_visible, B, out_idx,
+                       out_cnt, out_scores=None, ws=None, stream=None):
+    wp, wn = _ws(ws)
+    _check(lib().dsa_index_topk_fp8(ctypes.byref(dims), _p(q_idx), _p(w_idx), _p(idx_codes), _p(idx_scales),
+                                    T_cap, _p(n_visible), max_visible, B, _p(out_idx), _p(out_cnt),
+                                    _p(out_scores), wp, wn, _stream(stream)), "dsa_index_topk_fp8")
 
 
 def mla_gemm(a, lda, w, M, N, K, out, ldo, out_dtype=OUT_BF16, stream=None):

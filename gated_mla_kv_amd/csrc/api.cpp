@@ -191,12 +191,29 @@ bool null_any(std::initializer_list<const void*> ps) {
   return false;
 }
 
-int check_cache(const mla_cache* c, int B, int max_end) {
+// FP8 caches ([DSA] cache section) exist for the K3 layer shape: 656-byte latent rows
+// (kv_lora 512 in four scale blocks, d_shared 64) and 128-feature index keys.
+bool fp8_latent(const mla_cache* c) { return c->latent_format == MLA_CACHE_FP8; }
+bool fp8_index(const mla_cache* c) { return c->idx_format == MLA_CACHE_FP8; }
+
+int check_cache(const mla_dims* d, const mla_cache* c, int B, int max_end) {
   if (!c) return MLA_ERR_NULL;
   if (!c->latent) return MLA_ERR_NULL;
   if (c->batch < B || c->T_cap <= 0) return MLA_ERR_SHAPE;
   if (max_end > c->T_cap) return MLA_ERR_CAPACITY;
+  if ((c->latent_format != MLA_CACHE_BF16 && c->latent_format != MLA_CACHE_FP8) ||
+      (c->idx_format != MLA_CACHE_BF16 && c->idx_format != MLA_CACHE_FP8))
+    return MLA_ERR_UNSUPPORTED;
+  const bool k3 = d->kv_lora == 512 && d->d_shared == 64 && d->n_heads == 96;
+  if (fp8_latent(c) && !k3) return MLA_ERR_UNSUPPORTED;
+  if (fp8_index(c) && (!k3 || d->d_idx != 128)) return MLA_ERR_UNSUPPORTED;
   return MLA_OK;
+}
+
+// FP8 index keys: the scales [batch, T_cap] follow the codes [batch, T_cap, d_idx]
+float* idx_scales(const mla_dims* d, const mla_cache* c) {
+  if (!fp8_index(c) || !c->idx_k) return nullptr;
+  return (float*)((uint8_t*)c->idx_k + (size_t)c->batch * c->T_cap * d->d_idx);
 }
 
 int check_weights(const mla_dims* d, const mla_weights* w) {
@@ -222,6 +239,9 @@ KvAppendArgs append_args(const mla_dims* d, const mla_cache* c, const int32_t* p
   a.DN = d->d_nope;
   a.DV = d->d_v;
   a.DI = d->d_idx;
+  a.latent_fp8 = fp8_latent(c);
+  a.idx_fp8 = fp8_index(c);
+  a.idx_scale = idx_scales(d, c);
   return a;
 }
 
@@ -356,7 +376,7 @@ static int decode_attention_common(const mla_dims* d, const void* q_tilde, const
   if (!q_tilde || !cache || !o_latent || !ws) return MLA_ERR_NULL;
   if (gather ? (!sel_idx || !sel_cnt || !has_dsa(d)) : !n_visible) return gather && !has_dsa(d) ? MLA_ERR_UNSUPPORTED : MLA_ERR_NULL;
   const int span = gather ? d->topk : max_visible;
-  int rc = check_cache(cache, B, gather ? 0 : max_visible);
+  int rc = check_cache(d, cache, B, gather ? 0 : max_visible);
   if (rc) return rc;
   if (span < 1) return MLA_ERR_SHAPE;
   const int splits = auto_splits(B, span, num_splits);
@@ -367,6 +387,7 @@ static int decode_attention_common(const mla_dims* d, const void* q_tilde, const
   DecodeAttnArgs a{};
   a.q_tilde = (const uint16_t*)q_tilde;
   a.latent = (const uint16_t*)cache->latent;
+  a.fp8 = fp8_latent(cache);
   a.n_vis = n_visible;
   a.vis_offset = 0;
   a.sel_idx = sel_idx;
@@ -448,7 +469,7 @@ int kv_append(const mla_dims* d, const mla_cache* cache, const int32_t* pos, int
   if (B < 0 || T < 0) return MLA_ERR_SHAPE;
   if (B == 0 || T == 0) return MLA_OK;
   if (!pos || !c || !r) return MLA_ERR_NULL;
-  int rc = check_cache(cache, B, max_end);
+  int rc = check_cache(d, cache, B, max_end);
   if (rc) return rc;
   if (max_end < T) return MLA_ERR_SHAPE;
   if (idx_k && !has_dsa(d)) return MLA_ERR_UNSUPPORTED;
@@ -480,10 +501,11 @@ int kv_append(const mla_dims* d, const mla_cache* cache, const int32_t* pos, int
   return MLA_OK;
 }
 
-int dsa_index_topk(const mla_dims* d, const void* q_idx, const float* w_idx, const void* idx_k_cache,
-                   int32_t T_cap, const int32_t* n_visible, int32_t max_visible, int32_t B,
-                   int32_t* out_idx, int32_t* out_cnt, float* out_scores, void* ws, size_t ws_bytes,
-                   hipStream_t stream) {
+static int index_topk_common(const mla_dims* d, const void* q_idx, const float* w_idx,
+                             const void* idx_k_cache, const float* idx_k_scales, int32_t T_cap,
+                             const int32_t* n_visible, int32_t max_visible, int32_t B, int32_t* out_idx,
+                             int32_t* out_cnt, float* out_scores, void* ws, size_t ws_bytes,
+                             hipStream_t stream) {
   Shape s;
   if (!d) return MLA_ERR_NULL;
   if (!shape_of(d, &s)) return MLA_ERR_UNSUPPORTED;
@@ -506,6 +528,7 @@ int dsa_index_topk(const mla_dims* d, const void* q_idx, const float* w_idx, con
   sa.q_idx = (const uint16_t*)q_idx;
   sa.w_idx = w_idx;
   sa.idx_k = (const uint16_t*)idx_k_cache;
+  sa.idx_scale = idx_k_scales;
   sa.n_vis = n_visible;
   sa.B = B;
   sa.T_cap = T_cap;
@@ -523,6 +546,24 @@ int dsa_index_topk(const mla_dims* d, const void* q_idx, const float* w_idx, con
   ta.out_cnt = out_cnt;
   CHECK_HIP(launch_index_topk(sa, max_visible, ta, scratch, stream));
   return MLA_OK;
+}
+
+int dsa_index_topk(const mla_dims* d, const void* q_idx, const float* w_idx, const void* idx_k_cache,
+                   int32_t T_cap, const int32_t* n_visible, int32_t max_visible, int32_t B,
+                   int32_t* out_idx, int32_t* out_cnt, float* out_scores, void* ws, size_t ws_bytes,
+                   hipStream_t stream) {
+  return index_topk_common(d, q_idx, w_idx, idx_k_cache, nullptr, T_cap, n_visible, max_visible, B,
+                           out_idx, out_cnt, out_scores, ws, ws_bytes, stream);
+}
+
+int dsa_index_topk_fp8(const mla_dims* d, const void* q_idx, const float* w_idx, const void* idx_k_codes,
+                       const float* idx_k_scales, int32_t T_cap, const int32_t* n_visible,
+                       int32_t max_visible, int32_t B, int32_t* out_idx, int32_t* out_cnt,
+                       float* out_scores, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!idx_k_scales) return MLA_ERR_NULL;
+  if (d && d->d_idx != 128) return MLA_ERR_UNSUPPORTED;
+  return index_topk_common(d, q_idx, w_idx, idx_k_codes, idx_k_scales, T_cap, n_visible, max_visible, B,
+                           out_idx, out_cnt, out_scores, ws, ws_bytes, stream);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -594,7 +635,7 @@ int mla_prefill(const mla_dims* d, const mla_weights* w, const mla_cache* cache,
   int rc = check_weights(d, w);
   if (rc) return rc;
   if (!start_pos || !x || !y || !ws) return MLA_ERR_NULL;
-  rc = check_cache(cache, B, max_end);
+  rc = check_cache(d, cache, B, max_end);
   if (rc) return rc;
   if (!cache->k || !cache->v) return MLA_ERR_NULL;
   if (max_end < T) return MLA_ERR_SHAPE;
@@ -692,7 +733,7 @@ int mla_prefill_sparse(const mla_dims* d, const mla_weights* w, const mla_cache*
   if (rc) return rc;
   if (!idx_weights(w) || !w->w_idx_q) return MLA_ERR_NULL;
   if (!start_pos || !x || !y || !ws) return MLA_ERR_NULL;
-  rc = check_cache(cache, B, max_end);
+  rc = check_cache(d, cache, B, max_end);
   if (rc) return rc;
   if (!cache->idx_k) return MLA_ERR_NULL;
   if (max_end < T) return MLA_ERR_SHAPE;
@@ -713,6 +754,7 @@ int mla_prefill_sparse(const mla_dims* d, const mla_weights* w, const mla_cache*
     sa.q_idx = wsp.qidx + (size_t)r0 * d->n_idx_heads * d->d_idx;
     sa.w_idx = wsp.aw + (size_t)r0 * d->n_idx_heads;
     sa.idx_k = (const uint16_t*)cache->idx_k;
+    sa.idx_scale = idx_scales(d, cache);
     sa.n_vis = start_pos;
     sa.vis_offset = 1;
     sa.B = n;
@@ -738,6 +780,7 @@ int mla_prefill_sparse(const mla_dims* d, const mla_weights* w, const mla_cache*
     DecodeAttnArgs a{};
     a.q_tilde = sw.qt;
     a.latent = (const uint16_t*)cache->latent;
+    a.fp8 = fp8_latent(cache);
     a.sel_idx = sel;
     a.sel_cnt = cnt;
     a.sel_stride = d->topk;
@@ -779,7 +822,7 @@ int mla_decode(const mla_dims* d, const mla_weights* w, const mla_cache* cache, 
   int rc = check_weights(d, w);
   if (rc) return rc;
   if (!seq_len || !x || !y || !ws) return MLA_ERR_NULL;
-  rc = check_cache(cache, B, max_len);
+  rc = check_cache(d, cache, B, max_len);
   if (rc) return rc;
   if (max_len < 1) return MLA_ERR_SHAPE;
   if (out_dtype != MLA_OUT_BF16 && out_dtype != MLA_OUT_F32) return MLA_ERR_UNSUPPORTED;
@@ -865,6 +908,7 @@ int mla_decode(const mla_dims* d, const mla_weights* w, const mla_cache* cache, 
       sa.q_idx = wsp.qidx;
       sa.w_idx = wsp.aw;
       sa.idx_k = (const uint16_t*)cache->idx_k;
+      sa.idx_scale = idx_scales(d, cache);
       sa.n_vis = seq_len;
       sa.vis_offset = 1;
       sa.B = B;
@@ -888,6 +932,7 @@ int mla_decode(const mla_dims* d, const mla_weights* w, const mla_cache* cache, 
     DecodeAttnArgs a{};
     a.q_tilde = wsp.qt;
     a.latent = (const uint16_t*)cache->latent;
+    a.fp8 = fp8_latent(cache);
     a.n_vis = seq_len;
     a.vis_offset = 1;
     a.sel_idx = sel;

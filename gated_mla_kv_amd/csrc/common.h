@@ -103,6 +103,7 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // Loads / stores
 // ---------------------------------------------------------------------------------------
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *(const u32x4*)p; }
+__device__ __forceinline__ u32x2 ld8(const void* p) { return *(const u32x2*)p; }
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *(u32x4*)p = v; }
 __device__ __forceinline__ u32x4 zero16() { return u32x4{0u, 0u, 0u, 0u}; }
 
@@ -121,6 +122,37 @@ __device__ __forceinline__ float wave_max(float v) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+// ---------------------------------------------------------------------------------------
+// OCP E4M3 (FP8 caches). Decoding uses the hardware conversion (exact); encoding is written
+// out: round to nearest, ties to even, sign copied, magnitudes from 448 up saturate to 448.
+// ---------------------------------------------------------------------------------------
+// four E4M3 bytes -> four bf16 (exact: every E4M3 value is a bf16 value), as two packed words
+__device__ __forceinline__ u32x2 e4m3x4_to_bf16(uint32_t w) {
+  typedef float f32x2_ __attribute__((ext_vector_type(2)));
+  const f32x2_ lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+  const f32x2_ hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+  return u32x2{(__float_as_uint(lo.x) >> 16) | (__float_as_uint(lo.y) & 0xFFFF0000u),
+               (__float_as_uint(hi.x) >> 16) | (__float_as_uint(hi.y) & 0xFFFF0000u)};
+}
+__device__ __forceinline__ uint32_t e4m3_encode(float x) {
+  const uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
+  const float a = fabsf(x);
+  uint32_t mag;
+  if (a >= 448.f) {
+    mag = 0x7Eu;
+  } else if (a < 0.015625f) {  // below 2^-6: steps of 2^-9 (8 steps is the smallest normal)
+    mag = (uint32_t)rintf(a * 512.f);
+  } else {
+    const uint32_t ua = __float_as_uint(a);
+    const uint32_t e = (ua >> 23) - 120u;  // biased E4M3 exponent, 1..8
+    uint32_t q = (ua >> 20) & 7u;
+    const uint32_t rem = ua & 0xFFFFFu;
+    if (rem > 0x80000u || (rem == 0x80000u && (q & 1u))) ++q;  // a carry into the exponent is right
+    mag = min((e << 3) + q, 0x7Eu);
+  }
+  return sign | mag;
+}
+
 __device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + __expf(-x)); }
 
 // ---------------------------------------------------------------------------------------

@@ -22,6 +22,12 @@
 // * The running max is only moved when it grows by more than 8 (base 2): otherwise the old
 //   max stays and the rescale factor is exactly 1, so the accumulators are rarely rescaled.
 //   The result is the same softmax; only the reference point of the exponentials differs.
+// * FP8 main cache (K3.1 Gated DSA blog, cache section: 512 E4M3 codes, four fp32 block scales
+//   and r in bf16 per 656-byte row): all seven waves DMA the raw rows (3 of a tile's 21
+//   wave-wide loads each) into a 3-slot ring; after each step's barrier they convert the tile
+//   two ahead into the bf16 tile layout above (decode(code) * scale in fp32, rounded once to
+//   bf16; r copied), into the slot the P.V waves just released, then a second barrier. The
+//   MFMA code is the same; two bf16 slots instead of four.
 // * Each split writes its output divided by its own softmax sum, in fp16: a convex combination
 //   of cached rows, so bounded by the largest latent entry, at half the bytes of fp32 partials
 //   (11-bit significand; the merge weights them by 2^(m - M) * l in fp32).
@@ -42,6 +48,8 @@ constexpr int PROW = BT + 8;                  // P^T [head][position] row stride
 constexpr int KSD = DL / 16;                  // 36 score k-steps
 constexpr int MAX_SEL = 2048;                 // gathered positions per split (<= top-k)
 constexpr float RESCALE_SLACK = 8.0f;         // base-2 growth of the max before rescaling
+constexpr int F8CH = kFp8RowBytes / 16;       // 41 chunks of 16 bytes per FP8 row
+constexpr int F8SLOT = 21 * 1024;             // 32 rows (20,992 bytes) and the 21st load's spill
 }  // namespace k3dec
 
 __device__ __forceinline__ int swz_row(int r) { return ((r ^ (r >> 2)) & 1) | (r & 2) | ((r >> 1) & 4); }
@@ -61,11 +69,12 @@ __device__ __forceinline__ void wait_tiles_in_flight(int tiles) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
-template <bool GATHER>
+template <bool GATHER, bool FP8>
 __global__ __launch_bounds__(k3dec::NTHREADS) void decode_attn_k3_kernel(DecodeAttnArgs a) {
   using namespace k3dec;
-  constexpr int NSLOT = GATHER ? 3 : 4;
+  constexpr int NSLOT = FP8 ? 2 : (GATHER ? 3 : 4);
   __shared__ __attribute__((aligned(1024))) uint8_t lat_s[NSLOT][TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t f8_s[FP8 ? 3 : 1][FP8 ? F8SLOT : 16];
   __shared__ __attribute__((aligned(16))) uint16_t Ps[2][H * PROW];
   __shared__ float alpha_s[2][H];
   __shared__ int sel_s[GATHER ? MAX_SEL : 1];
@@ -93,6 +102,84 @@ __global__ __launch_bounds__(k3dec::NTHREADS) void decode_attn_k3_kernel(DecodeA
 
   const float sl2 = a.scale * 1.4426950408889634f;
   const size_t part = (size_t)b * a.n_splits + split;
+
+  // ---- FP8 rows: issue, wait and convert, run by all seven waves with the same barriers ----
+  const uint8_t* lat8 = (const uint8_t*)a.latent + (size_t)row_map(a.row0, a.rows_per_seq, b).seq * a.T_cap * kFp8RowBytes;
+  int issued8 = 0;
+  auto issue8 = [&]() {  // the next tile's raw rows: loads 3 w .. 3 w + 2 of its 21
+    if (!FP8 || issued8 >= n_tiles) return;
+    const int t = issued8++;
+    const uint32_t fs = lds_addr(f8_s[t % 3]);
+    const int j0 = t * BT;
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+      const int i = wave * 3 + k;
+      const int P = min(i * 64 + lane, BT * F8CH - 1);  // the last load's upper half repeats a chunk
+      const int r = P / F8CH, c = P - r * F8CH;
+      const int jr = min(j0 + r, n_pos - 1);  // rows past the end repeat a valid row (masked)
+      const int pos = GATHER ? sel_s[jr] : p0 + jr;
+      lds_dma16(lat8 + (size_t)pos * kFp8RowBytes + c * 16, fs + i * 1024);
+    }
+  };
+  auto wait8 = [&](int need) {  // this wave's loads of tile `need` have landed
+    const int after = issued8 - 1 - need;
+    if (after >= 2)
+      asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+    else if (after == 1)
+      asm volatile("s_waitcnt vmcnt(3)" ::: "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  };
+  auto convert8 = [&](int t) {  // raw tile t -> bf16 tile layout in lat_s[t % 2]
+    if (!FP8 || t >= n_tiles) return;
+    const uint8_t* fsrc = f8_s[t % 3];
+    uint8_t* dst = lat_s[t % NSLOT];
+    for (int u = tid; u < BT * 40; u += NTHREADS) {
+      if (u < BT * 32) {  // 16 codes of row r: latent features 16 j .. 16 j + 15
+        const int r = u >> 5, j = u & 31;
+        const u32x4 w = *(const u32x4*)(fsrc + r * kFp8RowBytes + j * 16);
+        const float sc = *(const float*)(fsrc + r * kFp8RowBytes + kFp8ScaleOff + (j >> 3) * 4);
+        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+        uint32_t o[8];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          typedef float f2 __attribute__((ext_vector_type(2)));
+          const f2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)ws[q], false);
+          const f2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)ws[q], true);
+          o[2 * q] = pack_bf16x2(lo.x * sc, lo.y * sc);
+          o[2 * q + 1] = pack_bf16x2(hi.x * sc, hi.y * sc);
+        }
+        const int sw = swz_row(r);
+        st16(dst + (r * CH + ((2 * j) ^ sw)) * 16, u32x4{o[0], o[1], o[2], o[3]});
+        st16(dst + (r * CH + ((2 * j + 1) ^ sw)) * 16, u32x4{o[4], o[5], o[6], o[7]});
+      } else {  // r: 8 chunks of bf16 copied
+        const int v = u - BT * 32, r = v >> 3, k = v & 7;
+        st16(dst + (r * CH + ((L / 8 + k) ^ swz_row(r))) * 16,
+             *(const u32x4*)(fsrc + r * kFp8RowBytes + kFp8ROff + k * 16));
+      }
+    }
+  };
+  // before the first step: tiles 0, 1 converted (and 2, 3 issued), with three barriers
+  auto prologue8 = [&]() {
+    issue8();
+    issue8();
+    issue8();
+    wait8(0);
+    __syncthreads();
+    convert8(0);
+    wait8(1);
+    __syncthreads();
+    issue8();  // tile 3, into the slot tile 0 used
+    convert8(1);
+    __syncthreads();
+  };
+  // after step t's barrier: tile t + 4 issued, tile t + 2 converted into the slot tile t used
+  auto step8 = [&](int t) {
+    issue8();
+    convert8(t + 2);
+    wait8(t + 3);
+    __syncthreads();
+  };
 
   // The two roles run separate code with the same barriers, so that the score waves' q~
   // registers and the P.V waves' accumulators are never live at the same point.
@@ -171,12 +258,24 @@ __global__ __launch_bounds__(k3dec::NTHREADS) void decode_attn_k3_kernel(DecodeA
       if (g2 == 0) alpha_s[t & 1][head] = alpha;
     };
 
-    __syncthreads();  // tile 0 is in LDS
-    if (n_tiles > 0) score_tile(0);
-    __syncthreads();  // P of tile 0 is ready; tile 1 is in LDS
-    for (int t = 0; t < n_tiles; ++t) {
-      if (t + 1 < n_tiles) score_tile(t + 1);
-      __syncthreads();
+    if constexpr (FP8) {
+      prologue8();
+      if (n_tiles > 0) score_tile(0);
+      wait8(2);
+      __syncthreads();  // P of tile 0 is ready
+      for (int t = 0; t < n_tiles; ++t) {
+        if (t + 1 < n_tiles) score_tile(t + 1);
+        __syncthreads();
+        step8(t);
+      }
+    } else {
+      __syncthreads();  // tile 0 is in LDS
+      if (n_tiles > 0) score_tile(0);
+      __syncthreads();  // P of tile 0 is ready; tile 1 is in LDS
+      for (int t = 0; t < n_tiles; ++t) {
+        if (t + 1 < n_tiles) score_tile(t + 1);
+        __syncthreads();
+      }
     }
     const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
     if (g2 == 0) {
@@ -222,20 +321,26 @@ __global__ __launch_bounds__(k3dec::NTHREADS) void decode_attn_k3_kernel(DecodeA
     };
     // tiles issued so far are [0, issued); wait until tile `need` has landed
     auto wait_for = [&](int need, int issued) { wait_tiles_in_flight(max(0, issued - 1 - need)); };
-    int issued = min(n_tiles, NSLOT - 1);
+    int issued = FP8 ? 0 : min(n_tiles, NSLOT - 1);
     for (int t = 0; t < issued; ++t) issue(t);
-    wait_for(0, issued);
+    if (!FP8) wait_for(0, issued);
     const int G = lane >> 4, jj = lane & 15;
     f32x16 o[4][3];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 3; ++j) o[i][j] = f32x16{};
-    __syncthreads();  // tile 0 is in LDS
-    if (n_tiles > 1) wait_for(1, issued);
-    __syncthreads();  // P of tile 0 is ready; tile 1 is in LDS
+    if constexpr (FP8) {
+      prologue8();
+      wait8(2);
+      __syncthreads();  // P of tile 0 is ready
+    } else {
+      __syncthreads();  // tile 0 is in LDS
+      if (n_tiles > 1) wait_for(1, issued);
+      __syncthreads();  // P of tile 0 is ready; tile 1 is in LDS
+    }
     for (int t = 0; t < n_tiles; ++t) {
-      if (issued < n_tiles) issue(issued++);  // tile t + NSLOT - 1, into the slot tile t-1 used
+      if (!FP8 && issued < n_tiles) issue(issued++);  // tile t + NSLOT - 1, into the slot tile t-1 used
       const uint8_t* slot = lat_s[t % NSLOT];
       const uint16_t* pbuf = Ps[t & 1];
       float al[3];
@@ -273,8 +378,9 @@ __global__ __launch_bounds__(k3dec::NTHREADS) void decode_attn_k3_kernel(DecodeA
         for (int hs = 0; hs < 3; ++hs) o[k & 3][hs] = mfma32(af, pb[k >> 2][hs], o[k & 3][hs]);
         af = an;
       }
-      if (t + 2 < n_tiles) wait_for(t + 2, issued);  // the score waves read it in the next step
+      if (!FP8 && t + 2 < n_tiles) wait_for(t + 2, issued);  // the score waves read it in the next step
       __syncthreads();
+      if constexpr (FP8) step8(t);
     }
     __syncthreads();  // 1/l of every head is in LDS
     if (a.n_splits == 1 && !a.lse) {  // one split: its normalised output is the result
@@ -312,10 +418,14 @@ __global__ __launch_bounds__(k3dec::NTHREADS) void decode_attn_k3_kernel(DecodeA
 
 hipError_t launch_decode_attention_k3(const DecodeAttnArgs& a, bool gather, hipStream_t st) {
   const int grid = a.B * a.n_splits;
-  if (gather)
-    decode_attn_k3_kernel<true><<<grid, k3dec::NTHREADS, 0, st>>>(a);
+  if (gather && a.fp8)
+    decode_attn_k3_kernel<true, true><<<grid, k3dec::NTHREADS, 0, st>>>(a);
+  else if (gather)
+    decode_attn_k3_kernel<true, false><<<grid, k3dec::NTHREADS, 0, st>>>(a);
+  else if (a.fp8)
+    decode_attn_k3_kernel<false, true><<<grid, k3dec::NTHREADS, 0, st>>>(a);
   else
-    decode_attn_k3_kernel<false><<<grid, k3dec::NTHREADS, 0, st>>>(a);
+    decode_attn_k3_kernel<false, false><<<grid, k3dec::NTHREADS, 0, st>>>(a);
   return hipGetLastError();
 }
 

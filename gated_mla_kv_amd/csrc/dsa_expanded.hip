@@ -7,7 +7,9 @@
 // 256 bytes per position, each read once; two 32-position tiles in flight per wave, eight waves
 // per 2048-position workgroup). Lane l ends with position l%32 and 16 heads, so the
 // head-weighted ReLU sum is in-lane plus one xor-32 shuffle. 1/sqrt(32*128) = 1/64 is folded
-// into a exactly.
+// into a exactly. FP8 index keys (128 E4M3 codes and one scale s >= 0 per position, the blog's
+// cache section) load 8 bytes per lane and k-step, widen exactly to bf16, and the position's
+// score is multiplied by s (ReLU(s z) = s ReLU(z) for s >= 0).
 //
 // Top-k (eq. (6)): S = the min(k, t) largest I, ties to the lower position, -0 == +0, written
 // in ascending position order, over order-preserving 32-bit keys of the fp32 scores.
@@ -56,13 +58,25 @@ __global__ __launch_bounds__(kScoreWaves * 64) void index_scores_kernel(IndexSco
   const int end = min(base + kScoreChunk, t);
   for (int i = threadIdx.x; i < kHistBins; i += kScoreWaves * 64) lhist[i] = 0;
   const uint16_t* kb = a.idx_k + (size_t)rm.seq * a.T_cap * DI;
+  const uint8_t* kb8 = (const uint8_t*)a.idx_k + (size_t)rm.seq * a.T_cap * DI;
+  const bool fp8 = a.idx_scale != nullptr;
   const int n_tiles = cdiv(end - base, 32);
   const int nt_w = wave < n_tiles ? cdiv(n_tiles - wave, kScoreWaves) : 0;  // this wave's tiles
-  // keys of this wave's j-th tile (positions p0 + l32): the B operand, one 16-byte load per k-step
+  // keys of this wave's j-th tile (positions p0 + l32): the B operand, one 16-byte (bf16) or
+  // 8-byte (FP8, widened when used) load per k-step
   auto load_keys = [&](int j, u32x4* kf) __attribute__((always_inline)) {
     const int pos = min(base + (wave + kScoreWaves * j) * 32 + l32, end - 1);  // past the end: not stored
+    if (fp8) {
 #pragma unroll
-    for (int s = 0; s < KS; ++s) kf[s] = ld16(kb + (size_t)pos * DI + s * 16 + g2 * 8);
+      for (int s = 0; s < KS; s += 2) {
+        const u32x2 w0 = ld8(kb8 + (size_t)pos * DI + s * 16 + g2 * 8);
+        const u32x2 w1 = ld8(kb8 + (size_t)pos * DI + (s + 1) * 16 + g2 * 8);
+        kf[s] = u32x4{w0.x, w0.y, w1.x, w1.y};  // raw codes, widened in score()
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < KS; ++s) kf[s] = ld16(kb + (size_t)pos * DI + s * 16 + g2 * 8);
+    }
   };
   u32x4 kf0[KS], kf1[KS];
   if (nt_w > 0) load_keys(0, kf0);
@@ -79,13 +93,24 @@ __global__ __launch_bounds__(kScoreWaves * 64) void index_scores_kernel(IndexSco
   __syncthreads();  // histogram cleared
   auto score = [&](int j, const u32x4* kf) __attribute__((always_inline)) {
     f32x16 acc = f32x16{};
+    if (fp8) {
 #pragma unroll
-    for (int s = 0; s < KS; ++s) acc = mfma32(qa[s], kf[s], acc);
+      for (int s = 0; s < KS; s += 2) {
+        const u32x2 a0 = e4m3x4_to_bf16(kf[s].x), a1 = e4m3x4_to_bf16(kf[s].y);
+        const u32x2 b0 = e4m3x4_to_bf16(kf[s].z), b1 = e4m3x4_to_bf16(kf[s].w);
+        acc = mfma32(qa[s], u32x4{a0.x, a0.y, a1.x, a1.y}, acc);
+        acc = mfma32(qa[s + 1], u32x4{b0.x, b0.y, b1.x, b1.y}, acc);
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < KS; ++s) acc = mfma32(qa[s], kf[s], acc);
+    }
     float sc = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) sc += wgt[r] * fmaxf(acc[r], 0.f);
     sc += __shfl_xor(sc, 32, 64);
     const int pos = base + (wave + kScoreWaves * j) * 32 + l32;
+    if (fp8) sc *= a.idx_scale[(size_t)rm.seq * a.T_cap + min(pos, end - 1)];
     if (pos < end && g2 == 0) {
       a.scores[(size_t)b * a.score_stride + pos] = sc;
       atomicAdd(&lhist[order_key(sc) >> 20], 1);

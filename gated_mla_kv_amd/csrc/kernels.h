@@ -22,11 +22,15 @@ struct KvAppendArgs {
   const uint16_t* k_nope; int ld_k_tok, ld_k_head;
   const uint16_t* v_new; int ld_v_tok, ld_v_head;
   const uint16_t* idx_new; int ld_idx;
-  uint16_t* latent;  // [B, T_cap, L+DS] or null
+  uint16_t* latent;  // [B, T_cap, L+DS] or null (FP8: [B, T_cap, kFp8RowBytes] bytes)
   uint16_t* k;       // [B, H, T_cap, DN+DS] or null
   uint16_t* v;       // [B, H, T_cap, DV] or null
-  uint16_t* idx;     // [B, T_cap, DI] or null
+  uint16_t* idx;     // [B, T_cap, DI] or null (FP8: [B, T_cap, DI] codes)
+  int latent_fp8, idx_fp8;
+  float* idx_scale;  // FP8 index keys: [B, T_cap] scales
 };
+// FP8 main-cache row (K3): 512 E4M3 codes of c, four fp32 scales (blocks of 128), r in bf16
+constexpr int kFp8Codes = 512, kFp8ScaleOff = 512, kFp8ROff = 528, kFp8RowBytes = 656;
 hipError_t launch_kv_append(const KvAppendArgs& a, hipStream_t s);
 
 struct PrefillAttnArgs {
@@ -59,6 +63,7 @@ struct DecodeAttnArgs {
   float* o_latent;  // [B, H, L]
   float* lse;       // [B, H] or null
   int row0, rows_per_seq;  // see row_map (latent rows of sequence row_map(..).seq)
+  int fp8;          // latent rows are FP8 main-cache rows (kFp8RowBytes each)
 };
 hipError_t launch_decode_attention(Shape s, const DecodeAttnArgs& a, bool gather, hipStream_t st);
 hipError_t launch_absorb_q(Shape s, const uint16_t* q, int ldq, const uint16_t* wkvb, int B,
@@ -81,7 +86,8 @@ __device__ __forceinline__ RowMap row_map(int row0, int rows_per_seq, int b) {
 struct IndexScoreArgs {
   const uint16_t* q_idx;  // [B, 32, 128]
   const float* w_idx;     // [B, 32]
-  const uint16_t* idx_k;  // [B, T_cap, 128]
+  const uint16_t* idx_k;  // [B, T_cap, 128] bf16, or E4M3 codes when idx_scale is set
+  const float* idx_scale; // [B, T_cap] FP8 key scales, or null
   const int32_t* n_vis;   // [B], plus vis_offset
   int vis_offset;
   int B, T_cap;

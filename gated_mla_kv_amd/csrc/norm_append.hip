@@ -8,6 +8,10 @@
 //   place of concatenation: the latent row c ‖ r, the expanded keys k_nope_h ‖ r for every
 //   head (the shared key part is the same r for all heads, shared-key-split page), the values
 //   and the index key. Pure 16-byte copies, bit-exact.
+//   FP8 caches (K3.1 Gated DSA blog, cache section): a latent row is the 512 E4M3 codes of c,
+//   four fp32 scales (blocks of 128) and r in bf16, 656 bytes; an index key is 128 codes with
+//   one fp32 scale kept in a separate array. A block's scale is its largest magnitude / 448
+//   (correctly rounded), a code is e4m3(v / scale) with the division correctly rounded.
 #include "common.h"
 #include "kernels.h"
 
@@ -74,6 +78,25 @@ __global__ __launch_bounds__(256) void layernorm_rows(const float* __restrict__ 
   }
 }
 
+// E4M3 codes of n = 8 * lanes values v (8 per lane, lanes in groups of `group` sharing a scale):
+// returns the 8 codes as two words and the group's scale.
+template <int GROUP>
+__device__ __forceinline__ u32x2 fp8_group(const u32x4 v, float& scale) {
+  float x[8] = {lo_bf16(v.x), hi_bf16(v.x), lo_bf16(v.y), hi_bf16(v.y),
+                lo_bf16(v.z), hi_bf16(v.z), lo_bf16(v.w), hi_bf16(v.w)};
+  float m = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(x[i]));
+#pragma unroll
+  for (int o = 1; o < GROUP; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+  scale = __fdiv_rn(m, 448.f);
+  uint32_t c[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    c[i] = scale > 0.f ? e4m3_encode(__fdiv_rn(x[i], scale)) : (__float_as_uint(x[i]) >> 24) & 0x80u;
+  return u32x2{c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24), c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24)};
+}
+
 // One workgroup per new token (b, t). Work items are 16-byte chunks:
 //   latent row: L/8 chunks of c then DS/8 of r; per head: DN/8 chunks of k_nope then DS/8 of r
 //   for K, DV/8 chunks for V; the index key: DI/8 chunks.
@@ -85,7 +108,17 @@ __global__ __launch_bounds__(256) void kv_append_kernel(KvAppendArgs a) {
   const size_t bt = (size_t)b * a.T + t;
   const int cL = a.L / 8, cS = a.DS / 8, cN = a.DN / 8, cV = a.DV / 8, cI = a.DI / 8;
   // latent
-  if (a.latent) {
+  if (a.latent && a.latent_fp8) {  // K3 only (L = 512, DS = 64): wave 0, lane l codes c[8l .. 8l+7]
+    if (threadIdx.x < 64) {
+      const int l = threadIdx.x;
+      uint8_t* row = (uint8_t*)a.latent + ((size_t)b * a.T_cap + p) * kFp8RowBytes;
+      float scale;
+      const u32x2 codes = fp8_group<16>(ld16(a.c + bt * a.ld_c + l * 8), scale);
+      *(u32x2*)(row + l * 8) = codes;
+      if ((l & 15) == 0) *(float*)(row + kFp8ScaleOff + (l >> 4) * 4) = scale;
+      if (l < 8) st16(row + kFp8ROff + l * 16, ld16(a.r + bt * a.ld_r + l * 8));
+    }
+  } else if (a.latent) {
     uint16_t* dst = a.latent + ((size_t)b * a.T_cap + p) * (a.L + a.DS);
     for (int i = threadIdx.x; i < cL + cS; i += blockDim.x) {
       const uint16_t* src = (i < cL) ? a.c + bt * a.ld_c + i * 8 : a.r + bt * a.ld_r + (i - cL) * 8;
@@ -110,7 +143,15 @@ __global__ __launch_bounds__(256) void kv_append_kernel(KvAppendArgs a) {
       st16(dst, ld16(src));
     }
   }
-  if (a.idx) {
+  if (a.idx && a.idx_fp8) {  // DI = 128: lanes 0..15 of wave 1, one scale per key
+    if (threadIdx.x >= 64 && threadIdx.x < 80) {
+      const int l = threadIdx.x - 64;
+      float scale;
+      const u32x2 codes = fp8_group<16>(ld16(a.idx_new + bt * a.ld_idx + l * 8), scale);
+      *(u32x2*)((uint8_t*)a.idx + ((size_t)b * a.T_cap + p) * a.DI + l * 8) = codes;
+      if (l == 0) a.idx_scale[(size_t)b * a.T_cap + p] = scale;
+    }
+  } else if (a.idx) {
     for (int i = threadIdx.x; i < cI; i += blockDim.x)
       st16(a.idx + ((size_t)b * a.T_cap + p) * a.DI + i * 8, ld16(a.idx_new + bt * a.ld_idx + i * 8));
   }

@@ -7,8 +7,9 @@ import ctypes
 import numpy as np
 import torch
 
-from . import (MlaCache, MlaWeights, OUT_BF16, PATH_ABSORBED, make_dims, mla_decode, mla_prefill,
-               workspace_bytes, mla_prefill_sparse, workspace_bytes_prefill_sparse)
+from . import (CACHE_BF16, CACHE_FP8, FP8_LATENT_ROW_BYTES, MlaCache, MlaWeights, OUT_BF16, PATH_ABSORBED,
+               make_dims, mla_decode, mla_prefill, workspace_bytes, mla_prefill_sparse,
+               workspace_bytes_prefill_sparse)
 
 _WEIGHT_NAMES = ("w_q_a", "g_q_a", "w_q_b", "w_kv_a", "g_kv_a", "w_kv_b", "w_g", "w_o",
                  "w_idx_q", "w_idx_k", "g_idx_k", "b_idx_k", "w_idx_w")
@@ -35,8 +36,9 @@ class LayerBuffers:
         self.w = {k: bf16_tensor(v, device) for k, v in weight_bits.items()}
         self.cw = MlaWeights(*[self.w[n].data_ptr() if n in self.w else None for n in _WEIGHT_NAMES])
 
-    def new_cache(self, B: int, T_cap: int, expanded: bool = True, index: bool = False):
-        return CacheBuffers(self.shape, B, T_cap, expanded, index, self.device)
+    def new_cache(self, B: int, T_cap: int, expanded: bool = True, index: bool = False, fp8_latent: bool = False,
+                  fp8_index: bool = False):
+        return CacheBuffers(self.shape, B, T_cap, expanded, index, self.device, fp8_latent, fp8_index)
 
     def workspace(self, B, T_new, max_len, path=PATH_ABSORBED, num_splits=0):
         n = workspace_bytes(self.dims, B, T_new, max_len, path, num_splits)
@@ -75,17 +77,31 @@ class LayerBuffers:
 
 
 class CacheBuffers:
-    """Caller-owned caches of one layer: latent, optional expanded K/V and index keys."""
+    """Caller-owned caches of one layer: latent, optional expanded K/V and index keys.
 
-    def __init__(self, d, B, T_cap, expanded=True, index=False, device="cuda"):
+    FP8 formats: ``latent`` is [B, T_cap, 656] uint8 rows (512 E4M3 codes, four fp32 scales,
+    64 bf16 shared-key values); ``idx`` is one uint8 buffer holding the [B, T_cap, 128] codes and
+    then the [B, T_cap] fp32 scales, viewed as ``idx_codes`` and ``idx_scales``."""
+
+    def __init__(self, d, B, T_cap, expanded=True, index=False, device="cuda", fp8_latent=False, fp8_index=False):
         bf = torch.bfloat16
-        self.latent = torch.zeros((B, T_cap, d.kv_lora + d.d_shared), dtype=bf, device=device)
+        if fp8_latent:
+            self.latent = torch.zeros((B, T_cap, FP8_LATENT_ROW_BYTES), dtype=torch.uint8, device=device)
+        else:
+            self.latent = torch.zeros((B, T_cap, d.kv_lora + d.d_shared), dtype=bf, device=device)
         self.k = torch.zeros((B, d.n_heads, T_cap, d.d_nope + d.d_shared), dtype=bf, device=device) if expanded else None
         self.v = torch.zeros((B, d.n_heads, T_cap, d.d_v), dtype=bf, device=device) if expanded else None
-        self.idx = torch.zeros((B, T_cap, d.d_idx), dtype=bf, device=device) if index else None
+        self.idx = self.idx_codes = self.idx_scales = None
+        if index and fp8_index:
+            self.idx = torch.zeros(B * T_cap * (d.d_idx + 4), dtype=torch.uint8, device=device)
+            self.idx_codes = self.idx[:B * T_cap * d.d_idx].view(B, T_cap, d.d_idx)
+            self.idx_scales = self.idx[B * T_cap * d.d_idx:].view(torch.float32).view(B, T_cap)
+        elif index:
+            self.idx = torch.zeros((B, T_cap, d.d_idx), dtype=bf, device=device)
         self.B, self.T_cap = B, T_cap
         p = lambda t: t.data_ptr() if t is not None else None  # noqa: E731
-        self.c = MlaCache(p(self.latent), p(self.k), p(self.v), p(self.idx), B, T_cap)
+        self.c = MlaCache(p(self.latent), p(self.k), p(self.v), p(self.idx), B, T_cap,
+                          CACHE_FP8 if fp8_latent else CACHE_BF16, CACHE_FP8 if fp8_index else CACHE_BF16)
 
     def struct(self) -> MlaCache:
         return self.c

@@ -90,14 +90,26 @@ typedef struct mla_weights {
 } mla_weights;
 
 /* Caller-owned caches with a fixed capacity of T_cap positions per sequence ([KV]; [DSA]
- * cache table). Unlike the pages' concatenating update, capacity is enforced. */
+ * cache table). Unlike the pages' concatenating update, capacity is enforced.
+ *
+ * Formats ([DSA] cache section, deployed caches): with latent_format = MLA_CACHE_FP8 a latent
+ * row is 656 bytes: the 512 OCP E4M3 codes of c_s, four fp32 scales (one per block of 128
+ * features; scale = max|c| / 448, code = e4m3(c / scale) rounded to nearest even), then r_s as
+ * 64 bf16. With idx_format = MLA_CACHE_FP8, idx_k holds [batch, T_cap, 128] E4M3 codes followed
+ * by [batch, T_cap] fp32 scales (132 bytes per position). Kernels read a value back as
+ * decode(code) * scale (the attention tile rounds it once to bf16). FP8 formats need the K3
+ * shape; others return MLA_ERR_UNSUPPORTED. Expanded k / v are always bf16. */
+enum { MLA_CACHE_BF16 = 0, MLA_CACHE_FP8 = 1 };
 typedef struct mla_cache {
-  void* latent;          /* [batch, T_cap, kv_lora + d_shared]: c_s (normalised) ‖ r_s */
+  void* latent;          /* [batch, T_cap, kv_lora + d_shared] bf16: c_s (normalised) ‖ r_s;
+                            FP8: [batch, T_cap, 656] bytes */
   void* k;               /* [batch, H, T_cap, d_nope + d_shared]: expanded keys, or NULL */
   void* v;               /* [batch, H, T_cap, d_v]: expanded values, or NULL */
-  void* idx_k;           /* [batch, T_cap, d_idx]: DSA index keys, or NULL */
+  void* idx_k;           /* [batch, T_cap, d_idx] bf16: DSA index keys, or NULL; FP8: see above */
   int32_t batch;
   int32_t T_cap;
+  int32_t latent_format; /* MLA_CACHE_BF16 or MLA_CACHE_FP8 */
+  int32_t idx_format;    /* MLA_CACHE_BF16 or MLA_CACHE_FP8 */
 } mla_cache;
 
 /* Status name ("MLA_OK", "MLA_ERR_SHAPE", ...). Never NULL. */
@@ -196,6 +208,15 @@ int dsa_index_topk(const mla_dims* dims, const void* q_idx, const float* w_idx,
                    const void* idx_k_cache, int32_t T_cap, const int32_t* n_visible,
                    int32_t max_visible, int32_t B, int32_t* out_idx, int32_t* out_cnt,
                    float* out_scores, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* As dsa_index_topk over FP8 index keys ([DSA] cache section): idx_k_codes [B, T_cap, 128] OCP
+ * E4M3 codes, idx_k_scales [B, T_cap] fp32 (>= 0); key s reads back as decode(code) * scale,
+ * so its score is scale times the score of the decoded codes. d_idx must be 128. */
+int dsa_index_topk_fp8(const mla_dims* dims, const void* q_idx, const float* w_idx,
+                       const void* idx_k_codes, const float* idx_k_scales, int32_t T_cap,
+                       const int32_t* n_visible, int32_t max_visible, int32_t B, int32_t* out_idx,
+                       int32_t* out_cnt, float* out_scores, void* ws, size_t ws_bytes,
+                       hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------------
  * Stage entry points: the kernels of the whole-layer calls, each callable alone so that every

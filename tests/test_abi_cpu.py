@@ -23,7 +23,7 @@ FAKE = 0x1000  # a non-null pointer value; never dereferenced by the validation 
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w]+\s*\*?\s*(mla_\w+|kv_append|dsa_index_topk)\s*\(",
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w]+\s*\*?\s*(mla_\w+|kv_append|dsa_index_topk\w*)\s*\(",
                                  text, flags=re.M)))
 
 
@@ -161,3 +161,23 @@ def test_prefill_sparse_validation():
     assert call(B=0) == OK
     assert gm.workspace_bytes_prefill_sparse(d, 2, 10, 50) > gm.workspace_bytes(d, 2, 10, 50)
     assert gm.workspace_bytes_prefill_sparse(gm.make_dims(K3.replace(n_idx_heads=0)), 2, 10, 50) == 0
+
+
+def test_cache_format_validation():
+    """FP8 caches exist for the K3 shape only; unknown formats are rejected before any launch."""
+    L = gm.lib()
+    call = lambda dims, cc: L.kv_append(ctypes.byref(gm.make_dims(dims)), ctypes.byref(cc), FAKE, 8, 2, 4,  # noqa: E731
+                                        FAKE, FAKE, None, None, None, None)
+    c = _cache(T_cap=16)
+    c.latent_format = gm.CACHE_FP8
+    assert call(TINY, c) == ERR_UNSUPPORTED
+    c.latent_format = 7
+    assert call(K3, c) == ERR_UNSUPPORTED
+    c.latent_format, c.idx_format = gm.CACHE_BF16, 2
+    assert call(K3, c) == ERR_UNSUPPORTED
+    # and the decode entry points see the same check
+    c2 = _cache()
+    c2.latent_format = gm.CACHE_FP8
+    assert _call_decode(gm.make_dims(TINY), c2) == ERR_UNSUPPORTED
+    assert L.dsa_index_topk_fp8(ctypes.byref(gm.make_dims(K3)), FAKE, FAKE, FAKE, None, 10, FAKE, 5, 1, FAKE,
+                                FAKE, None, FAKE, 1 << 30, None) == ERR_NULL
