@@ -13,11 +13,13 @@ Readings where the page is silent (listed with their support in the design notes
 * The four latent scales belong to four blocks of 128 consecutive latent features (a latent
   narrower than 128, as in the small test layer, is one block); the index key has one scale
   for its 128 features.
-* A block's scale is its largest magnitude divided by 448, rounded to FP32 (so that block's
-  largest element maps to +-448); the code of a value v is v / scale computed in FP32 and
-  rounded to the nearest E4M3 value, ties to even, with the sign copied (a block of zeros has
-  scale 0 and codes +-0). Encoding saturates at 448: v / scale can exceed 448 by the FP32
-  rounding of the scale, never by half an E4M3 step.
+* A block's scale is the smallest power of two 2^k (k >= -126, an FP32 value) with
+  max|v| <= 448 * 2^k, so the block's largest element codes into [224, 448]; the code of a value
+  v is v / 2^k (exact) rounded to the nearest E4M3 value, ties to even, with the sign copied (a
+  block of zeros has scale 0 and codes +-0). The page gives the scales' type, not their rule; a
+  power of two keeps E4M3's full relative precision, makes the division exact, and makes
+  decode(code) * scale an exponent shift that gfx950's scaled FP8 conversions perform in one
+  instruction.
 * A cached index key reads back as decode(code) * scale, exact in float64. A cached latent
   value reads back in the layer's compute type: decode(code) * scale formed in FP32 and rounded
   once to BF16 (the page's deployed path feeds the main cache to BF16 attention kernels; the
@@ -69,16 +71,20 @@ def e4m3_encode(x) -> np.ndarray:
 def quantize_blocks(v, block: int):
     """v [..., n] (values of the cache type) -> codes [..., n] uint8, scales [..., n/block] fp32.
 
-    scale = fp32(max|v| / 448) per block; code = e4m3(fp32(v / scale)), 0 where scale = 0.
+    scale = the smallest 2^k (k >= -126) with max|v| <= 448 * 2^k per block, 0 for a zero block;
+    code = e4m3(v / scale).
     """
     v = np.asarray(v, dtype=F64)
     n = v.shape[-1]
     vb = v.reshape(v.shape[:-1] + (n // block, block))
-    absmax = np.abs(vb).max(-1).astype(np.float32)              # exact: v holds bf16 values
-    scale = absmax / np.float32(E4M3_MAX)                        # fp32 division, correctly rounded
-    safe = np.where(scale > 0, scale, np.float32(1))
-    ratio = vb.astype(np.float32) / safe[..., None]              # fp32 division
-    codes = np.where(scale[..., None] > 0, e4m3_encode(ratio), e4m3_encode(vb * 0.0))
+    absmax = np.abs(vb).max(-1)
+    # absmax = f * 2^E with 0.5 <= f < 1, and 448 = 0.875 * 2^9: the bound holds for k = E - 9
+    # when f <= 0.875, else for k = E - 8
+    f, E = np.frexp(np.where(absmax > 0, absmax, 1.0))
+    k = np.maximum(np.where(f <= 0.875, E - 9, E - 8), -126)
+    scale = np.where(absmax > 0, np.ldexp(1.0, k), 0.0)
+    safe = np.where(scale > 0, scale, 1.0)
+    codes = np.where(scale[..., None] > 0, e4m3_encode(vb / safe[..., None]), e4m3_encode(vb * 0.0))
     return codes.reshape(v.shape).astype(np.uint8), scale.astype(np.float32)
 
 

@@ -71,17 +71,19 @@ def test_block_quantizer_scale_and_error_bound():
     codes, scales = F.quantize_latent(v, K3)
     assert codes.shape == (64, 512) and scales.shape == (64, 4) and scales.dtype == np.float32
     vb = v.reshape(64, 4, 128)
-    # the scale is the block's largest magnitude over 448, in fp32; that element codes to +-448
-    assert np.array_equal(scales, (np.abs(vb).max(-1).astype(np.float32) / np.float32(448)))
+    # the scale is the smallest power of two with max|v| <= 448 * scale
+    amax = np.abs(vb).max(-1)
+    m, e = np.frexp(scales.astype(np.float64))
+    assert np.all(m == 0.5) and np.all(amax <= 448 * scales) and np.all(amax > 224 * scales)
+    # so the block's largest element codes into [224, 448] (just above 224 rounds to 224)
     cb = codes.reshape(64, 4, 128)
     top = np.abs(vb).argmax(-1)
-    top_codes = np.take_along_axis(cb, top[..., None], -1)[..., 0]
-    assert np.all((top_codes & 0x7F) == 0x7E)
-    # read-back error: half an E4M3 step (2^-4 relative; 2^-10 * scale below the normal range),
-    # plus the fp32 rounding of v / scale
+    top_vals = np.abs(F.e4m3_decode(np.take_along_axis(cb, top[..., None], -1)[..., 0]))
+    assert np.all((top_vals >= 224) & (top_vals <= 448))
+    # read-back error: half an E4M3 step (2^-4 relative; 2^-10 * scale below the normal range)
     back = F.dequantize_latent(codes, scales)
     s = np.repeat(scales.astype(np.float64), 128, -1)
-    assert np.all(np.abs(back - v) <= (2.0 ** -4 + 2.0 ** -22) * np.abs(v) + 2.0 ** -10 * s)
+    assert np.all(np.abs(back - v) <= 2.0 ** -4 * np.abs(v) + 2.0 ** -10 * s)
     # exactly representable values come back exactly
     assert np.array_equal(F.dequantize_latent(*F.quantize_latent(back, K3)), back)
 
@@ -90,10 +92,9 @@ def test_zero_block():
     v = np.zeros((2, 512))
     v[1, 200] = -3.0
     codes, scales = F.quantize_latent(v, K3)
-    assert scales[0].tolist() == [0, 0, 0, 0] and scales[1, 1] == np.float32(3.0 / 448)
+    assert scales[0].tolist() == [0, 0, 0, 0] and scales[1, 1] == 2.0 ** -7   # 3 <= 448 / 128
     assert np.all(F.dequantize_latent(codes, scales)[0] == 0)
-    # the largest element reads back as -448 * fp32(3 / 448), within 2^-24 relative of -3
-    assert F.dequantize_latent(codes, scales)[1, 200] == -448.0 * np.float64(np.float32(3.0) / np.float32(448))
+    assert F.dequantize_latent(codes, scales)[1, 200] == -3.0                  # 384 * 2^-7, exact
 
 
 def test_cache_reads_back_dequantized_values():
@@ -163,6 +164,21 @@ def test_latent_read_back_matches_torch():
     vals = torch.from_numpy(codes).view(torch.float8_e4m3fn).float().reshape(50, 4, 128)
     ref = (vals * torch.from_numpy(scales)[..., None]).to(torch.bfloat16).double().reshape(50, 512).numpy()
     assert np.array_equal(got, ref)
-    # within one bf16 rounding (2^-8 relative) of the exact read-back value
+    # within one bf16 rounding (2^-8 relative) of the exact read-back value, and equal to it for
+    # power-of-two scales (the quantizer's): E4M3 values are bf16 values
     exact = F.dequantize_latent(codes, scales)
     assert np.all(np.abs(got - exact) <= 2.0 ** -8 * np.abs(exact) * (1 + 2.0 ** -20))
+    pow2 = np.ldexp(1.0, rng.integers(-30, 5, (50, 4))).astype(np.float32)
+    assert np.array_equal(F.latent_read_back(codes, pow2), F.dequantize_latent(codes, pow2))
+
+
+def test_power_of_two_scale_at_the_boundary():
+    """max|v| exactly 448 * 2^k takes scale 2^k (the element codes to 448); just above takes 2^(k+1)."""
+    v = np.zeros((3, 128))
+    v[0, 0] = 448.0 * 2.0 ** -5
+    v[1, 0] = 450.0 * 2.0 ** -5      # the next bf16 value above 448 * 2^-5
+    v[2, 0] = 224.0 * 2.0 ** -5
+    codes, scales = F.quantize_blocks(v, 128)
+    assert scales[0, 0] == 2.0 ** -5 and F.e4m3_decode(codes[0, 0]) == 448
+    assert scales[1, 0] == 2.0 ** -4
+    assert scales[2, 0] == 2.0 ** -6 and F.e4m3_decode(codes[2, 0]) == 448
