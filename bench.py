@@ -182,6 +182,24 @@ def decode_benches(args, d, lw, log):
     log(f"[bench] whole mla_decode step (absorbed): {out['mla_decode_step_us']:.1f} us")
     del dc2, wsd
 
+    # the same sequences in the FP8 main cache (656 B per position), quantized by kv_append (setup)
+    fcache = L.new_cache(B, nvis, expanded=False, fp8_latent=True)
+    zpos = torch.zeros(B, dtype=torch.int32, device=dev)
+    gm.kv_append(L.dims, fcache.c, zpos, nvis, B, nvis, lat[..., :d.kv_lora].contiguous(),
+                 lat[..., d.kv_lora:].contiguous())
+    dec8 = lambda: gm.mla_decode_attention(L.dims, qt, fcache.c, n_vis, nvis, B, o, None, 0, dws)  # noqa: E731
+    dec8()
+    torch.cuda.synchronize()
+    t8 = median(time_events(dec8, it, flush=flush))
+    b8 = B * nvis * gm.FP8_LATENT_ROW_BYTES
+    r8 = roof_hbm("decode_attn_k3_kernel<fp8>+decode_merge_kernel", b8, t8 * 1e3, "decode_fp8:B32_T8192")
+    log(f"[bench] FP8-cache absorbed decode attention: {t8 * 1e3:.1f} us, {r8['achieved']:.0f} GB/s "
+        f"({kv_bytes / (t8 * 1e-3) / 1e9:.0f} GB/s of bf16-cache bytes)")
+    out["fp8_cache"] = {"workload": "K3 absorbed decode attention, B=32, cache T=8192 (8193 visible), FP8 latent "
+                                    "cache (656 B per position)", "kv_bytes": b8, "us": round(t8 * 1e3, 2),
+                        "value": r8["achieved"], "unit": "GB/s", "roofline": r8}
+    del fcache
+
     # expanded cache for the same sequences, built from the latents by the kv_b projection (setup)
     log("[bench] expanded decode workload: building K/V [32, 96, 8193, 192|128] from the latents")
     ecache = L.new_cache(B, nvis, expanded=True)
@@ -247,7 +265,7 @@ def decode_benches(args, d, lw, log):
     idx5 = bf16_tensor(make_index_prefix(dd, B5, nv5, seed=0), dev)
     c5 = gm.MlaCache(lat5.data_ptr(), None, None, idx5.data_ptr(), B5, nv5)
     f32 = lambda bits: torch.from_numpy((bits.astype("uint32") << 16).view("float32")).to(dev)  # noqa: E731
-    qi = f32(normal_bf16((B5, dd.n_idx_heads, dd.d_idx), 0.5, 0, 25))
+    qi = bf16_tensor(normal_bf16((B5, dd.n_idx_heads, dd.d_idx), 0.5, 0, 25), dev)  # bf16, as the kernels take it
     wi = f32(normal_bf16((B5, dd.n_idx_heads), 1.0, 0, 26))
     n5 = torch.full((B5,), nv5, dtype=torch.int32, device=dev)
     sel = torch.empty((B5, dd.topk), dtype=torch.int32, device=dev)
@@ -280,6 +298,31 @@ def decode_benches(args, d, lw, log):
                                  "gbs": round(b_idx / (t_topk * 1e-6 * 1e3) / 1e9, 1)},
                   "sparse_attention": {"us": round(t_sparse * 1e3, 2), "bytes": b_sel,
                                        "gbs": round(b_sel / (t_sparse * 1e-6 * 1e3) / 1e9, 1)}}
+    # the same DSA step over FP8 caches (656 B latent rows, 132 B index keys), quantized by kv_append
+    f5 = L5.new_cache(B5, nv5, expanded=False, index=True, fp8_latent=True, fp8_index=True)
+    gm.kv_append(L5.dims, f5.c, torch.zeros(B5, dtype=torch.int32, device=dev), nv5, B5, nv5,
+                 lat5[..., :dd.kv_lora].contiguous(), lat5[..., dd.kv_lora:].contiguous(), None, None, idx5)
+    topk8 = lambda: gm.dsa_index_topk_fp8(L5.dims, qi, wi, f5.idx_codes, f5.idx_scales, nv5, n5, nv5, B5,  # noqa: E731
+                                          sel, cnt, None, ws5)
+    sparse8 = lambda: gm.mla_sparse_attention(L5.dims, qt5, f5.c, sel, cnt, B5, o5, None, 0, ws5)  # noqa: E731
+
+    def dsa8_fn():
+        topk8()
+        sparse8()
+
+    dsa8_fn()
+    torch.cuda.synchronize()
+    t8 = median(time_events(dsa8_fn, it, flush=flush))
+    t8_topk = median(time_events(topk8, it, flush=flush))
+    b8 = B5 * nv5 * (dd.d_idx + 4) + B5 * dd.topk * gm.FP8_LATENT_ROW_BYTES
+    r8 = roof_hbm("index_scores_kernel<fp8>+topk kernels+decode_attn_k3_kernel<gather,fp8>+decode_merge_kernel",
+                  b8, t8 * 1e3, "dsa_fp8:B8_T65536")
+    log(f"[bench] FP8-cache DSA decode: index+top-k {t8_topk * 1e3:.1f} us, together {t8 * 1e3:.1f} us, "
+        f"{r8['achieved']:.0f} GB/s")
+    out["dsa"]["fp8_cache"] = {"workload": "K3.1 Gated DSA decode, B=8, T=65536, FP8 caches (132 B index keys, "
+                                           "656 B latent rows)", "bytes": b8, "us": round(t8 * 1e3, 2),
+                               "index_topk_us": round(t8_topk * 1e3, 2), "value": r8["achieved"], "unit": "GB/s",
+                               "roofline": r8}
     del flush_buf
     return out
 

@@ -25,9 +25,10 @@
 // * FP8 main cache (K3.1 Gated DSA blog, cache section: 512 E4M3 codes, four fp32 block scales
 //   and r in bf16 per 656-byte row): all seven waves DMA the raw rows (3 of a tile's 21
 //   wave-wide loads each) into a 3-slot ring; after each step's barrier they convert the tile
-//   two ahead into the bf16 tile layout above (decode(code) * scale in fp32, rounded once to
-//   bf16; r copied), into the slot the P.V waves just released, then a second barrier. The
-//   MFMA code is the same; two bf16 slots instead of four.
+//   two ahead into the bf16 tile layout above (decode(code) * scale: the scales are powers of
+//   two, so one v_cvt_scalef32_pk_bf16_fp8 per two values, exact; r copied), into the slot the
+//   P.V waves just released, then a second barrier. The MFMA code is the same; two bf16 slots
+//   instead of four.
 // * Each split writes its output divided by its own softmax sum, in fp16: a convex combination
 //   of cached rows, so bounded by the largest latent entry, at half the bytes of fp32 partials
 //   (11-bit significand; the merge weights them by 2^(m - M) * l in fp32).
@@ -143,11 +144,8 @@ __global__ __launch_bounds__(k3dec::NTHREADS) void decode_attn_k3_kernel(DecodeA
         uint32_t o[8];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          typedef float f2 __attribute__((ext_vector_type(2)));
-          const f2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)ws[q], false);
-          const f2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)ws[q], true);
-          o[2 * q] = pack_bf16x2(lo.x * sc, lo.y * sc);
-          o[2 * q + 1] = pack_bf16x2(hi.x * sc, hi.y * sc);
+          o[2 * q] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)ws[q], sc, false));
+          o[2 * q + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)ws[q], sc, true));
         }
         const int sw = swz_row(r);
         st16(dst + (r * CH + ((2 * j) ^ sw)) * 16, u32x4{o[0], o[1], o[2], o[3]});
@@ -173,11 +171,11 @@ __global__ __launch_bounds__(k3dec::NTHREADS) void decode_attn_k3_kernel(DecodeA
     convert8(1);
     __syncthreads();
   };
-  // after step t's barrier: tile t + 4 issued, tile t + 2 converted into the slot tile t used
+  // after step t's barrier (each wave waited for its loads of tile t + 2 before it): tile t + 4
+  // issued, tile t + 2 converted into the slot tile t used
   auto step8 = [&](int t) {
     issue8();
     convert8(t + 2);
-    wait8(t + 3);
     __syncthreads();
   };
 
@@ -265,6 +263,7 @@ __global__ __launch_bounds__(k3dec::NTHREADS) void decode_attn_k3_kernel(DecodeA
       __syncthreads();  // P of tile 0 is ready
       for (int t = 0; t < n_tiles; ++t) {
         if (t + 1 < n_tiles) score_tile(t + 1);
+        wait8(t + 2);
         __syncthreads();
         step8(t);
       }
@@ -379,6 +378,7 @@ __global__ __launch_bounds__(k3dec::NTHREADS) void decode_attn_k3_kernel(DecodeA
         af = an;
       }
       if (!FP8 && t + 2 < n_tiles) wait_for(t + 2, issued);  // the score waves read it in the next step
+      if (FP8) wait8(t + 2);  // converted after this barrier
       __syncthreads();
       if constexpr (FP8) step8(t);
     }

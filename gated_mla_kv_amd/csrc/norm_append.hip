@@ -10,8 +10,8 @@
 //   and the index key. Pure 16-byte copies, bit-exact.
 //   FP8 caches (K3.1 Gated DSA blog, cache section): a latent row is the 512 E4M3 codes of c,
 //   four fp32 scales (blocks of 128) and r in bf16, 656 bytes; an index key is 128 codes with
-//   one fp32 scale kept in a separate array. A block's scale is its largest magnitude / 448
-//   (correctly rounded), a code is e4m3(v / scale) with the division correctly rounded.
+//   one fp32 scale kept in a separate array. A block's scale is the smallest power of two 2^k
+//   (k >= -126) with max|v| <= 448 * 2^k; a code is e4m3(v * 2^-k), the product exact.
 #include "common.h"
 #include "kernels.h"
 
@@ -89,11 +89,16 @@ __device__ __forceinline__ u32x2 fp8_group(const u32x4 v, float& scale) {
   for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(x[i]));
 #pragma unroll
   for (int o = 1; o < GROUP; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-  scale = __fdiv_rn(m, 448.f);
+  // m = 1.f * 2^(e - 127): 448 * 2^k >= m for k = e - 135 when 1.f <= 1.75, else for k = e - 134
+  const uint32_t mb = __float_as_uint(m);
+  const int e = (int)(mb >> 23);
+  const int k = max((mb & 0x7FFFFFu) <= 0x600000u ? e - 135 : e - 134, -126);
+  scale = m > 0.f ? __uint_as_float((uint32_t)(k + 127) << 23) : 0.f;
+  const float inv = __uint_as_float((uint32_t)(127 - k) << 23);  // 2^-k, exact
   uint32_t c[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i)
-    c[i] = scale > 0.f ? e4m3_encode(__fdiv_rn(x[i], scale)) : (__float_as_uint(x[i]) >> 24) & 0x80u;
+    c[i] = m > 0.f ? e4m3_encode(x[i] * inv) : (__float_as_uint(x[i]) >> 24) & 0x80u;
   return u32x2{c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24), c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24)};
 }
 

@@ -94,11 +94,12 @@ typedef struct mla_weights {
  *
  * Formats ([DSA] cache section, deployed caches): with latent_format = MLA_CACHE_FP8 a latent
  * row is 656 bytes: the 512 OCP E4M3 codes of c_s, four fp32 scales (one per block of 128
- * features; scale = max|c| / 448, code = e4m3(c / scale) rounded to nearest even), then r_s as
- * 64 bf16. With idx_format = MLA_CACHE_FP8, idx_k holds [batch, T_cap, 128] E4M3 codes followed
- * by [batch, T_cap] fp32 scales (132 bytes per position). Kernels read a value back as
- * decode(code) * scale (the attention tile rounds it once to bf16). FP8 formats need the K3
- * shape; others return MLA_ERR_UNSUPPORTED. Expanded k / v are always bf16. */
+ * features: the smallest power of two 2^k, k >= -126, with max|c| <= 448 * 2^k; code =
+ * e4m3(c / 2^k) rounded to nearest even), then r_s as 64 bf16. With idx_format =
+ * MLA_CACHE_FP8, idx_k holds [batch, T_cap, 128] E4M3 codes followed by [batch, T_cap] fp32
+ * scales of the same rule (132 bytes per position). A value reads back as decode(code) * scale.
+ * kv_append writes these formats; FP8 formats need the K3 shape, others return
+ * MLA_ERR_UNSUPPORTED. Expanded k / v are always bf16. */
 enum { MLA_CACHE_BF16 = 0, MLA_CACHE_FP8 = 1 };
 typedef struct mla_cache {
   void* latent;          /* [batch, T_cap, kv_lora + d_shared] bf16: c_s (normalised) ‖ r_s;

@@ -9,7 +9,9 @@ the oracle computes one by one (sampled rows, heads and sequences):
 * Gated DSA decode, B=8, cache T=65536: index scores, top-2048 (boundary rule), sparse attention,
   and the whole sparse mla_decode step for sampled sequences;
 * Gated DSA prefill, B=1, T=4096, top-2048: sampled rows past 2048 (where the selection drops
-  positions) against the oracle's DSA steps over the first 2,100 tokens.
+  positions) against the oracle's DSA steps over the first 2,100 tokens;
+* FP8 caches (656-byte latent rows, 132-byte index keys) written by kv_append: absorbed decode
+  at B=32, T=8192, and the DSA index scores, top-2048 and sparse attention at B=8, T=65536.
 Large inputs are drawn on the device (workloads.device_normal_bf16); the oracle gets the rows
 copied back."""
 import numpy as np
@@ -263,3 +265,71 @@ def test_decode_step_full_size(k3_weights, path):
         else:
             y_ref, _ = O.layer_forward(xb[:, None], w64, oc, d, form="absorbed")
             check_rows(to_np(y[b]), y_ref[0, 0], f"absorbed decode y b={b}")
+
+
+def _fp8_cache_from(lat, idx=None):
+    """FP8 caches quantized by kv_append from device bf16 rows (all positions of every sequence)."""
+    from gated_mla_kv_amd.layer import CacheBuffers
+    B, nvis = lat.shape[:2]
+    cache = CacheBuffers(D, B, nvis, expanded=False, index=idx is not None, fp8_latent=True,
+                         fp8_index=idx is not None)
+    gm.kv_append(gm.make_dims(D), cache.c, torch.zeros(B, dtype=torch.int32, device="cuda"), nvis, B, nvis,
+                 lat[..., :D.kv_lora].contiguous(), lat[..., D.kv_lora:].contiguous(), None, None, idx)
+    return cache
+
+
+def test_absorbed_decode_fp8_B32_T8192():
+    B, nvis = 32, 8193
+    print("FP8-cache absorbed decode B=32 n_vis=8193", flush=True)
+    lat = device_normal_bf16((B, nvis, D.d_latent), 1.0, 8, 1)
+    qt = device_normal_bf16((B, H, D.d_latent), 0.05, 8, 2)
+    dims = gm.make_dims(DD)
+    cache = _fp8_cache_from(lat)
+    n = torch.full((B,), nvis, dtype=torch.int32, device="cuda")
+    o = torch.empty((B, H, D.kv_lora), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, H), dtype=torch.float32, device="cuda")
+    ws = torch.empty(gm.workspace_bytes(dims, B, 1, nvis, gm.PATH_ABSORBED), dtype=torch.uint8, device="cuda")
+    gm.mla_decode_attention(dims, qt, cache.c, n, nvis, B, o, lse, 0, ws)
+    torch.cuda.synchronize()
+    for b in (0, 13, 31):
+        oc = O.Cache(DD, 1, expanded=False, fp8_latent=True)
+        oc.set_prefix(f64t(lat[b])[None])
+        o_ref, l_ref = O.attention_absorbed(f64t(qt[b])[None, None], oc.latent, O.softmax_scale(DD), nvis - 1, DD)
+        check_rows(to_np(o[b]), o_ref[0, 0], f"fp8 absorbed o b={b}")
+        check_scores(to_np(lse[b]), l_ref[0, :, 0], f"fp8 absorbed lse b={b}")
+
+
+def test_dsa_fp8_B8_T65536():
+    B, nvis = 8, 65537
+    print("FP8-cache DSA index + top-2048 + sparse attention B=8 n_vis=65537", flush=True)
+    dims = gm.make_dims(D)
+    lat = device_normal_bf16((B, nvis, D.d_latent), 1.0, 9, 1)
+    idx = device_normal_bf16((B, nvis, D.d_idx), 1.0, 9, 2)
+    qi = device_normal_bf16((B, D.n_idx_heads, D.d_idx), 0.5, 9, 3)
+    wi = normal_bf16((B, D.n_idx_heads), 1.0, 9, 4)
+    wi_d = torch.tensor(bf16_bits_to_f32(wi), device="cuda")
+    qt = device_normal_bf16((B, H, D.d_latent), 0.05, 9, 5)
+    cache = _fp8_cache_from(lat, idx)
+    n = torch.full((B,), nvis, dtype=torch.int32, device="cuda")
+    sel = torch.empty((B, D.topk), dtype=torch.int32, device="cuda")
+    cnt = torch.empty((B,), dtype=torch.int32, device="cuda")
+    scores = torch.empty((B, nvis), dtype=torch.float32, device="cuda")
+    ws = torch.empty(gm.workspace_bytes(dims, B, 1, nvis, gm.PATH_SPARSE), dtype=torch.uint8, device="cuda")
+    gm.dsa_index_topk_fp8(dims, qi, wi_d, cache.idx_codes, cache.idx_scales, nvis, n, nvis, B, sel, cnt, scores, ws)
+    o = torch.empty((B, H, D.kv_lora), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, H), dtype=torch.float32, device="cuda")
+    gm.mla_sparse_attention(dims, qt, cache.c, sel, cnt, B, o, lse, 0, ws)
+    torch.cuda.synchronize()
+    sel_h, cnt_h, sc_h = sel.cpu().numpy(), cnt.cpu().numpy(), scores.cpu().numpy().astype(np.float64)
+    for b in (0, 7):
+        oc = O.Cache(D, 1, expanded=False, fp8_latent=True, fp8_index=True)
+        oc.set_prefix(f64t(lat[b])[None], f64t(idx[b])[None])
+        ref = O.index_scores(f64t(qi[b]), bf16_bits_to_f32(wi[b]).astype(np.float64), oc.idx[0], nvis)
+        check_scores(sc_h[b], ref, f"fp8 index scores b={b}")
+        assert cnt_h[b] == D.topk
+        got = sel_h[b]
+        np.testing.assert_array_equal(got, O.select_topk(sc_h[b], D.topk))
+        _boundary_rule(got, ref, D.topk)
+        o_ref, l_ref = O.attention_absorbed_subset(f64t(qt[b]), oc.latent[0], got, O.softmax_scale(D), D)
+        check_rows(to_np(o[b]), o_ref, f"fp8 sparse o b={b}")
+        check_scores(to_np(lse[b]), l_ref, f"fp8 sparse lse b={b}")
