@@ -50,7 +50,9 @@ class MlaWeights(ctypes.Structure):
 class MlaCache(ctypes.Structure):
     _fields_ = [("latent", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
                 ("idx_k", ctypes.c_void_p), ("batch", ctypes.c_int32), ("T_cap", ctypes.c_int32),
-                ("latent_format", ctypes.c_int32), ("idx_format", ctypes.c_int32)]
+                ("latent_format", ctypes.c_int32), ("idx_format", ctypes.c_int32),
+                ("block_table", ctypes.c_void_p), ("page_size", ctypes.c_int32), ("max_blocks", ctypes.c_int32),
+                ("n_pages", ctypes.c_int32)]
 
 
 _lib = None

@@ -207,13 +207,28 @@ int check_cache(const mla_dims* d, const mla_cache* c, int B, int max_end) {
   const bool k3 = d->kv_lora == 512 && d->d_shared == 64 && d->n_heads == 96;
   if (fp8_latent(c) && !k3) return MLA_ERR_UNSUPPORTED;
   if (fp8_index(c) && (!k3 || d->d_idx != 128)) return MLA_ERR_UNSUPPORTED;
+  if (c->block_table) {  // paged latent / index caches ([DSA] pseudocode note on page mapping)
+    if (!k3 || c->k || c->v) return MLA_ERR_UNSUPPORTED;  // the expanded cache is not paged
+    if (c->page_size <= 0 || c->page_size % 32 != 0 || c->max_blocks <= 0 || c->n_pages <= 0)
+      return MLA_ERR_SHAPE;
+    if ((int64_t)c->page_size * c->max_blocks != c->T_cap) return MLA_ERR_SHAPE;
+    if ((int64_t)c->n_pages * c->page_size >= ((int64_t)1 << 31)) return MLA_ERR_SHAPE;
+  }
   return MLA_OK;
 }
 
-// FP8 index keys: the scales [batch, T_cap] follow the codes [batch, T_cap, d_idx]
+PageTable page_table(const mla_cache* c) {
+  PageTable p{};
+  if (c->block_table) p = PageTable{c->block_table, c->page_size, c->max_blocks, c->n_pages};
+  return p;
+}
+
+// FP8 index keys: the scales follow the codes, one per cache row ([batch, T_cap] rows, or
+// [n_pages, page_size] when paged)
 float* idx_scales(const mla_dims* d, const mla_cache* c) {
   if (!fp8_index(c) || !c->idx_k) return nullptr;
-  return (float*)((uint8_t*)c->idx_k + (size_t)c->batch * c->T_cap * d->d_idx);
+  const size_t rows = c->block_table ? (size_t)c->n_pages * c->page_size : (size_t)c->batch * c->T_cap;
+  return (float*)((uint8_t*)c->idx_k + rows * d->d_idx);
 }
 
 int check_weights(const mla_dims* d, const mla_weights* w) {
@@ -242,6 +257,7 @@ KvAppendArgs append_args(const mla_dims* d, const mla_cache* c, const int32_t* p
   a.latent_fp8 = fp8_latent(c);
   a.idx_fp8 = fp8_index(c);
   a.idx_scale = idx_scales(d, c);
+  a.pages = page_table(c);
   return a;
 }
 
@@ -388,6 +404,7 @@ static int decode_attention_common(const mla_dims* d, const void* q_tilde, const
   a.q_tilde = (const uint16_t*)q_tilde;
   a.latent = (const uint16_t*)cache->latent;
   a.fp8 = fp8_latent(cache);
+  a.pages = page_table(cache);
   a.n_vis = n_visible;
   a.vis_offset = 0;
   a.sel_idx = sel_idx;
@@ -637,6 +654,7 @@ int mla_prefill(const mla_dims* d, const mla_weights* w, const mla_cache* cache,
   if (!start_pos || !x || !y || !ws) return MLA_ERR_NULL;
   rc = check_cache(d, cache, B, max_end);
   if (rc) return rc;
+  if (cache->block_table) return MLA_ERR_UNSUPPORTED;  // dense prefill attends over the expanded cache
   if (!cache->k || !cache->v) return MLA_ERR_NULL;
   if (max_end < T) return MLA_ERR_SHAPE;
   if (out_dtype != MLA_OUT_BF16 && out_dtype != MLA_OUT_F32) return MLA_ERR_UNSUPPORTED;
@@ -755,6 +773,7 @@ int mla_prefill_sparse(const mla_dims* d, const mla_weights* w, const mla_cache*
     sa.w_idx = wsp.aw + (size_t)r0 * d->n_idx_heads;
     sa.idx_k = (const uint16_t*)cache->idx_k;
     sa.idx_scale = idx_scales(d, cache);
+    sa.pages = page_table(cache);
     sa.n_vis = start_pos;
     sa.vis_offset = 1;
     sa.B = n;
@@ -781,6 +800,7 @@ int mla_prefill_sparse(const mla_dims* d, const mla_weights* w, const mla_cache*
     a.q_tilde = sw.qt;
     a.latent = (const uint16_t*)cache->latent;
     a.fp8 = fp8_latent(cache);
+    a.pages = page_table(cache);
     a.sel_idx = sel;
     a.sel_cnt = cnt;
     a.sel_stride = d->topk;
@@ -909,6 +929,7 @@ int mla_decode(const mla_dims* d, const mla_weights* w, const mla_cache* cache, 
       sa.w_idx = wsp.aw;
       sa.idx_k = (const uint16_t*)cache->idx_k;
       sa.idx_scale = idx_scales(d, cache);
+      sa.pages = page_table(cache);
       sa.n_vis = seq_len;
       sa.vis_offset = 1;
       sa.B = B;
@@ -933,6 +954,7 @@ int mla_decode(const mla_dims* d, const mla_weights* w, const mla_cache* cache, 
     a.q_tilde = wsp.qt;
     a.latent = (const uint16_t*)cache->latent;
     a.fp8 = fp8_latent(cache);
+    a.pages = page_table(cache);
     a.n_vis = seq_len;
     a.vis_offset = 1;
     a.sel_idx = sel;

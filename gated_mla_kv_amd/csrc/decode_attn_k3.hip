@@ -90,13 +90,21 @@ __global__ __launch_bounds__(k3dec::NTHREADS) void decode_attn_k3_kernel(DecodeA
   const int p1 = min(p0 + a.chunk, n_vis);
   const int n_pos = GATHER ? min(max(p1 - p0, 0), MAX_SEL) : max(p1 - p0, 0);
   const int n_tiles = (n_pos + BT - 1) / BT;
-  const uint16_t* lat = a.latent + (size_t)row_map(a.row0, a.rows_per_seq, b).seq * a.T_cap * DL;
+  // cache rows: unpaged, position p of this sequence is row p past lat; paged, the page table
+  // gives the row within the pool (lat = the pool)
+  const int seq = row_map(a.row0, a.rows_per_seq, b).seq;
+  const bool paged = a.pages.table != nullptr;
+  const size_t seq_rows = paged ? 0 : (size_t)seq * a.T_cap;
+  auto crow = [&](int p) __attribute__((always_inline)) {
+    return paged ? (int)cache_row(a.pages, a.T_cap, seq, p) : p;
+  };
+  const uint16_t* lat = a.latent + seq_rows * DL;
 
-  if (GATHER) {  // this split's selected positions, clamped into the cache
+  if (GATHER) {  // this split's selected positions, clamped into the cache, as cache rows
     const int32_t* sel = a.sel_idx + (size_t)b * a.sel_stride;
     for (int i = tid; i < n_pos; i += NTHREADS) {
       const int p = sel[p0 + i];
-      sel_s[i] = (p >= 0 && p < a.T_cap) ? p : 0;
+      sel_s[i] = crow((p >= 0 && p < a.T_cap) ? p : 0);
     }
     __syncthreads();
   }
@@ -105,21 +113,22 @@ __global__ __launch_bounds__(k3dec::NTHREADS) void decode_attn_k3_kernel(DecodeA
   const size_t part = (size_t)b * a.n_splits + split;
 
   // ---- FP8 rows: issue, wait and convert, run by all seven waves with the same barriers ----
-  const uint8_t* lat8 = (const uint8_t*)a.latent + (size_t)row_map(a.row0, a.rows_per_seq, b).seq * a.T_cap * kFp8RowBytes;
+  const uint8_t* lat8 = (const uint8_t*)a.latent + seq_rows * kFp8RowBytes;
   int issued8 = 0;
   auto issue8 = [&]() {  // the next tile's raw rows: loads 3 w .. 3 w + 2 of its 21
     if (!FP8 || issued8 >= n_tiles) return;
     const int t = issued8++;
     const uint32_t fs = lds_addr(f8_s[t % 3]);
     const int j0 = t * BT;
+    const int row0 = GATHER ? 0 : crow(p0 + j0);  // a tile lies in one page
 #pragma unroll
     for (int k = 0; k < 3; ++k) {
       const int i = wave * 3 + k;
       const int P = min(i * 64 + lane, BT * F8CH - 1);  // the last load's upper half repeats a chunk
       const int r = P / F8CH, c = P - r * F8CH;
       const int jr = min(j0 + r, n_pos - 1);  // rows past the end repeat a valid row (masked)
-      const int pos = GATHER ? sel_s[jr] : p0 + jr;
-      lds_dma16(lat8 + (size_t)pos * kFp8RowBytes + c * 16, fs + i * 1024);
+      const int row = GATHER ? sel_s[jr] : row0 + (jr - j0);
+      lds_dma16(lat8 + (size_t)row * kFp8RowBytes + c * 16, fs + i * 1024);
     }
   };
   auto wait8 = [&](int need) {  // this wave's loads of tile `need` have landed
@@ -301,7 +310,9 @@ __global__ __launch_bounds__(k3dec::NTHREADS) void decode_attn_k3_kernel(DecodeA
       const uint32_t slot_addr = lds_addr(lat_s[t % NSLOT]);
       const int j0 = t * BT;
       if (!GATHER && j0 + BT <= n_pos) {  // whole tile of consecutive rows: offsets only
-        const char* base = (const char*)(lat + (size_t)(p0 + j0) * DL);
+        // a tile lies in one page; its first row is wave-uniform (the DMA takes it in SGPRs)
+        const int row0 = __builtin_amdgcn_readfirstlane(crow(p0 + j0));
+        const char* base = (const char*)(lat + (size_t)row0 * DL);
 #pragma unroll
         for (int k = 0; k < NLOAD_W; ++k)
           lds_dma16_sbase(doff[k] & 0xFFFFu, base, slot_addr + (pw * NLOAD_W + k) * 1024);
@@ -314,8 +325,8 @@ __global__ __launch_bounds__(k3dec::NTHREADS) void decode_attn_k3_kernel(DecodeA
         const int r = P / CH, cs = P - r * CH;
         const int c = cs ^ swz_row(r);
         const int jr = min(j0 + r, n_pos - 1);  // rows past the end repeat a valid row (masked)
-        const int pos = GATHER ? sel_s[jr] : p0 + jr;
-        lds_dma16(lat + (size_t)pos * DL + c * 8, slot_addr + i * 1024);
+        const int row = GATHER ? sel_s[jr] : crow(p0 + j0) + (jr - j0);
+        lds_dma16(lat + (size_t)row * DL + c * 8, slot_addr + i * 1024);
       }
     };
     // tiles issued so far are [0, issued); wait until tile `need` has landed

@@ -57,25 +57,30 @@ __global__ __launch_bounds__(kScoreWaves * 64) void index_scores_kernel(IndexSco
   if (base >= t) return;
   const int end = min(base + kScoreChunk, t);
   for (int i = threadIdx.x; i < kHistBins; i += kScoreWaves * 64) lhist[i] = 0;
-  const uint16_t* kb = a.idx_k + (size_t)rm.seq * a.T_cap * DI;
-  const uint8_t* kb8 = (const uint8_t*)a.idx_k + (size_t)rm.seq * a.T_cap * DI;
+  const uint16_t* kb = a.idx_k;                 // cache rows from cache_row (paged or not)
+  const uint8_t* kb8 = (const uint8_t*)a.idx_k;
   const bool fp8 = a.idx_scale != nullptr;
   const int n_tiles = cdiv(end - base, 32);
   const int nt_w = wave < n_tiles ? cdiv(n_tiles - wave, kScoreWaves) : 0;  // this wave's tiles
   // keys of this wave's j-th tile (positions p0 + l32): the B operand, one 16-byte (bf16) or
   // 8-byte (FP8, widened when used) load per k-step
+  // cache row of a position of this wave's j-th tile (a 32-position tile lies in one page)
+  auto key_row = [&](int j, int pos) __attribute__((always_inline)) {
+    const int p0 = base + (wave + kScoreWaves * j) * 32;
+    return cache_row(a.pages, a.T_cap, rm.seq, p0) + (pos - p0);
+  };
   auto load_keys = [&](int j, u32x4* kf) __attribute__((always_inline)) {
-    const int pos = min(base + (wave + kScoreWaves * j) * 32 + l32, end - 1);  // past the end: not stored
+    const size_t row = key_row(j, min(base + (wave + kScoreWaves * j) * 32 + l32, end - 1));  // past the end: not stored
     if (fp8) {
 #pragma unroll
       for (int s = 0; s < KS; s += 2) {
-        const u32x2 w0 = ld8(kb8 + (size_t)pos * DI + s * 16 + g2 * 8);
-        const u32x2 w1 = ld8(kb8 + (size_t)pos * DI + (s + 1) * 16 + g2 * 8);
+        const u32x2 w0 = ld8(kb8 + row * DI + s * 16 + g2 * 8);
+        const u32x2 w1 = ld8(kb8 + row * DI + (s + 1) * 16 + g2 * 8);
         kf[s] = u32x4{w0.x, w0.y, w1.x, w1.y};  // raw codes, widened in score()
       }
     } else {
 #pragma unroll
-      for (int s = 0; s < KS; ++s) kf[s] = ld16(kb + (size_t)pos * DI + s * 16 + g2 * 8);
+      for (int s = 0; s < KS; ++s) kf[s] = ld16(kb + row * DI + s * 16 + g2 * 8);
     }
   };
   u32x4 kf0[KS], kf1[KS];
@@ -110,7 +115,7 @@ __global__ __launch_bounds__(kScoreWaves * 64) void index_scores_kernel(IndexSco
     for (int r = 0; r < 16; ++r) sc += wgt[r] * fmaxf(acc[r], 0.f);
     sc += __shfl_xor(sc, 32, 64);
     const int pos = base + (wave + kScoreWaves * j) * 32 + l32;
-    if (fp8) sc *= a.idx_scale[(size_t)rm.seq * a.T_cap + min(pos, end - 1)];
+    if (fp8) sc *= a.idx_scale[key_row(j, min(pos, end - 1))];
     if (pos < end && g2 == 0) {
       a.scores[(size_t)b * a.score_stride + pos] = sc;
       atomicAdd(&lhist[order_key(sc) >> 20], 1);

@@ -14,6 +14,20 @@ hipError_t launch_rmsnorm(const float* x, int ldx, const uint16_t* gain, int M, 
 hipError_t launch_layernorm(const float* x, int ldx, const uint16_t* gain, const uint16_t* bias,
                             int M, int N, float eps, uint16_t* out, int ldo, hipStream_t s);
 
+// Paged latent and index caches: position p of sequence s lives in cache row
+//   table[s * max_blocks + p / page_size] * page_size + p % page_size
+// of a pool of n_pages pages (page indices clamped into the pool); without a table, in row
+// s * T_cap + p. page_size is a multiple of 32, so a 32-position tile never crosses a page.
+struct PageTable {
+  const int32_t* table;  // [batch, max_blocks] or null
+  int page_size, max_blocks, n_pages;
+};
+__device__ __forceinline__ size_t cache_row(const PageTable& pt, int T_cap, int seq, int pos) {
+  if (!pt.table) return (size_t)seq * T_cap + pos;
+  const int pg = min(max(pt.table[(size_t)seq * pt.max_blocks + pos / pt.page_size], 0), pt.n_pages - 1);
+  return (size_t)pg * pt.page_size + pos % pt.page_size;
+}
+
 struct KvAppendArgs {
   const int32_t* pos;  // [B] first position of each sequence's new tokens
   int B, T, T_cap, H, L, DS, DN, DV, DI;
@@ -28,6 +42,7 @@ struct KvAppendArgs {
   uint16_t* idx;     // [B, T_cap, DI] or null (FP8: [B, T_cap, DI] codes)
   int latent_fp8, idx_fp8;
   float* idx_scale;  // FP8 index keys: [B, T_cap] scales
+  PageTable pages;   // rows of latent / idx / idx_scale (k and v are never paged)
 };
 // FP8 main-cache row (K3): 512 E4M3 codes of c, four fp32 scales (blocks of 128), r in bf16
 constexpr int kFp8Codes = 512, kFp8ScaleOff = 512, kFp8ROff = 528, kFp8RowBytes = 656;
@@ -64,6 +79,7 @@ struct DecodeAttnArgs {
   float* lse;       // [B, H] or null
   int row0, rows_per_seq;  // see row_map (latent rows of sequence row_map(..).seq)
   int fp8;          // latent rows are FP8 main-cache rows (kFp8RowBytes each)
+  PageTable pages;  // latent rows of (sequence, position)
 };
 hipError_t launch_decode_attention(Shape s, const DecodeAttnArgs& a, bool gather, hipStream_t st);
 hipError_t launch_absorb_q(Shape s, const uint16_t* q, int ldq, const uint16_t* wkvb, int B,
@@ -88,6 +104,7 @@ struct IndexScoreArgs {
   const float* w_idx;     // [B, 32]
   const uint16_t* idx_k;  // [B, T_cap, 128] bf16, or E4M3 codes when idx_scale is set
   const float* idx_scale; // [B, T_cap] FP8 key scales, or null
+  PageTable pages;        // rows of idx_k / idx_scale
   const int32_t* n_vis;   // [B], plus vis_offset
   int vis_offset;
   int B, T_cap;

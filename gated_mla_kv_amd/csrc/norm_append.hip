@@ -111,12 +111,13 @@ __global__ __launch_bounds__(256) void kv_append_kernel(KvAppendArgs a) {
   const int p = a.pos[b] + t;
   if (p < 0 || p >= a.T_cap) return;  // outside the cache: nothing is written
   const size_t bt = (size_t)b * a.T + t;
+  const size_t crow = cache_row(a.pages, a.T_cap, b, p);  // latent / index-key row
   const int cL = a.L / 8, cS = a.DS / 8, cN = a.DN / 8, cV = a.DV / 8, cI = a.DI / 8;
   // latent
   if (a.latent && a.latent_fp8) {  // K3 only (L = 512, DS = 64): wave 0, lane l codes c[8l .. 8l+7]
     if (threadIdx.x < 64) {
       const int l = threadIdx.x;
-      uint8_t* row = (uint8_t*)a.latent + ((size_t)b * a.T_cap + p) * kFp8RowBytes;
+      uint8_t* row = (uint8_t*)a.latent + crow * kFp8RowBytes;
       float scale;
       const u32x2 codes = fp8_group<16>(ld16(a.c + bt * a.ld_c + l * 8), scale);
       *(u32x2*)(row + l * 8) = codes;
@@ -124,7 +125,7 @@ __global__ __launch_bounds__(256) void kv_append_kernel(KvAppendArgs a) {
       if (l < 8) st16(row + kFp8ROff + l * 16, ld16(a.r + bt * a.ld_r + l * 8));
     }
   } else if (a.latent) {
-    uint16_t* dst = a.latent + ((size_t)b * a.T_cap + p) * (a.L + a.DS);
+    uint16_t* dst = a.latent + crow * (a.L + a.DS);
     for (int i = threadIdx.x; i < cL + cS; i += blockDim.x) {
       const uint16_t* src = (i < cL) ? a.c + bt * a.ld_c + i * 8 : a.r + bt * a.ld_r + (i - cL) * 8;
       st16(dst + i * 8, ld16(src));
@@ -153,12 +154,12 @@ __global__ __launch_bounds__(256) void kv_append_kernel(KvAppendArgs a) {
       const int l = threadIdx.x - 64;
       float scale;
       const u32x2 codes = fp8_group<16>(ld16(a.idx_new + bt * a.ld_idx + l * 8), scale);
-      *(u32x2*)((uint8_t*)a.idx + ((size_t)b * a.T_cap + p) * a.DI + l * 8) = codes;
-      if (l == 0) a.idx_scale[(size_t)b * a.T_cap + p] = scale;
+      *(u32x2*)((uint8_t*)a.idx + crow * a.DI + l * 8) = codes;
+      if (l == 0) a.idx_scale[crow] = scale;
     }
   } else if (a.idx) {
     for (int i = threadIdx.x; i < cI; i += blockDim.x)
-      st16(a.idx + ((size_t)b * a.T_cap + p) * a.DI + i * 8, ld16(a.idx_new + bt * a.ld_idx + i * 8));
+      st16(a.idx + crow * a.DI + i * 8, ld16(a.idx_new + bt * a.ld_idx + i * 8));
   }
 }
 

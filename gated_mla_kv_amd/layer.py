@@ -37,8 +37,9 @@ class LayerBuffers:
         self.cw = MlaWeights(*[self.w[n].data_ptr() if n in self.w else None for n in _WEIGHT_NAMES])
 
     def new_cache(self, B: int, T_cap: int, expanded: bool = True, index: bool = False, fp8_latent: bool = False,
-                  fp8_index: bool = False):
-        return CacheBuffers(self.shape, B, T_cap, expanded, index, self.device, fp8_latent, fp8_index)
+                  fp8_index: bool = False, page_size: int = 0, n_pages: int = 0, block_table=None):
+        return CacheBuffers(self.shape, B, T_cap, expanded, index, self.device, fp8_latent, fp8_index, page_size,
+                            n_pages, block_table)
 
     def workspace(self, B, T_new, max_len, path=PATH_ABSORBED, num_splits=0):
         n = workspace_bytes(self.dims, B, T_new, max_len, path, num_splits)
@@ -81,27 +82,40 @@ class CacheBuffers:
 
     FP8 formats: ``latent`` is [B, T_cap, 656] uint8 rows (512 E4M3 codes, four fp32 scales,
     64 bf16 shared-key values); ``idx`` is one uint8 buffer holding the [B, T_cap, 128] codes and
-    then the [B, T_cap] fp32 scales, viewed as ``idx_codes`` and ``idx_scales``."""
+    then the [B, T_cap] fp32 scales, viewed as ``idx_codes`` and ``idx_scales``.
 
-    def __init__(self, d, B, T_cap, expanded=True, index=False, device="cuda", fp8_latent=False, fp8_index=False):
+    Paged (``page_size`` > 0): latent and idx are pools of ``n_pages`` pages of ``page_size``
+    rows ([n_pages, page_size, ...] in place of [B, T_cap, ...]) and ``block_table`` [B, T_cap /
+    page_size] int32 maps each sequence's blocks to pages; the expanded cache is not kept."""
+
+    def __init__(self, d, B, T_cap, expanded=True, index=False, device="cuda", fp8_latent=False, fp8_index=False,
+                 page_size=0, n_pages=0, block_table=None):
         bf = torch.bfloat16
+        paged = page_size > 0
+        R0, R1 = (n_pages, page_size) if paged else (B, T_cap)   # rows of the latent / index arrays
         if fp8_latent:
-            self.latent = torch.zeros((B, T_cap, FP8_LATENT_ROW_BYTES), dtype=torch.uint8, device=device)
+            self.latent = torch.zeros((R0, R1, FP8_LATENT_ROW_BYTES), dtype=torch.uint8, device=device)
         else:
-            self.latent = torch.zeros((B, T_cap, d.kv_lora + d.d_shared), dtype=bf, device=device)
+            self.latent = torch.zeros((R0, R1, d.kv_lora + d.d_shared), dtype=bf, device=device)
+        expanded = expanded and not paged
         self.k = torch.zeros((B, d.n_heads, T_cap, d.d_nope + d.d_shared), dtype=bf, device=device) if expanded else None
         self.v = torch.zeros((B, d.n_heads, T_cap, d.d_v), dtype=bf, device=device) if expanded else None
         self.idx = self.idx_codes = self.idx_scales = None
         if index and fp8_index:
-            self.idx = torch.zeros(B * T_cap * (d.d_idx + 4), dtype=torch.uint8, device=device)
-            self.idx_codes = self.idx[:B * T_cap * d.d_idx].view(B, T_cap, d.d_idx)
-            self.idx_scales = self.idx[B * T_cap * d.d_idx:].view(torch.float32).view(B, T_cap)
+            self.idx = torch.zeros(R0 * R1 * (d.d_idx + 4), dtype=torch.uint8, device=device)
+            self.idx_codes = self.idx[:R0 * R1 * d.d_idx].view(R0, R1, d.d_idx)
+            self.idx_scales = self.idx[R0 * R1 * d.d_idx:].view(torch.float32).view(R0, R1)
         elif index:
-            self.idx = torch.zeros((B, T_cap, d.d_idx), dtype=bf, device=device)
+            self.idx = torch.zeros((R0, R1, d.d_idx), dtype=bf, device=device)
+        self.block_table = None
+        if paged:
+            self.block_table = torch.as_tensor(block_table, dtype=torch.int32).to(device).contiguous()
+            assert self.block_table.shape == (B, T_cap // page_size)
         self.B, self.T_cap = B, T_cap
         p = lambda t: t.data_ptr() if t is not None else None  # noqa: E731
         self.c = MlaCache(p(self.latent), p(self.k), p(self.v), p(self.idx), B, T_cap,
-                          CACHE_FP8 if fp8_latent else CACHE_BF16, CACHE_FP8 if fp8_index else CACHE_BF16)
+                          CACHE_FP8 if fp8_latent else CACHE_BF16, CACHE_FP8 if fp8_index else CACHE_BF16,
+                          p(self.block_table), page_size, T_cap // page_size if paged else 0, n_pages)
 
     def struct(self) -> MlaCache:
         return self.c

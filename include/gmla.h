@@ -111,6 +111,19 @@ typedef struct mla_cache {
   int32_t T_cap;
   int32_t latent_format; /* MLA_CACHE_BF16 or MLA_CACHE_FP8 */
   int32_t idx_format;    /* MLA_CACHE_BF16 or MLA_CACHE_FP8 */
+  /* Paged latent and index caches ([DSA] pseudocode note: the deployed path maps positions to
+   * pages), or block_table = NULL for the [batch, T_cap] layout above. With a table, latent and
+   * idx_k are pools of n_pages pages of page_size rows each (FP8 index scales: one per pool row,
+   * after the codes), and position p of sequence s is pool row
+   *   block_table[s * max_blocks + p / page_size] * page_size + p % page_size.
+   * page_size must be a multiple of 32 and T_cap = page_size * max_blocks; page indices are
+   * clamped into [0, n_pages) on the device. The expanded k / v are not paged (must be NULL),
+   * and mla_prefill (which attends over them) returns MLA_ERR_UNSUPPORTED. Pages may be shared
+   * between sequences for reading; two sequences appending into one page race. */
+  const int32_t* block_table; /* [batch, max_blocks] device, or NULL */
+  int32_t page_size;
+  int32_t max_blocks;
+  int32_t n_pages;
 } mla_cache;
 
 /* Status name ("MLA_OK", "MLA_ERR_SHAPE", ...). Never NULL. */

@@ -181,3 +181,26 @@ def test_cache_format_validation():
     assert _call_decode(gm.make_dims(TINY), c2) == ERR_UNSUPPORTED
     assert L.dsa_index_topk_fp8(ctypes.byref(gm.make_dims(K3)), FAKE, FAKE, FAKE, None, 10, FAKE, 5, 1, FAKE,
                                 FAKE, None, FAKE, 1 << 30, None) == ERR_NULL
+
+
+def test_paged_cache_validation():
+    """Page tables: page_size a multiple of 32, T_cap = page_size * max_blocks, no expanded
+    cache, K3 shape; dense prefill (expanded attention) refuses them."""
+    L = gm.lib()
+    d = gm.make_dims(K3)
+
+    def paged(page=64, blocks=4, pages=10, k=None, v=None):
+        c = _cache(k=k, v=v, T_cap=page * blocks)
+        c.block_table, c.page_size, c.max_blocks, c.n_pages = FAKE, page, blocks, pages
+        return c
+
+    call = lambda cc, dims=d: L.kv_append(ctypes.byref(dims), ctypes.byref(cc), FAKE, 8, 2, 4,  # noqa: E731
+                                          FAKE, FAKE, None, None, None, None)
+    assert call(paged(page=48, blocks=5)) == ERR_SHAPE
+    c = paged()
+    c.T_cap = 300
+    assert call(c) == ERR_SHAPE
+    assert call(paged(pages=0)) == ERR_SHAPE
+    assert call(paged(k=FAKE, v=FAKE)) == ERR_UNSUPPORTED
+    assert call(paged(), gm.make_dims(TINY)) == ERR_UNSUPPORTED
+    assert _call_prefill(d, paged(k=None, v=None), max_end=50) == ERR_UNSUPPORTED
