@@ -180,6 +180,21 @@ def decode_benches(args, d, lw, log):
     torch.cuda.synchronize()
     out["mla_decode_step_us"] = round(median(time_events(step, it, flush=flush)) * 1e3, 2)
     log(f"[bench] whole mla_decode step (absorbed): {out['mla_decode_step_us']:.1f} us")
+    # the same step captured once in a HIP graph and replayed (no launch gaps between its kernels)
+    gs = torch.cuda.Stream()
+    gs.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(gs):
+        step()
+    torch.cuda.current_stream().wait_stream(gs)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    graph.replay()
+    torch.cuda.synchronize()
+    out["mla_decode_step_graph_us"] = round(median(time_events(graph.replay, it, flush=flush)) * 1e3, 2)
+    log(f"[bench] whole mla_decode step (absorbed), HIP graph replay: {out['mla_decode_step_graph_us']:.1f} us")
+    del graph
     del dc2, wsd
 
     # the same sequences in the FP8 main cache (656 B per position), quantized by kv_append (setup)
@@ -199,6 +214,23 @@ def decode_benches(args, d, lw, log):
                                     "cache (656 B per position)", "kv_bytes": b8, "us": round(t8 * 1e3, 2),
                         "value": r8["achieved"], "unit": "GB/s", "roofline": r8}
     del fcache
+    # the same sequences in a paged cache: 64-position pages, each sequence's pages shuffled over the pool
+    page = 64
+    nbk = -(-nvis // page)
+    table = torch.randperm(B * nbk, generator=torch.Generator().manual_seed(0)).view(B, nbk).to(torch.int32)
+    pcache = L.new_cache(B, nbk * page, expanded=False, page_size=page, n_pages=B * nbk, block_table=table)
+    gm.kv_append(L.dims, pcache.c, zpos, nvis, B, nvis, lat[..., :d.kv_lora].contiguous(),
+                 lat[..., d.kv_lora:].contiguous())
+    decp = lambda: gm.mla_decode_attention(L.dims, qt, pcache.c, n_vis, nvis, B, o, None, 0, dws)  # noqa: E731
+    decp()
+    torch.cuda.synchronize()
+    tp = median(time_events(decp, it, flush=flush))
+    rp = roof_hbm("decode_attn_k3_kernel+decode_merge_kernel (paged)", kv_bytes, tp * 1e3)
+    log(f"[bench] paged-cache absorbed decode attention (64-position pages): {tp * 1e3:.1f} us, {rp['achieved']:.0f} GB/s")
+    out["paged_cache"] = {"workload": "K3 absorbed decode attention, B=32, cache T=8192 (8193 visible), bf16 latent "
+                                      "in 64-position pages, shuffled", "kv_bytes": kv_bytes, "us": round(tp * 1e3, 2),
+                          "value": rp["achieved"], "unit": "GB/s", "roofline": rp}
+    del pcache
 
     # expanded cache for the same sequences, built from the latents by the kv_b projection (setup)
     log("[bench] expanded decode workload: building K/V [32, 96, 8193, 192|128] from the latents")
