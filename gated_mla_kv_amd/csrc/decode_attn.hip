@@ -483,8 +483,11 @@ __global__ __launch_bounds__(256) void vup_gate_k3_kernel(const float* __restric
                                                           void* __restrict__ u, int u_f32) {
   using S = ShapeK3;
   constexpr int H = S::H, DN = S::DN, DV = S::DV, L = S::L;
-  const int h = blockIdx.x;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // 256 threads: the four row groups of head blockIdx.x; 64 threads: row group blockIdx.x % 4 of
+  // head blockIdx.x / 4 (four times the workgroups, for few tokens)
+  const bool one_wave = blockDim.x == 64;
+  const int h = one_wave ? blockIdx.x >> 2 : blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = one_wave ? (blockIdx.x & 3) : (threadIdx.x >> 6);
   const int g2 = lane >> 5, l32 = lane & 31;
   const uint16_t* wrow = wkvb + ((size_t)h * (DN + DV) + DN + wave * 32 + l32) * L + g2 * 8;
   for (int t0 = blockIdx.y * 32; t0 < B; t0 += gridDim.y * 32) {  // token blocks of this workgroup
@@ -633,8 +636,8 @@ hipError_t launch_vup_gate(Shape s, const float* o, const uint16_t* wkvb, const 
   if (B <= 0) return hipSuccess;
   if (s == Shape::K3 && B > 32)  // many tokens: W^V_h staged once per 128 tokens
     vup_gate_k3_lds_kernel<<<dim3(ShapeK3::H, cdiv(B, 128)), 256, 0, st>>>(o, wkvb, g_pre, B, u, u_f32);
-  else if (s == Shape::K3)
-    vup_gate_k3_kernel<<<dim3(ShapeK3::H, cdiv(B, 32)), 256, 0, st>>>(o, wkvb, g_pre, B, u, u_f32);
+  else if (s == Shape::K3)  // one wave per (head, row group): 384 workgroups stream W^V
+    vup_gate_k3_kernel<<<dim3(ShapeK3::H * 4, cdiv(B, 32)), 64, 0, st>>>(o, wkvb, g_pre, B, u, u_f32);
   else
     vup_gate_kernel<ShapeTiny><<<ShapeTiny::H, 256, 0, st>>>(o, wkvb, g_pre, B, u, u_f32);
   return hipGetLastError();
