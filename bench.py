@@ -473,6 +473,29 @@ def counter_pass(log):
         gm.mla_sparse_attention(dims5, qt, c, sel, cnt, B, o, None, 0, ws)
     torch.cuda.synchronize()
     log("[counters] DSA decode done")
+    # FP8 caches (quantized by kv_append first): the DSA step B=8 x 65537, then absorbed decode B=32 x 8193
+    from gated_mla_kv_amd.layer import CacheBuffers
+    f8 = CacheBuffers(dd, B, nv, expanded=False, index=True, fp8_latent=True, fp8_index=True)
+    gm.kv_append(dims5, f8.c, torch.zeros(B, dtype=torch.int32, device=dev), nv, B, nv,
+                 lat[..., :dd.kv_lora].contiguous(), lat[..., dd.kv_lora:].contiguous(), None, None, idx)
+    for _ in range(2):
+        gm.dsa_index_topk_fp8(dims5, qi, wi, f8.idx_codes, f8.idx_scales, nv, n, nv, B, sel, cnt, None, ws)
+        gm.mla_sparse_attention(dims5, qt, f8.c, sel, cnt, B, o, None, 0, ws)
+    torch.cuda.synchronize()
+    del lat, idx, f8, c, o, ws
+    B, nv = 32, 8193
+    lat = device_normal_bf16((B, nv, d.d_latent), 1.0, 9, 14)
+    qt = device_normal_bf16((B, H, d.d_latent), 0.05, 9, 15)
+    f8 = CacheBuffers(d, B, nv, expanded=False, fp8_latent=True)
+    gm.kv_append(dims, f8.c, torch.zeros(B, dtype=torch.int32, device=dev), nv, B, nv,
+                 lat[..., :d.kv_lora].contiguous(), lat[..., d.kv_lora:].contiguous())
+    n = torch.full((B,), nv, dtype=torch.int32, device=dev)
+    o = torch.empty((B, H, d.kv_lora), dtype=torch.float32, device=dev)
+    ws = torch.empty(gm.workspace_bytes(dims, B, 1, nv, gm.PATH_ABSORBED), dtype=torch.uint8, device=dev)
+    for _ in range(2):
+        gm.mla_decode_attention(dims, qt, f8.c, n, nv, B, o, None, 0, ws)
+    torch.cuda.synchronize()
+    log("[counters] FP8 caches done")
 
 
 def main():
