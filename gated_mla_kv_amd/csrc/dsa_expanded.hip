@@ -138,6 +138,113 @@ __global__ __launch_bounds__(kScoreWaves * 64) void index_scores_kernel(IndexSco
   }
 }
 
+// Prefill rows of one sequence see nested prefixes of one index cache, so a workgroup takes 8
+// consecutive rows (one per wave) and a 256-position block of keys, staged once in LDS for all
+// of them (256-byte rows, 16-byte chunk c at c ^ (row & 15); FP8 codes: 128-byte rows, chunk c
+// at c ^ (row & 7), widened when read, and the block's scales). Each wave scores its row's
+// visible positions of the block as index_scores_kernel does; the top digits go to per-row LDS
+// histograms of 16-bit counters (two bins per word: at most 256 per bin), added to the rows'
+// histograms at the end.
+constexpr int kRowsPerWg = 8, kRowBlock = 256;
+
+__global__ __launch_bounds__(kRowsPerWg * 64) void index_scores_rows_kernel(IndexScoreArgs a) {
+  constexpr int NIH = 32, DI = 128, KS = DI / 16;
+  __shared__ __attribute__((aligned(16))) uint8_t keys_s[kRowBlock * DI * 2];
+  __shared__ uint32_t hist2[kRowsPerWg * kHistBins / 2];
+  __shared__ float kscale_s[kRowBlock];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g2 = lane >> 5, l32 = lane & 31;
+  const int p0 = blockIdx.x * kRowBlock;
+  auto visible = [&](int row) __attribute__((always_inline)) {
+    const RowMap rm = row_map(a.row0, a.rows_per_seq, row);
+    return min(min(a.n_vis[rm.seq] + a.vis_offset + rm.extra, a.T_cap), a.score_stride);
+  };
+  const int b = blockIdx.y * kRowsPerWg + wave;  // this wave's row
+  const int b_last = min((int)blockIdx.y * kRowsPerWg + kRowsPerWg, a.B) - 1;
+  const int seq = row_map(a.row0, a.rows_per_seq, b_last).seq;
+  const int t_last = visible(b_last);  // the block's longest row
+  if (p0 >= t_last) return;
+  const int t = b < a.B ? visible(b) : 0;
+  const bool fp8 = a.idx_scale != nullptr;
+  for (int i = tid; i < kRowsPerWg * kHistBins / 2; i += kRowsPerWg * 64) hist2[i] = 0;
+  // the block's keys (positions past t_last repeat its last one; never scored)
+  constexpr int NT = kRowsPerWg * 64;
+  if (!fp8) {
+    u32x4 v[kRowBlock * 16 / NT];
+#pragma unroll
+    for (int k = 0; k < kRowBlock * 16 / NT; ++k) {
+      const int i = k * NT + tid, r = i >> 4, c = i & 15;
+      v[k] = ld16(a.idx_k + cache_row(a.pages, a.T_cap, seq, min(p0 + r, t_last - 1)) * DI + c * 8);
+    }
+#pragma unroll
+    for (int k = 0; k < kRowBlock * 16 / NT; ++k) {
+      const int i = k * NT + tid, r = i >> 4, c = i & 15;
+      st16(keys_s + r * 256 + ((c ^ (r & 15)) << 4), v[k]);
+    }
+  } else {
+    u32x4 v[kRowBlock * 8 / NT];
+#pragma unroll
+    for (int k = 0; k < kRowBlock * 8 / NT; ++k) {
+      const int i = k * NT + tid, r = i >> 3, c = i & 7;
+      v[k] = ld16((const uint8_t*)a.idx_k + cache_row(a.pages, a.T_cap, seq, min(p0 + r, t_last - 1)) * DI + c * 16);
+    }
+#pragma unroll
+    for (int k = 0; k < kRowBlock * 8 / NT; ++k) {
+      const int i = k * NT + tid, r = i >> 3, c = i & 7;
+      st16(keys_s + r * 128 + ((c ^ (r & 7)) << 4), v[k]);
+    }
+    for (int i = tid; i < kRowBlock; i += NT)
+      kscale_s[i] = a.idx_scale[cache_row(a.pages, a.T_cap, seq, min(p0 + i, t_last - 1))];
+  }
+  u32x4 qa[KS];
+  float wgt[16];
+  if (b < a.B) {
+    const uint16_t* qrow = a.q_idx + ((size_t)b * NIH + l32) * DI;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) qa[s] = ld16(qrow + s * 16 + g2 * 8);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) wgt[r] = a.w_idx[(size_t)b * NIH + (r >> 2) * 8 + g2 * 4 + (r & 3)] * a.scale;
+  }
+  __syncthreads();  // keys staged, histograms cleared
+  for (int j = 0; j < kRowBlock / 32 && p0 + 32 * j < t; ++j) {
+    const int r = 32 * j + l32;  // key row of this lane
+    f32x16 acc = f32x16{};
+    if (fp8) {
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const u32x2 w = ld8(keys_s + r * 128 + ((s ^ (r & 7)) << 4) + g2 * 8);
+        const u32x2 lo = e4m3x4_to_bf16(w.x), hi = e4m3x4_to_bf16(w.y);
+        acc = mfma32(qa[s], u32x4{lo.x, lo.y, hi.x, hi.y}, acc);
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+        acc = mfma32(qa[s], ld16(keys_s + r * 256 + (((2 * s + g2) ^ (r & 15)) << 4)), acc);
+    }
+    float sc = 0.f;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) sc += wgt[q] * fmaxf(acc[q], 0.f);
+    sc += __shfl_xor(sc, 32, 64);
+    if (fp8) sc *= kscale_s[r];
+    const int pos = p0 + r;
+    if (pos < t && g2 == 0) {
+      a.scores[(size_t)b * a.score_stride + pos] = sc;
+      const uint32_t bin = order_key(sc) >> 20;
+      atomicAdd(&hist2[wave * (kHistBins / 2) + (bin >> 1)], (bin & 1) ? 65536u : 1u);
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < kRowsPerWg * kHistBins / 2; i += NT) {
+    const uint32_t w = hist2[i];
+    const int row = blockIdx.y * kRowsPerWg + i / (kHistBins / 2), bin = 2 * (i % (kHistBins / 2));
+    if (w && row < a.B) {
+      int* gh = a.hist + (size_t)row * kHistBins + bin;
+      if (w & 0xFFFFu) atomicAdd(gh, (int)(w & 0xFFFFu));
+      if (w >> 16) atomicAdd(gh + 1, (int)(w >> 16));
+    }
+  }
+}
+
 __global__ void zero_words_kernel(int32_t* p, int n) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = 0;
@@ -831,7 +938,11 @@ hipError_t launch_index_topk(IndexScoreArgs sa, int max_visible, TopkArgs ta, in
   ta.off_stride = S;
   const int nz = B * kHistBins;
   zero_words_kernel<<<cdiv(nz, 256), 256, 0, st>>>(scratch, nz);
-  if (max_visible > 0)
+  // rows of one sequence (a prefill's tokens) share each key block among eight rows
+  const bool one_seq = sa.rows_per_seq > 1 && sa.row0 / sa.rows_per_seq == (sa.row0 + B - 1) / sa.rows_per_seq;
+  if (max_visible > 0 && one_seq)
+    index_scores_rows_kernel<<<dim3(cdiv(max_visible, kRowBlock), cdiv(B, kRowsPerWg)), kRowsPerWg * 64, 0, st>>>(sa);
+  else if (max_visible > 0)
     index_scores_kernel<<<dim3(cdiv(max_visible, kScoreChunk), B), kScoreWaves * 64, 0, st>>>(sa);
   topk_count_kernel<<<dim3(S, B), 256, 0, st>>>(ta);
   topk_select_kernel<<<B, kTopkThreads, 0, st>>>(ta);

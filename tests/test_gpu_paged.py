@@ -105,12 +105,14 @@ def test_paged_dsa_decode_step(fp8):
     assert torch.equal(got[:, :T + 1], flat.latent[:, :T + 1])
 
 
-def test_paged_dsa_prefill():
+@pytest.mark.parametrize("B", [1, 2])
+def test_paged_dsa_prefill(B):
+    """B = 1 takes the row-blocked index-score kernel (rows of one sequence), B = 2 the per-row one."""
     from gated_mla_kv_amd.layer import LayerBuffers
     d = K3_SMALL_TOPK
     lw = make_layer_weights(d, seed=190, dist="k3", perturb_norms=True)
     L = LayerBuffers(d, lw.w)
-    B, P, T, T_cap, page = 2, 40, 100, 160, 32
+    P, T, T_cap, page = 40, 300, 352, 32
     paged, flat, table = _caches(d, B, T_cap, page, 4, 191, index=True)
     _append(d, (paged, flat), make_latent_prefix(d, B, P, seed=191), make_index_prefix(d, B, P, seed=191))
     x = dev_bf16(make_tokens(d, B, T, seed=191))
