@@ -161,7 +161,7 @@ def decode_benches(args, d, lw, log):
     t_cold = median(time_events(dec, it, flush=flush))
     t_hot = median(time_events(dec, it))
     kv_bytes = B * nvis * d.d_latent * 2
-    r = roof_hbm("decode_attn_k3_kernel+decode_merge_kernel", kv_bytes, t_cold * 1e3, "decode:B32_T8192")
+    r = roof_hbm("decode_attn_k3_kernel<false, false>+decode_merge_kernel", kv_bytes, t_cold * 1e3, "decode:B32_T8192")
     log(f"[bench] absorbed decode attention: {t_cold * 1e3:.1f} us cold, {t_hot * 1e3:.1f} us hot, "
         f"{r['achieved']:.0f} GB/s")
     out.update({"workload": "K3 absorbed decode attention, B=32, cache T=8192 (8193 visible), bf16 latent",
@@ -207,7 +207,7 @@ def decode_benches(args, d, lw, log):
     torch.cuda.synchronize()
     t8 = median(time_events(dec8, it, flush=flush))
     b8 = B * nvis * gm.FP8_LATENT_ROW_BYTES
-    r8 = roof_hbm("decode_attn_k3_kernel<fp8>+decode_merge_kernel", b8, t8 * 1e3, "decode_fp8:B32_T8192")
+    r8 = roof_hbm("decode_attn_k3_kernel<false, true>+decode_merge_kernel", b8, t8 * 1e3, "decode_fp8:B32_T8192")
     log(f"[bench] FP8-cache absorbed decode attention: {t8 * 1e3:.1f} us, {r8['achieved']:.0f} GB/s "
         f"({kv_bytes / (t8 * 1e-3) / 1e9:.0f} GB/s of bf16-cache bytes)")
     out["fp8_cache"] = {"workload": "K3 absorbed decode attention, B=32, cache T=8192 (8193 visible), FP8 latent "
@@ -319,7 +319,7 @@ def decode_benches(args, d, lw, log):
     t_dsa = median(time_events(dsa_fn, it, flush=flush))
     b_idx = B5 * nv5 * dd.d_idx * 2
     b_sel = B5 * dd.topk * dd.d_latent * 2
-    r5 = roof_hbm("index_scores_kernel+topk_count_kernel+topk_select_kernel+topk_compact_kernel+decode_attn_k3_kernel<gather>+decode_merge_kernel",
+    r5 = roof_hbm("index_scores_kernel+topk_count_kernel+topk_select_kernel+topk_compact_kernel+decode_attn_k3_kernel<true, false>+decode_merge_kernel",
                   b_idx + b_sel, t_dsa * 1e3, "dsa:B8_T65536")
     log(f"[bench] DSA decode: index+top-k {t_topk * 1e3:.1f} us, sparse {t_sparse * 1e3:.1f} us, "
         f"together {t_dsa * 1e3:.1f} us, {r5['achieved']:.0f} GB/s")
@@ -347,7 +347,7 @@ def decode_benches(args, d, lw, log):
     t8 = median(time_events(dsa8_fn, it, flush=flush))
     t8_topk = median(time_events(topk8, it, flush=flush))
     b8 = B5 * nv5 * (dd.d_idx + 4) + B5 * dd.topk * gm.FP8_LATENT_ROW_BYTES
-    r8 = roof_hbm("index_scores_kernel<fp8>+topk kernels+decode_attn_k3_kernel<gather,fp8>+decode_merge_kernel",
+    r8 = roof_hbm("index_scores_kernel (FP8 keys)+topk_count_kernel+topk_select_kernel+topk_compact_kernel+decode_attn_k3_kernel<true, true>+decode_merge_kernel",
                   b8, t8 * 1e3, "dsa_fp8:B8_T65536")
     log(f"[bench] FP8-cache DSA decode: index+top-k {t8_topk * 1e3:.1f} us, together {t8 * 1e3:.1f} us, "
         f"{r8['achieved']:.0f} GB/s")

@@ -333,3 +333,31 @@ def test_dsa_fp8_B8_T65536():
         o_ref, l_ref = O.attention_absorbed_subset(f64t(qt[b]), oc.latent[0], got, O.softmax_scale(D), D)
         check_rows(to_np(o[b]), o_ref, f"fp8 sparse o b={b}")
         check_scores(to_np(lse[b]), l_ref, f"fp8 sparse lse b={b}")
+
+
+def test_paged_decode_B32_T8192_equals_contiguous():
+    """The bench's paged layout (64-position pages shuffled over the pool) at full size: the
+    absorbed decode over it equals the contiguous cache's bit for bit, and the contiguous
+    result is the one checked against the oracle above."""
+    from gated_mla_kv_amd.layer import CacheBuffers
+    B, nvis, page = 32, 8193, 64
+    print("paged decode B=32 n_vis=8193", flush=True)
+    lat = device_normal_bf16((B, nvis, D.d_latent), 1.0, 10, 1)
+    qt = device_normal_bf16((B, H, D.d_latent), 0.05, 10, 2)
+    dims = gm.make_dims(DD)
+    nb = -(-nvis // page)
+    table = torch.randperm(B * nb, generator=torch.Generator().manual_seed(10)).view(B, nb).to(torch.int32)
+    paged = CacheBuffers(DD, B, nb * page, expanded=False, page_size=page, n_pages=B * nb, block_table=table)
+    gm.kv_append(dims, paged.c, torch.zeros(B, dtype=torch.int32, device="cuda"), nvis, B, nvis,
+                 lat[..., :D.kv_lora].contiguous(), lat[..., D.kv_lora:].contiguous())
+    flat = gm.MlaCache(lat.data_ptr(), None, None, None, B, nvis)
+    n = torch.full((B,), nvis, dtype=torch.int32, device="cuda")
+    ws = torch.empty(gm.workspace_bytes(dims, B, 1, nvis, gm.PATH_ABSORBED), dtype=torch.uint8, device="cuda")
+    outs = []
+    for c in (paged.c, flat):
+        o = torch.empty((B, H, D.kv_lora), dtype=torch.float32, device="cuda")
+        lse = torch.empty((B, H), dtype=torch.float32, device="cuda")
+        gm.mla_decode_attention(dims, qt, c, n, nvis, B, o, lse, 0, ws)
+        torch.cuda.synchronize()
+        outs.append((o, lse))
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
