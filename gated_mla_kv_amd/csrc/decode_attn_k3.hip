@@ -318,19 +318,30 @@ __global__ __launch_bounds__(k3dec::NTHREADS) void decode_attn_k3_kernel(DecodeA
           lds_dma16_sbase(doff[k] & 0xFFFFu, base, slot_addr + (pw * NLOAD_W + k) * 1024);
         return;
       }
-      // gathered (or tail) rows: all nine source rows first (one LDS read each, waited for
-      // together), then the nine loads; rows past the end repeat a valid row (masked)
-      const int row0 = GATHER ? 0 : crow(p0 + j0);
-      int rows[NLOAD_W];
+      // rows past the end repeat a valid row (masked)
+      if constexpr (GATHER) {
+        // gathered rows: all nine source rows are read from LDS together, then the nine loads
+        // (faster than three at a time although it spills a few registers)
+        int rows[NLOAD_W];
 #pragma unroll
-      for (int k = 0; k < NLOAD_W; ++k) {
-        const int jr = min(j0 + (int)(doff[k] >> 16), n_pos - 1);
-        rows[k] = GATHER ? sel_s[jr] : row0 + (jr - j0);
-      }
+        for (int k = 0; k < NLOAD_W; ++k) rows[k] = sel_s[min(j0 + (int)(doff[k] >> 16), n_pos - 1)];
 #pragma unroll
-      for (int k = 0; k < NLOAD_W; ++k) {
-        const uint32_t coff = (doff[k] & 0xFFFFu) - (doff[k] >> 16) * (DL * 2);  // the chunk's byte offset
-        lds_dma16((const char*)lat + (size_t)rows[k] * (DL * 2) + coff, slot_addr + (pw * NLOAD_W + k) * 1024);
+        for (int k = 0; k < NLOAD_W; ++k) {
+          const uint32_t coff = (doff[k] & 0xFFFFu) - (doff[k] >> 16) * (DL * 2);  // the chunk's byte offset
+          lds_dma16((const char*)lat + (size_t)rows[k] * (DL * 2) + coff, slot_addr + (pw * NLOAD_W + k) * 1024);
+        }
+      } else {
+        // the partial last tile of a split: consecutive rows (a rolled loop keeps the P.V waves'
+        // registers free)
+        const int row0 = crow(p0 + j0);
+#pragma unroll 1
+        for (int k = 0; k < NLOAD_W; ++k) {
+          const int i = pw * NLOAD_W + k;
+          const int P = i * 64 + lane;  // destination chunk of this lane
+          const int r = P / CH, c = (P - r * CH) ^ swz_row(r);
+          const int jr = min(j0 + r, n_pos - 1);
+          lds_dma16(lat + (size_t)(row0 + (jr - j0)) * DL + c * 8, slot_addr + i * 1024);
+        }
       }
     };
     // tiles issued so far are [0, issued); wait until tile `need` has landed
