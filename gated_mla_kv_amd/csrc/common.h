@@ -72,6 +72,16 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const void* p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
+// LDS transpose read of bytes (ds_read_b64_tr_b8). Within each group of 16 lanes, lane j points
+// at &tile[k0 + (j>>1)][n0 + 8*(j&1)] of a row-major byte tile; lane i then holds
+// tile[k0 + r][n0 + i] in byte r, r = 0..7 (eight rows of one column).
+// Takes the LDS byte address (as from lds_addr).
+__device__ __forceinline__ u32x2 lds_read_tr8(uint32_t lds_byte_addr) {
+  typedef int i32x2_t __attribute__((ext_vector_type(2)));
+  i32x2_t v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((GMLA_LDS i32x2_t*)(uintptr_t)lds_byte_addr);
+  return __builtin_bit_cast(u32x2, v);
+}
+
 // One wave-wide global_load_lds_dwordx4: lane L's 16 bytes from `gsrc` land in LDS at
 // lds_byte_addr + 16*L (which must be the same in every lane). Issued from inline asm so that the compiler does not place a blanket
 // vmcnt(0) wait in front of every later LDS read (it cannot tell LDS-DMA destinations apart);

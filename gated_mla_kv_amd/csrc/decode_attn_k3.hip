@@ -23,12 +23,15 @@
 //   max stays and the rescale factor is exactly 1, so the accumulators are rarely rescaled.
 //   The result is the same softmax; only the reference point of the exponentials differs.
 // * FP8 main cache (K3.1 Gated DSA blog, cache section: 512 E4M3 codes, four fp32 block scales
-//   and r in bf16 per 656-byte row): all seven waves DMA the raw rows (3 of a tile's 21
-//   wave-wide loads each) into a 3-slot ring; after each step's barrier they convert the tile
-//   two ahead into the bf16 tile layout above (decode(code) * scale: the scales are powers of
-//   two, so one v_cvt_scalef32_pk_bf16_fp8 per two values, exact; r copied), into the slot the
-//   P.V waves just released, then a second barrier. The MFMA code is the same; two bf16 slots
-//   instead of four.
+//   and r in bf16 per 656-byte row): P.V waves 3-5 DMA the raw rows (7 of a tile's 21
+//   wave-wide loads each) into a 6-slot ring of raw tiles (rows at a 656-byte pitch), five tiles
+//   ahead, and the MFMA operands are formed from the raw tile in registers, one barrier per tile
+//   as above. Score waves read 8 codes of their row and decode them with the row's block scale
+//   (v_cvt_scalef32_pk_bf16_fp8: the scales are powers of two, so the bf16 value is exactly
+//   decode(code) * scale); r is read as bf16. P.V waves read 8 positions of one feature with
+//   ds_read_b64_tr_b8, decode them unscaled, and multiply the P^T entries of those positions by
+//   the positions' scales for the wave's 128-feature block (a power of two again, so
+//   bf16(p) * scale is exact and every product equals the bf16 path's).
 // * Each split writes its output divided by its own softmax sum, in fp16: a convex combination
 //   of cached rows, so bounded by the largest latent entry, at half the bytes of fp32 partials
 //   (11-bit significand; the merge weights them by 2^(m - M) * l in fp32).
@@ -51,6 +54,8 @@ constexpr int MAX_SEL = 2048;                 // gathered positions per split (<
 constexpr float RESCALE_SLACK = 8.0f;         // base-2 growth of the max before rescaling
 constexpr int F8CH = kFp8RowBytes / 16;       // 41 chunks of 16 bytes per FP8 row
 constexpr int F8SLOT = 21 * 1024;             // 32 rows (20,992 bytes) and the 21st load's spill
+constexpr int NS8 = 6;                        // raw FP8 tiles in the ring
+constexpr int NL8 = 7;                        // 1 KB loads per tile issued by each of waves 3-5
 }  // namespace k3dec
 
 __device__ __forceinline__ int swz_row(int r) { return ((r ^ (r >> 2)) & 1) | (r & 2) | ((r >> 1) & 4); }
@@ -58,6 +63,27 @@ __device__ __forceinline__ int swz_row(int r) { return ((r ^ (r >> 2)) & 1) | (r
 __device__ __forceinline__ int perm_row_k3(int m) {
   const int a = m >> 3, g = (m >> 2) & 1, b = m & 3;
   return 16 * (a >> 1) + 8 * g + 4 * (a & 1) + b;
+}
+
+// two E4M3 codes (bytes 2*HI, 2*HI + 1 of w) -> packed bf16 pair, times 2^exponent(sc)
+template <bool HI>
+__device__ __forceinline__ uint32_t cvt_fp8x2(uint32_t w, float sc) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, sc, HI));
+}
+__device__ __forceinline__ u32x4 cvt_fp8x8(u32x2 c, float sc) {
+  return u32x4{cvt_fp8x2<false>(c.x, sc), cvt_fp8x2<true>(c.x, sc), cvt_fp8x2<false>(c.y, sc),
+               cvt_fp8x2<true>(c.y, sc)};
+}
+// eight bf16 values (k = 0..7 of an MFMA operand) times per-k powers of two: exact
+__device__ __forceinline__ u32x4 scale_bf16x8(u32x4 w, const float* s) {
+  uint32_t x[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float lo = __builtin_bit_cast(float, x[q] << 16) * s[2 * q];
+    const float hi = __builtin_bit_cast(float, x[q] & 0xFFFF0000u) * s[2 * q + 1];
+    x[q] = (__builtin_bit_cast(uint32_t, hi) & 0xFFFF0000u) | (__builtin_bit_cast(uint32_t, lo) >> 16);
+  }
+  return u32x4{x[0], x[1], x[2], x[3]};
 }
 
 // vmcnt wait leaving at most `tiles` of this wave's most recent tile loads (9 each) in flight.
@@ -73,9 +99,9 @@ __device__ __forceinline__ void wait_tiles_in_flight(int tiles) {
 template <bool GATHER, bool FP8>
 __global__ __launch_bounds__(k3dec::NTHREADS) void decode_attn_k3_kernel(DecodeAttnArgs a) {
   using namespace k3dec;
-  constexpr int NSLOT = FP8 ? 2 : (GATHER ? 3 : 4);
-  __shared__ __attribute__((aligned(1024))) uint8_t lat_s[NSLOT][TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t f8_s[FP8 ? 3 : 1][FP8 ? F8SLOT : 16];
+  constexpr int NSLOT = GATHER ? 3 : 4;  // bf16 tiles in the ring
+  __shared__ __attribute__((aligned(1024))) uint8_t lat_s[FP8 ? 1 : NSLOT][FP8 ? 16 : TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t f8_s[FP8 ? NS8 : 1][FP8 ? F8SLOT : 16];
   __shared__ __attribute__((aligned(16))) uint16_t Ps[2][H * PROW];
   __shared__ float alpha_s[2][H];
   __shared__ int sel_s[GATHER ? MAX_SEL : 1];
@@ -112,82 +138,6 @@ __global__ __launch_bounds__(k3dec::NTHREADS) void decode_attn_k3_kernel(DecodeA
   const float sl2 = a.scale * 1.4426950408889634f;
   const size_t part = (size_t)b * a.n_splits + split;
 
-  // ---- FP8 rows: issue, wait and convert, run by all seven waves with the same barriers ----
-  const uint8_t* lat8 = (const uint8_t*)a.latent + seq_rows * kFp8RowBytes;
-  int issued8 = 0;
-  auto issue8 = [&]() {  // the next tile's raw rows: loads 3 w .. 3 w + 2 of its 21
-    if (!FP8 || issued8 >= n_tiles) return;
-    const int t = issued8++;
-    const uint32_t fs = lds_addr(f8_s[t % 3]);
-    const int j0 = t * BT;
-    const int row0 = GATHER ? 0 : crow(p0 + j0);  // a tile lies in one page
-#pragma unroll
-    for (int k = 0; k < 3; ++k) {
-      const int i = wave * 3 + k;
-      const int P = min(i * 64 + lane, BT * F8CH - 1);  // the last load's upper half repeats a chunk
-      const int r = P / F8CH, c = P - r * F8CH;
-      const int jr = min(j0 + r, n_pos - 1);  // rows past the end repeat a valid row (masked)
-      const int row = GATHER ? sel_s[jr] : row0 + (jr - j0);
-      lds_dma16(lat8 + (size_t)row * kFp8RowBytes + c * 16, fs + i * 1024);
-    }
-  };
-  auto wait8 = [&](int need) {  // this wave's loads of tile `need` have landed
-    const int after = issued8 - 1 - need;
-    if (after >= 2)
-      asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
-    else if (after == 1)
-      asm volatile("s_waitcnt vmcnt(3)" ::: "memory");
-    else
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  };
-  auto convert8 = [&](int t) {  // raw tile t -> bf16 tile layout in lat_s[t % 2]
-    if (!FP8 || t >= n_tiles) return;
-    const uint8_t* fsrc = f8_s[t % 3];
-    uint8_t* dst = lat_s[t % NSLOT];
-    for (int u = tid; u < BT * 40; u += NTHREADS) {
-      if (u < BT * 32) {  // 16 codes of row r: latent features 16 j .. 16 j + 15
-        const int r = u >> 5, j = u & 31;
-        const u32x4 w = *(const u32x4*)(fsrc + r * kFp8RowBytes + j * 16);
-        const float sc = *(const float*)(fsrc + r * kFp8RowBytes + kFp8ScaleOff + (j >> 3) * 4);
-        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-        uint32_t o[8];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          o[2 * q] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)ws[q], sc, false));
-          o[2 * q + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)ws[q], sc, true));
-        }
-        const int sw = swz_row(r);
-        st16(dst + (r * CH + ((2 * j) ^ sw)) * 16, u32x4{o[0], o[1], o[2], o[3]});
-        st16(dst + (r * CH + ((2 * j + 1) ^ sw)) * 16, u32x4{o[4], o[5], o[6], o[7]});
-      } else {  // r: 8 chunks of bf16 copied
-        const int v = u - BT * 32, r = v >> 3, k = v & 7;
-        st16(dst + (r * CH + ((L / 8 + k) ^ swz_row(r))) * 16,
-             *(const u32x4*)(fsrc + r * kFp8RowBytes + kFp8ROff + k * 16));
-      }
-    }
-  };
-  // before the first step: tiles 0, 1 converted (and 2, 3 issued), with three barriers
-  auto prologue8 = [&]() {
-    issue8();
-    issue8();
-    issue8();
-    wait8(0);
-    __syncthreads();
-    convert8(0);
-    wait8(1);
-    __syncthreads();
-    issue8();  // tile 3, into the slot tile 0 used
-    convert8(1);
-    __syncthreads();
-  };
-  // after step t's barrier (each wave waited for its loads of tile t + 2 before it): tile t + 4
-  // issued, tile t + 2 converted into the slot tile t used
-  auto step8 = [&](int t) {
-    issue8();
-    convert8(t + 2);
-    __syncthreads();
-  };
-
   // The two roles run separate code with the same barriers, so that the score waves' q~
   // registers and the P.V waves' accumulators are never live at the same point.
   if (wave < 3) {
@@ -211,26 +161,62 @@ __global__ __launch_bounds__(k3dec::NTHREADS) void decode_attn_k3_kernel(DecodeA
     uint32_t aoff[4];
 #pragma unroll
     for (int m = 0; m < 4; ++m) aoff[m] = lds_addr(lat_s[0]) + srow_base + (((2 * m + g2) ^ srow_swz) << 4);
+    const uint32_t f8_row = lds_addr(f8_s[0]) + srow * kFp8RowBytes + 8 * g2;  // FP8: this lane's codes
     auto score_tile = [&](int t) {
-      const uint32_t so = (t % NSLOT) * TILE_BYTES;
-      uint32_t ab[4];
-#pragma unroll
-      for (int m = 0; m < 4; ++m) ab[m] = aoff[m] + so;
-      auto lat_row = [&](int s) __attribute__((always_inline)) {
-        return *(GMLA_LDS const u32x4*)(ab[s & 3] + 128 * (s >> 2));
-      };
-      constexpr int PF = GATHER ? 6 : 8;  // LDS reads run PF k-steps ahead of their MFMA
-      u32x4 ar[PF];
-#pragma unroll
-      for (int s = 0; s < PF; ++s) ar[s] = lat_row(s);
-      // two accumulator chains (even and odd k-steps) so that consecutive MFMAs are independent
       f32x16 sacc2[2] = {f32x16{}, f32x16{}};
+      if constexpr (FP8) {
+        // the row's 512 codes decoded with its block scales, 8 per lane and k-step; r as bf16
+        // one address register per tile; the k-steps are immediate offsets from it (the empty asm
+        // keeps the compiler from hoisting one loop-invariant address per k-step instead)
+        uint32_t fr = f8_row + (t % NS8) * F8SLOT;
+        asm volatile("" : "+v"(fr));
+        const f32x4 sc4 = *(GMLA_LDS const f32x4*)(fr - 8 * g2 + kFp8ScaleOff);
+        auto raw = [&](int s) __attribute__((always_inline)) {
+          return *(GMLA_LDS const u32x2*)(fr + 16 * s);
+        };
+        auto rpart = [&](int s) __attribute__((always_inline)) {
+          return *(GMLA_LDS const u32x4*)(fr + 8 * g2 + kFp8ROff + 32 * s);
+        };
+        constexpr int PF8 = 8;  // LDS reads run PF8 k-steps ahead of their MFMA
+        u32x2 cr[PF8];
+        u32x4 rr[KSD - L / 16];
 #pragma unroll
-      for (int s = 0; s < KSD; ++s) {
-        const u32x4 cur = ar[s % PF];
-        if (s + PF < KSD) ar[s % PF] = lat_row(s + PF);
-        __builtin_amdgcn_sched_barrier(0);
-        sacc2[s & 1] = mfma32(cur, qf[s], sacc2[s & 1]);
+        for (int s = 0; s < PF8; ++s) cr[s] = raw(s);
+#pragma unroll
+        for (int s = 0; s < KSD; ++s) {
+          u32x4 cur;
+          if (s < L / 16) {
+            cur = cvt_fp8x8(cr[s % PF8], sc4[s >> 3]);
+            if (s + PF8 < L / 16)
+              cr[s % PF8] = raw(s + PF8);
+            else if (s + PF8 < KSD)
+              rr[s + PF8 - L / 16] = rpart(s + PF8 - L / 16);
+          } else {
+            cur = rr[s - L / 16];
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          sacc2[s & 1] = mfma32(cur, qf[s], sacc2[s & 1]);
+        }
+      } else {
+        const uint32_t so = (t % NSLOT) * TILE_BYTES;
+        uint32_t ab[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) ab[m] = aoff[m] + so;
+        auto lat_row = [&](int s) __attribute__((always_inline)) {
+          return *(GMLA_LDS const u32x4*)(ab[s & 3] + 128 * (s >> 2));
+        };
+        constexpr int PF = GATHER ? 6 : 8;  // LDS reads run PF k-steps ahead of their MFMA
+        u32x4 ar[PF];
+#pragma unroll
+        for (int s = 0; s < PF; ++s) ar[s] = lat_row(s);
+        // two accumulator chains (even and odd k-steps) so that consecutive MFMAs are independent
+#pragma unroll
+        for (int s = 0; s < KSD; ++s) {
+          const u32x4 cur = ar[s % PF];
+          if (s + PF < KSD) ar[s % PF] = lat_row(s + PF);
+          __builtin_amdgcn_sched_barrier(0);
+          sacc2[s & 1] = mfma32(cur, qf[s], sacc2[s & 1]);
+        }
       }
       f32x16 sacc = sacc2[0] + sacc2[1];
       const int jbase = t * BT;
@@ -265,25 +251,12 @@ __global__ __launch_bounds__(k3dec::NTHREADS) void decode_attn_k3_kernel(DecodeA
       if (g2 == 0) alpha_s[t & 1][head] = alpha;
     };
 
-    if constexpr (FP8) {
-      prologue8();
-      if (n_tiles > 0) score_tile(0);
-      wait8(2);
-      __syncthreads();  // P of tile 0 is ready
-      for (int t = 0; t < n_tiles; ++t) {
-        if (t + 1 < n_tiles) score_tile(t + 1);
-        wait8(t + 2);
-        __syncthreads();
-        step8(t);
-      }
-    } else {
-      __syncthreads();  // tile 0 is in LDS
-      if (n_tiles > 0) score_tile(0);
-      __syncthreads();  // P of tile 0 is ready; tile 1 is in LDS
-      for (int t = 0; t < n_tiles; ++t) {
-        if (t + 1 < n_tiles) score_tile(t + 1);
-        __syncthreads();
-      }
+    __syncthreads();  // tile 0 is in LDS
+    if (n_tiles > 0) score_tile(0);
+    __syncthreads();  // P of tile 0 is ready; tile 1 is in LDS
+    for (int t = 0; t < n_tiles; ++t) {
+      if (t + 1 < n_tiles) score_tile(t + 1);
+      __syncthreads();
     }
     const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
     if (g2 == 0) {
@@ -295,6 +268,64 @@ __global__ __launch_bounds__(k3dec::NTHREADS) void decode_attn_k3_kernel(DecodeA
   } else {
     // ---------------- P.V waves: latent features [pw*128, pw*128 + 128) ----------------
     const int pw = wave - 3;
+    // ---- FP8 rows: issued by P.V waves 3-5 (7 of a tile's 21 wave-wide loads each) ----
+    // Load i of a tile fills tile bytes 1024 i .. 1024 i + 1023 (the last one's upper half repeats
+    // the tile's last chunk); d8[k] holds this lane's source row r in the tile (bits 16+) and the
+    // byte offset r * 656 + 16 c of its chunk (bits 0-15).
+    const uint8_t* lat8 = (const uint8_t*)a.latent + seq_rows * kFp8RowBytes;
+    uint32_t d8[NL8];
+#pragma unroll
+    for (int k = 0; k < NL8; ++k) {
+      const int i = (wave - 3) * NL8 + k;
+      const int P = min(i * 64 + lane, BT * F8CH - 1);
+      const int r = P / F8CH;
+      d8[k] = ((uint32_t)r << 16) | (uint32_t)(P * 16);
+    }
+    int issued8 = 0;
+    auto issue8 = [&]() {  // the next tile's raw rows
+      if (!FP8 || issued8 >= n_tiles) return;
+      const int t = issued8++;
+      if (wave < 3 || wave == 6) return;
+      const uint32_t fs = lds_addr(f8_s[t % NS8]) + (wave - 3) * NL8 * 1024;
+      const int j0 = t * BT;
+      if (!GATHER && j0 + BT <= n_pos) {  // whole tile of consecutive rows (one page): offsets only
+        const int row0 = __builtin_amdgcn_readfirstlane(crow(p0 + j0));
+        const uint8_t* base = lat8 + (size_t)row0 * kFp8RowBytes;
+#pragma unroll
+        for (int k = 0; k < NL8; ++k) lds_dma16_sbase(d8[k] & 0xFFFFu, base, fs + k * 1024);
+        return;
+      }
+      // gathered rows, or the partial last tile (rows past the end repeat a valid row, masked)
+      const int row0 = GATHER ? 0 : crow(p0 + j0);
+#pragma unroll 1
+      for (int k = 0; k < NL8; ++k) {
+        const int r = (int)(d8[k] >> 16);
+        const uint32_t coff = (d8[k] & 0xFFFFu) - (uint32_t)(r * kFp8RowBytes);
+        const int jr = min(j0 + r, n_pos - 1);
+        const int row = GATHER ? sel_s[jr] : row0 + (jr - j0);
+        lds_dma16(lat8 + (size_t)row * kFp8RowBytes + coff, fs + k * 1024);
+      }
+    };
+    auto wait8 = [&](int need) {  // this wave's loads of tile `need` have landed
+      const int after = issued8 - 1 - need;
+      static_assert(NL8 == 7, "vmcnt immediates");
+      if (after >= 4)
+        asm volatile("s_waitcnt vmcnt(28)" ::: "memory");
+      else if (after == 3)
+        asm volatile("s_waitcnt vmcnt(21)" ::: "memory");
+      else if (after == 2)
+        asm volatile("s_waitcnt vmcnt(14)" ::: "memory");
+      else if (after == 1)
+        asm volatile("s_waitcnt vmcnt(7)" ::: "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    };
+    // before the first step: tiles 0 .. NS8-2 issued, tile 0 landed (the barrier follows)
+    auto prologue8 = [&]() {
+#pragma unroll
+      for (int i = 0; i + 1 < NS8; ++i) issue8();
+      wait8(0);
+    };
     // Per-lane source offsets (bytes from the tile's first row) of this wave's 9 loads, with the
     // row in the top bits for the clamped path: chunk P = i*64 + lane of the tile is row P/72,
     // swizzled chunk (P%72) ^ swz(row).
@@ -306,41 +337,43 @@ __global__ __launch_bounds__(k3dec::NTHREADS) void decode_attn_k3_kernel(DecodeA
       doff[k] = (uint32_t)(r * DL * 2 + c * 16) | ((uint32_t)r << 16);
     }
     auto issue = [&](int t) {  // this wave's 9 of the 36 DMA loads of tile t
-      if (t >= n_tiles) return;
-      const uint32_t slot_addr = lds_addr(lat_s[t % NSLOT]);
-      const int j0 = t * BT;
-      if (!GATHER && j0 + BT <= n_pos) {  // whole tile of consecutive rows: offsets only
-        // a tile lies in one page; its first row is wave-uniform (the DMA takes it in SGPRs)
-        const int row0 = __builtin_amdgcn_readfirstlane(crow(p0 + j0));
-        const char* base = (const char*)(lat + (size_t)row0 * DL);
+      if constexpr (!FP8) {
+        if (t >= n_tiles) return;
+        const uint32_t slot_addr = lds_addr(lat_s[t % NSLOT]);
+        const int j0 = t * BT;
+        if (!GATHER && j0 + BT <= n_pos) {  // whole tile of consecutive rows: offsets only
+          // a tile lies in one page; its first row is wave-uniform (the DMA takes it in SGPRs)
+          const int row0 = __builtin_amdgcn_readfirstlane(crow(p0 + j0));
+          const char* base = (const char*)(lat + (size_t)row0 * DL);
 #pragma unroll
-        for (int k = 0; k < NLOAD_W; ++k)
-          lds_dma16_sbase(doff[k] & 0xFFFFu, base, slot_addr + (pw * NLOAD_W + k) * 1024);
-        return;
-      }
-      // rows past the end repeat a valid row (masked)
-      if constexpr (GATHER) {
-        // gathered rows: all nine source rows are read from LDS together, then the nine loads
-        // (faster than three at a time although it spills a few registers)
-        int rows[NLOAD_W];
-#pragma unroll
-        for (int k = 0; k < NLOAD_W; ++k) rows[k] = sel_s[min(j0 + (int)(doff[k] >> 16), n_pos - 1)];
-#pragma unroll
-        for (int k = 0; k < NLOAD_W; ++k) {
-          const uint32_t coff = (doff[k] & 0xFFFFu) - (doff[k] >> 16) * (DL * 2);  // the chunk's byte offset
-          lds_dma16((const char*)lat + (size_t)rows[k] * (DL * 2) + coff, slot_addr + (pw * NLOAD_W + k) * 1024);
+          for (int k = 0; k < NLOAD_W; ++k)
+            lds_dma16_sbase(doff[k] & 0xFFFFu, base, slot_addr + (pw * NLOAD_W + k) * 1024);
+          return;
         }
-      } else {
-        // the partial last tile of a split: consecutive rows (a rolled loop keeps the P.V waves'
-        // registers free)
-        const int row0 = crow(p0 + j0);
+        // rows past the end repeat a valid row (masked)
+        if constexpr (GATHER) {
+          // gathered rows: all nine source rows are read from LDS together, then the nine loads
+          // (faster than three at a time although it spills a few registers)
+          int rows[NLOAD_W];
+#pragma unroll
+          for (int k = 0; k < NLOAD_W; ++k) rows[k] = sel_s[min(j0 + (int)(doff[k] >> 16), n_pos - 1)];
+#pragma unroll
+          for (int k = 0; k < NLOAD_W; ++k) {
+            const uint32_t coff = (doff[k] & 0xFFFFu) - (doff[k] >> 16) * (DL * 2);  // the chunk's byte offset
+            lds_dma16((const char*)lat + (size_t)rows[k] * (DL * 2) + coff, slot_addr + (pw * NLOAD_W + k) * 1024);
+          }
+        } else {
+          // the partial last tile of a split: consecutive rows (a rolled loop keeps the P.V waves'
+          // registers free)
+          const int row0 = crow(p0 + j0);
 #pragma unroll 1
-        for (int k = 0; k < NLOAD_W; ++k) {
-          const int i = pw * NLOAD_W + k;
-          const int P = i * 64 + lane;  // destination chunk of this lane
-          const int r = P / CH, c = (P - r * CH) ^ swz_row(r);
-          const int jr = min(j0 + r, n_pos - 1);
-          lds_dma16(lat + (size_t)(row0 + (jr - j0)) * DL + c * 8, slot_addr + i * 1024);
+          for (int k = 0; k < NLOAD_W; ++k) {
+            const int i = pw * NLOAD_W + k;
+            const int P = i * 64 + lane;  // destination chunk of this lane
+            const int r = P / CH, c = (P - r * CH) ^ swz_row(r);
+            const int jr = min(j0 + r, n_pos - 1);
+            lds_dma16(lat + (size_t)(row0 + (jr - j0)) * DL + c * 8, slot_addr + i * 1024);
+          }
         }
       }
     };
@@ -350,6 +383,8 @@ __global__ __launch_bounds__(k3dec::NTHREADS) void decode_attn_k3_kernel(DecodeA
     for (int t = 0; t < issued; ++t) issue(t);
     if (!FP8) wait_for(0, issued);
     const int G = lane >> 4, jj = lane & 15;
+    const uint32_t tr8_off = (8 * (G >> 1) + (jj >> 1)) * kFp8RowBytes + 16 * (G & 1) + 8 * (jj & 1);
+    const uint32_t f8_slot0 = lds_addr(f8_s[0]);
     f32x16 o[4][3];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -357,16 +392,20 @@ __global__ __launch_bounds__(k3dec::NTHREADS) void decode_attn_k3_kernel(DecodeA
       for (int j = 0; j < 3; ++j) o[i][j] = f32x16{};
     if constexpr (FP8) {
       prologue8();
-      wait8(2);
-      __syncthreads();  // P of tile 0 is ready
+      __syncthreads();  // tile 0 is in LDS
+      wait8(1);
+      __syncthreads();  // P of tile 0 is ready; tile 1 is in LDS
     } else {
       __syncthreads();  // tile 0 is in LDS
       if (n_tiles > 1) wait_for(1, issued);
       __syncthreads();  // P of tile 0 is ready; tile 1 is in LDS
     }
     for (int t = 0; t < n_tiles; ++t) {
-      if (!FP8 && issued < n_tiles) issue(issued++);  // tile t + NSLOT - 1, into the slot tile t-1 used
-      const uint8_t* slot = lat_s[t % NSLOT];
+      if constexpr (FP8)
+        issue8();  // tile t + NS8 - 1, into the slot tile t - 1 used
+      else if (issued < n_tiles)
+        issue(issued++);  // tile t + NSLOT - 1, into the slot tile t-1 used
+      const uint8_t* slot = lat_s[t % (FP8 ? 1 : NSLOT)];
       const uint16_t* pbuf = Ps[t & 1];
       float al[3];
 #pragma unroll
@@ -386,27 +425,61 @@ __global__ __launch_bounds__(k3dec::NTHREADS) void decode_attn_k3_kernel(DecodeA
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
         for (int hs = 0; hs < 3; ++hs) pb[ks][hs] = ld16(pbuf + (hs * 32 + l32) * PROW + ks * 16 + g2 * 8);
-      auto lat_frag = [&](int k) __attribute__((always_inline)) {
-        const int ks = k >> 2, dt = k & 3;
-        const int r0 = ks * 16 + 8 * (G >> 1) + (jj >> 2), r1 = r0 + 4;
-        const int fcol = (pw * 4 + dt) * 32 + 16 * (G & 1) + 4 * (jj & 3);
-        const int c = fcol >> 3, off = (fcol & 7) * 2;
-        const u32x2 lo = lds_read_tr16(slot + (r0 * CH + (c ^ swz_row(r0))) * 16 + off);
-        const u32x2 hi = lds_read_tr16(slot + (r1 * CH + (c ^ swz_row(r1))) * 16 + off);
-        return u32x4{lo.x, lo.y, hi.x, hi.y};
-      };
-      u32x4 af = lat_frag(0);
+      if constexpr (FP8) {
+        // P^T entries times their positions' scales for this wave's block: the products with the
+        // unscaled codes are then those of the decoded values
+        uint32_t fsa = f8_slot0 + (t % NS8) * F8SLOT;
+        asm volatile("" : "+v"(fsa));  // one address register; the rest are immediate offsets
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const u32x4 an = lat_frag(k < 7 ? k + 1 : 7);
+        for (int ks = 0; ks < 2; ++ks) {
+          float psc[8];
 #pragma unroll
-        for (int hs = 0; hs < 3; ++hs) o[k & 3][hs] = mfma32(af, pb[k >> 2][hs], o[k & 3][hs]);
-        af = an;
+          for (int i = 0; i < 8; ++i)
+            psc[i] = *(GMLA_LDS const float*)(fsa + g2 * 8 * kFp8RowBytes + (ks * 16 + i) * kFp8RowBytes + kFp8ScaleOff +
+                                              4 * pw);
+#pragma unroll
+          for (int hs = 0; hs < 3; ++hs) pb[ks][hs] = scale_bf16x8(pb[ks][hs], psc);
+        }
+        // Lat^T fragments: 8 positions of one feature per lane, one transposed byte read each
+        // lane (G, jj) starts at row 8 (G >> 1) + (jj >> 1), byte 16 (G & 1) + 8 (jj & 1) of the block
+        const uint32_t fla = fsa + pw * 128 + tr8_off;
+        auto raw_frag = [&](int k) __attribute__((always_inline)) {
+          const int ks = k >> 2, dt = k & 3;
+          return lds_read_tr8(fla + ks * 16 * kFp8RowBytes + dt * 32);
+        };
+        u32x2 cr = raw_frag(0);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const u32x2 cn = raw_frag(k < 7 ? k + 1 : 7);
+          const u32x4 af = cvt_fp8x8(cr, 1.0f);
+#pragma unroll
+          for (int hs = 0; hs < 3; ++hs) o[k & 3][hs] = mfma32(af, pb[k >> 2][hs], o[k & 3][hs]);
+          cr = cn;
+        }
+      } else {
+        auto lat_frag = [&](int k) __attribute__((always_inline)) {
+          const int ks = k >> 2, dt = k & 3;
+          const int r0 = ks * 16 + 8 * (G >> 1) + (jj >> 2), r1 = r0 + 4;
+          const int fcol = (pw * 4 + dt) * 32 + 16 * (G & 1) + 4 * (jj & 3);
+          const int c = fcol >> 3, off = (fcol & 7) * 2;
+          const u32x2 lo = lds_read_tr16(slot + (r0 * CH + (c ^ swz_row(r0))) * 16 + off);
+          const u32x2 hi = lds_read_tr16(slot + (r1 * CH + (c ^ swz_row(r1))) * 16 + off);
+          return u32x4{lo.x, lo.y, hi.x, hi.y};
+        };
+        u32x4 af = lat_frag(0);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const u32x4 an = lat_frag(k < 7 ? k + 1 : 7);
+#pragma unroll
+          for (int hs = 0; hs < 3; ++hs) o[k & 3][hs] = mfma32(af, pb[k >> 2][hs], o[k & 3][hs]);
+          af = an;
+        }
       }
-      if (!FP8 && t + 2 < n_tiles) wait_for(t + 2, issued);  // the score waves read it in the next step
-      if (FP8) wait8(t + 2);  // converted after this barrier
+      if constexpr (FP8)
+        wait8(t + 2);  // the score waves read it in the next step
+      else if (t + 2 < n_tiles)
+        wait_for(t + 2, issued);  // the score waves read it in the next step
       __syncthreads();
-      if constexpr (FP8) step8(t);
     }
     __syncthreads();  // 1/l of every head is in LDS
     if (a.n_splits == 1 && !a.lse) {  // one split: its normalised output is the result
