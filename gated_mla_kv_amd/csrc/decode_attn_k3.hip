@@ -124,6 +124,9 @@ __global__ __launch_bounds__(k3dec::NTHREADS) void decode_attn_k3_kernel(DecodeA
   auto crow = [&](int p) __attribute__((always_inline)) {
     return paged ? (int)cache_row(a.pages, a.T_cap, seq, p) : p;
   };
+  auto crow_uniform = [&](int p) __attribute__((always_inline)) {  // p the same in every lane
+    return paged ? (int)cache_row_uniform(a.pages, a.T_cap, seq, p) : p;
+  };
   const uint16_t* lat = a.latent + seq_rows * DL;
 
   if (GATHER) {  // this split's selected positions, clamped into the cache, as cache rows
@@ -289,14 +292,14 @@ __global__ __launch_bounds__(k3dec::NTHREADS) void decode_attn_k3_kernel(DecodeA
       const uint32_t fs = lds_addr(f8_s[t % NS8]) + (wave - 3) * NL8 * 1024;
       const int j0 = t * BT;
       if (!GATHER && j0 + BT <= n_pos) {  // whole tile of consecutive rows (one page): offsets only
-        const int row0 = __builtin_amdgcn_readfirstlane(crow(p0 + j0));
+        const int row0 = __builtin_amdgcn_readfirstlane(crow_uniform(p0 + j0));
         const uint8_t* base = lat8 + (size_t)row0 * kFp8RowBytes;
 #pragma unroll
         for (int k = 0; k < NL8; ++k) lds_dma16_sbase(d8[k] & 0xFFFFu, base, fs + k * 1024);
         return;
       }
       // gathered rows, or the partial last tile (rows past the end repeat a valid row, masked)
-      const int row0 = GATHER ? 0 : crow(p0 + j0);
+      const int row0 = GATHER ? 0 : crow_uniform(p0 + j0);
 #pragma unroll 1
       for (int k = 0; k < NL8; ++k) {
         const int r = (int)(d8[k] >> 16);
@@ -343,7 +346,7 @@ __global__ __launch_bounds__(k3dec::NTHREADS) void decode_attn_k3_kernel(DecodeA
         const int j0 = t * BT;
         if (!GATHER && j0 + BT <= n_pos) {  // whole tile of consecutive rows: offsets only
           // a tile lies in one page; its first row is wave-uniform (the DMA takes it in SGPRs)
-          const int row0 = __builtin_amdgcn_readfirstlane(crow(p0 + j0));
+          const int row0 = __builtin_amdgcn_readfirstlane(crow_uniform(p0 + j0));
           const char* base = (const char*)(lat + (size_t)row0 * DL);
 #pragma unroll
           for (int k = 0; k < NLOAD_W; ++k)
@@ -365,7 +368,7 @@ __global__ __launch_bounds__(k3dec::NTHREADS) void decode_attn_k3_kernel(DecodeA
         } else {
           // the partial last tile of a split: consecutive rows (a rolled loop keeps the P.V waves'
           // registers free)
-          const int row0 = crow(p0 + j0);
+          const int row0 = crow_uniform(p0 + j0);
 #pragma unroll 1
           for (int k = 0; k < NLOAD_W; ++k) {
             const int i = pw * NLOAD_W + k;

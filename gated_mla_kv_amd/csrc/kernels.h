@@ -27,6 +27,18 @@ __device__ __forceinline__ size_t cache_row(const PageTable& pt, int T_cap, int 
   const int pg = min(max(pt.table[(size_t)seq * pt.max_blocks + pos / pt.page_size], 0), pt.n_pages - 1);
   return (size_t)pg * pt.page_size + pos % pt.page_size;
 }
+// As cache_row for a wave-uniform (seq, pos), with the table entry read through the scalar
+// cache: its wait (lgkmcnt) leaves the wave's outstanding vector loads in flight, where a vector
+// load of the entry would wait for all of them.
+__device__ __forceinline__ size_t cache_row_uniform(const PageTable& pt, int T_cap, int seq, int pos) {
+  if (!pt.table) return (size_t)seq * T_cap + pos;
+  const int32_t* e = pt.table + (size_t)__builtin_amdgcn_readfirstlane(seq) * pt.max_blocks +
+                     __builtin_amdgcn_readfirstlane(pos) / pt.page_size;
+  int v;
+  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(e) : "memory");
+  const int pg = min(max(v, 0), pt.n_pages - 1);
+  return (size_t)pg * pt.page_size + pos % pt.page_size;
+}
 
 struct KvAppendArgs {
   const int32_t* pos;  // [B] first position of each sequence's new tokens
