@@ -39,12 +39,21 @@ namespace gmla {
 // ------------------------------------------------------------------------------------------
 __device__ __forceinline__ uint32_t order_key(float f);
 constexpr int kHistBins = 4096;      // first radix digit: the top 12 bits of the order key
-constexpr int kScoreChunk = 2048;    // positions per workgroup
+constexpr int kScoreChunkMin = 512;  // fewest positions per workgroup
 constexpr int kScoreWaves = 8;
+constexpr int kScoreBufs = 2;  // key tiles in flight per wave (3 and 4 measured slower)
 
-// One workgroup per (2048-position chunk, row); wave w scores the 32-position tiles w, w+8, ... of
-// the chunk with the keys of the next tile already in flight, and every score's top digit goes
-// into an LDS histogram that is added to the row's histogram at the end.
+// One workgroup per (chunk of a.chunk positions, row); wave w scores the 32-position tiles w,
+// w+8, ... of the chunk with the keys of the next tile already in flight, and every score's top
+// digit goes into an LDS histogram that is added to the row's histogram at the end. The launcher
+// sizes the chunks so that all rows' workgroups fill the CUs once (one per CU): with a fixed
+// chunk, B = 8 rows of 65,537 positions made 264 workgroups, and the 8 past the 256 CUs ran as
+// a second round.
+// FP8 (codes + per-key scale) and PAGED are template parameters so that the tile loop has no
+// branches: the wait counts for the keys in flight then stay exact (at a runtime branch the
+// compiler waits for every outstanding load), and a paged tile's table entry is read through the
+// scalar cache, leaving the key loads in flight.
+template <bool FP8, bool PAGED>
 __global__ __launch_bounds__(kScoreWaves * 64) void index_scores_kernel(IndexScoreArgs a) {
   constexpr int NIH = 32, DI = 128, KS = DI / 16;
   __shared__ int lhist[kHistBins];
@@ -53,40 +62,44 @@ __global__ __launch_bounds__(kScoreWaves * 64) void index_scores_kernel(IndexSco
   const int b = blockIdx.y;
   const RowMap rm = row_map(a.row0, a.rows_per_seq, b);
   const int t = min(min(a.n_vis[rm.seq] + a.vis_offset + rm.extra, a.T_cap), a.score_stride);
-  const int base = blockIdx.x * kScoreChunk;
+  const int base = blockIdx.x * a.chunk;
   if (base >= t) return;
-  const int end = min(base + kScoreChunk, t);
+  const int end = min(base + a.chunk, t);
   for (int i = threadIdx.x; i < kHistBins; i += kScoreWaves * 64) lhist[i] = 0;
-  const uint16_t* kb = a.idx_k;                 // cache rows from cache_row (paged or not)
+  const uint16_t* kb = a.idx_k;
   const uint8_t* kb8 = (const uint8_t*)a.idx_k;
-  const bool fp8 = a.idx_scale != nullptr;
   const int n_tiles = cdiv(end - base, 32);
   const int nt_w = wave < n_tiles ? cdiv(n_tiles - wave, kScoreWaves) : 0;  // this wave's tiles
-  // keys of this wave's j-th tile (positions p0 + l32): the B operand, one 16-byte (bf16) or
-  // 8-byte (FP8, widened when used) load per k-step
-  // cache row of a position of this wave's j-th tile (a 32-position tile lies in one page)
-  auto key_row = [&](int j, int pos) __attribute__((always_inline)) {
-    const int p0 = base + (wave + kScoreWaves * j) * 32;
-    return cache_row(a.pages, a.T_cap, rm.seq, p0) + (pos - p0);
+  // cache row of this lane's position in the wave's j-th tile (a 32-position tile lies in one
+  // page); tiles past the chunk's last re-read it and positions past the end repeat the last one
+  // (their scores are not stored), so that the tile loop needs no branches
+  auto key_row = [&](int j) __attribute__((always_inline)) {
+    const int p0 = base + min(wave + kScoreWaves * j, n_tiles - 1) * 32;
+    const int pos = min(p0 + l32, end - 1);
+    if constexpr (PAGED)
+      return cache_row_uniform(a.pages, a.T_cap, rm.seq, p0) + (size_t)(pos - p0);
+    else
+      return (size_t)rm.seq * a.T_cap + pos;
   };
-  auto load_keys = [&](int j, u32x4* kf) __attribute__((always_inline)) {
-    const size_t row = key_row(j, min(base + (wave + kScoreWaves * j) * 32 + l32, end - 1));  // past the end: not stored
-    if (fp8) {
+  // keys of this wave's j-th tile (positions p0 + l32): the B operand, one 16-byte (bf16) or
+  // 8-byte (FP8, widened when used) load per k-step, and the FP8 key's scale with them
+  auto load_keys = [&](int j, u32x4* kf, float& ks) __attribute__((always_inline)) {
+    const size_t row = key_row(j);
+    if constexpr (FP8) {
 #pragma unroll
       for (int s = 0; s < KS; s += 2) {
         const u32x2 w0 = ld8(kb8 + row * DI + s * 16 + g2 * 8);
         const u32x2 w1 = ld8(kb8 + row * DI + (s + 1) * 16 + g2 * 8);
         kf[s] = u32x4{w0.x, w0.y, w1.x, w1.y};  // raw codes, widened in score()
       }
+      ks = a.idx_scale[row];
     } else {
 #pragma unroll
       for (int s = 0; s < KS; ++s) kf[s] = ld16(kb + row * DI + s * 16 + g2 * 8);
+      ks = 1.f;
     }
   };
-  u32x4 kf0[KS], kf1[KS];
-  if (nt_w > 0) load_keys(0, kf0);
-  if (nt_w > 1) load_keys(1, kf1);
-  // A operand: q^I rows (heads) for this lane's head l32
+  // A operand (loaded before the keys, whose loads then stay in flight past its wait): q^I rows (heads) for this lane's head l32
   u32x4 qa[KS];
   const uint16_t* qrow = a.q_idx + ((size_t)b * NIH + l32) * DI;
 #pragma unroll
@@ -95,10 +108,14 @@ __global__ __launch_bounds__(kScoreWaves * 64) void index_scores_kernel(IndexSco
   float wgt[16];
 #pragma unroll
   for (int r = 0; r < 16; ++r) wgt[r] = a.w_idx[(size_t)b * NIH + (r >> 2) * 8 + g2 * 4 + (r & 3)] * a.scale;
+  u32x4 kf[kScoreBufs][KS];  // keys of this wave's next kScoreBufs tiles, in flight together
+  float kscale[kScoreBufs];
+#pragma unroll
+  for (int i = 0; i < kScoreBufs; ++i) load_keys(i, kf[i], kscale[i]);
   __syncthreads();  // histogram cleared
-  auto score = [&](int j, const u32x4* kf) __attribute__((always_inline)) {
+  auto score = [&](int j, const u32x4* kf, float ks) __attribute__((always_inline)) {
     f32x16 acc = f32x16{};
-    if (fp8) {
+    if constexpr (FP8) {
 #pragma unroll
       for (int s = 0; s < KS; s += 2) {
         const u32x2 a0 = e4m3x4_to_bf16(kf[s].x), a1 = e4m3x4_to_bf16(kf[s].y);
@@ -114,19 +131,20 @@ __global__ __launch_bounds__(kScoreWaves * 64) void index_scores_kernel(IndexSco
 #pragma unroll
     for (int r = 0; r < 16; ++r) sc += wgt[r] * fmaxf(acc[r], 0.f);
     sc += __shfl_xor(sc, 32, 64);
+    if constexpr (FP8) sc *= ks;
     const int pos = base + (wave + kScoreWaves * j) * 32 + l32;
-    if (fp8) sc *= a.idx_scale[key_row(j, min(pos, end - 1))];
     if (pos < end && g2 == 0) {
       a.scores[(size_t)b * a.score_stride + pos] = sc;
       atomicAdd(&lhist[order_key(sc) >> 20], 1);
     }
   };
-  for (int j = 0; j < nt_w; j += 2) {
-    score(j, kf0);
-    if (j + 2 < nt_w) load_keys(j + 2, kf0);
-    if (j + 1 < nt_w) {
-      score(j + 1, kf1);
-      if (j + 3 < nt_w) load_keys(j + 3, kf1);
+  // branch-free steady state: every step scores one tile and starts the loads kScoreBufs ahead
+  // (past the wave's last tile they re-read the chunk's last tile, unused)
+  for (int j = 0; j < nt_w; j += kScoreBufs) {
+#pragma unroll
+    for (int i = 0; i < kScoreBufs; ++i) {
+      score(j + i, kf[i], kscale[i]);
+      load_keys(j + i + kScoreBufs, kf[i], kscale[i]);
     }
   }
   __syncthreads();
@@ -942,8 +960,25 @@ hipError_t launch_index_topk(IndexScoreArgs sa, int max_visible, TopkArgs ta, in
   const bool one_seq = sa.rows_per_seq > 1 && sa.row0 / sa.rows_per_seq == (sa.row0 + B - 1) / sa.rows_per_seq;
   if (max_visible > 0 && one_seq)
     index_scores_rows_kernel<<<dim3(cdiv(max_visible, kRowBlock), cdiv(B, kRowsPerWg)), kRowsPerWg * 64, 0, st>>>(sa);
-  else if (max_visible > 0)
-    index_scores_kernel<<<dim3(cdiv(max_visible, kScoreChunk), B), kScoreWaves * 64, 0, st>>>(sa);
+  else if (max_visible > 0) {
+    // chunks per row such that the B rows' workgroups fill the CUs a whole number of times
+    int dev = 0, n_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n_cu < 1)
+      n_cu = 256;
+    const int cpr = max(1, n_cu * cdiv(B, n_cu) / B);
+    sa.chunk = max(kScoreChunkMin, cdiv(cdiv(max_visible, cpr), 32) * 32);
+    const dim3 grid(cdiv(max_visible, sa.chunk), B);
+    const bool fp8 = sa.idx_scale != nullptr, paged = sa.pages.table != nullptr;
+    if (fp8 && paged)
+      index_scores_kernel<true, true><<<grid, kScoreWaves * 64, 0, st>>>(sa);
+    else if (fp8)
+      index_scores_kernel<true, false><<<grid, kScoreWaves * 64, 0, st>>>(sa);
+    else if (paged)
+      index_scores_kernel<false, true><<<grid, kScoreWaves * 64, 0, st>>>(sa);
+    else
+      index_scores_kernel<false, false><<<grid, kScoreWaves * 64, 0, st>>>(sa);
+  }
   topk_count_kernel<<<dim3(S, B), 256, 0, st>>>(ta);
   topk_select_kernel<<<B, kTopkThreads, 0, st>>>(ta);
   topk_compact_kernel<<<dim3(S, B), 256, 0, st>>>(ta);
