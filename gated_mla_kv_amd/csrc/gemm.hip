@@ -492,15 +492,15 @@ __global__ __launch_bounds__(256) void gemm_nt_skinny_lds(GemmArgs g, float* par
   const int k1 = blockIdx.y * kr;
   // rows past N re-read the last row (computed, never stored)
   const uint16_t* wr = wrow_ptr(g, min(n0 + (lane & 31), g.N - 1)) + k1 + half * 8;
-  // activation staging: thread t copies token t / 8, k [32 (t % 8), +32) of each chunk
+  // activation staging: thread t copies token t / 8, k [32 (t % 8), +32) of each chunk; tokens
+  // past M copy token 0 (their outputs are computed, never stored)
   const int tt = tid >> 3, part = tid & 7;
-  const bool xok = tt < g.M;
-  const uint16_t* xg = g.a + (size_t)(xok ? tt : 0) * g.lda + k1 + part * 32;
+  const uint16_t* xg = g.a + (size_t)(tt < g.M ? tt : 0) * g.lda + k1 + part * 32;
   const int nch = kr / kSkChunk;
   u32x4 xr[4], wa[16], wb[16];
   auto load_x = [&](int ch) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) xr[i] = xok ? ld16(xg + ch * kSkChunk + i * 8) : zero16();
+    for (int i = 0; i < 4; ++i) xr[i] = ld16(xg + ch * kSkChunk + i * 8);
   };
   auto load_w = [&](int ch, u32x4* v) __attribute__((always_inline)) {
 #pragma unroll
@@ -511,10 +511,11 @@ __global__ __launch_bounds__(256) void gemm_nt_skinny_lds(GemmArgs g, float* par
     uint16_t* xb = xs[ch & 1];
 #pragma unroll
     for (int i = 0; i < 4; ++i) st16(xb + tt * kSkXPitch + part * 32 + i * 8, xr[i]);
-    if (ch + 1 < nch) {
-      load_x(ch + 1);
-      load_w(ch + 1, wnext);
-    }
+    // the next chunk (the last one again after the last: unused), with no branch, so that the
+    // MFMAs below wait only for this chunk's weights (at a branch the compiler waits for all loads)
+    const int cn = min(ch + 1, nch - 1);
+    load_x(cn);
+    load_w(cn, wnext);
     __syncthreads();
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
@@ -524,10 +525,12 @@ __global__ __launch_bounds__(256) void gemm_nt_skinny_lds(GemmArgs g, float* par
   };
   load_x(0);
   load_w(0, wa);
-  for (int ch = 0; ch < nch; ch += 2) {
+  int ch = 0;
+  for (; ch + 1 < nch; ch += 2) {
     step(ch, wa, wb);
-    if (ch + 1 < nch) step(ch + 1, wb, wa);
+    step(ch + 1, wb, wa);
   }
+  if (ch < nch) step(ch, wa, wb);
   // acc[r] = out(m = lane % 32, n = n0 + 8 (r / 4) + 4 half + r % 4)
   const int m = lane & 31;
   if (m >= g.M) return;
