@@ -435,12 +435,23 @@ __global__ __launch_bounds__(256) void absorb_q_k3_kernel(const uint16_t* __rest
   if ((int)blockIdx.y * 32 >= B) return;
   stage_rows_512(wk_s, kAbsPitch, wkvb + (size_t)h * (DN + DV) * L, DN, wave, lane);  // W^K_h
   const int G = lane >> 4, jj = lane & 15, g2 = lane >> 5, l32 = lane & 31;
-  for (int t0 = blockIdx.y * 32; t0 < B; t0 += gridDim.y * 32) {
-    const int tok = min(t0 + l32, B - 1);  // tokens past B: computed, not stored
+  // q_nope of this lane's token in block t0 (tokens past B: the last one, computed, not stored),
+  // and the 16-byte chunk tid % 8 of token t0 + tid / 8's q_shared, copied to q~[.., L:]
+  const int ctok = tid / (DS / 8), cch = tid % (DS / 8);  // 32 tokens x 8 chunks = 256 threads
+  auto load_q = [&](int t0, u32x4* qb, u32x4& sh) __attribute__((always_inline)) {
+    const int tok = min(t0 + l32, B - 1);
     const uint16_t* qrow = q + (size_t)tok * ldq + h * DQK + g2 * 8;
-    u32x4 qb[DN / 16];
 #pragma unroll
     for (int ks = 0; ks < DN / 16; ++ks) qb[ks] = ld16(qrow + ks * 16);
+    sh = ld16(q + (size_t)min(t0 + ctok, B - 1) * ldq + h * DQK + DN + cch * 8);
+  };
+  const int tstep = gridDim.y * 32, tlast = (B - 1) / 32 * 32;
+  u32x4 qb[DN / 16], qn[DN / 16], sh, shn;
+  load_q(blockIdx.y * 32, qb, sh);
+  for (int t0 = blockIdx.y * 32; t0 < B; t0 += tstep) {
+    // the next block's loads (no branch: they stay in flight under this block's MFMAs)
+    load_q(min(t0 + tstep, tlast), qn, shn);
+    __builtin_amdgcn_sched_barrier(0);
     f32x16 acc[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};
 #pragma unroll
     for (int ks = 0; ks < DN / 16; ++ks) {
@@ -464,11 +475,10 @@ __global__ __launch_bounds__(256) void absorb_q_k3_kernel(const uint16_t* __rest
                                      pack_bf16x2(acc[dt][jg * 4 + 2], acc[dt][jg * 4 + 3])};
         }
     }
-    // q~[.., L:] = q_shared (64 values = 8 chunks of 16 bytes per token)
-    for (int i = tid; i < 32 * (DS / 8); i += 256) {
-      const int tt = t0 + i / (DS / 8), c = i % (DS / 8);
-      if (tt < B) st16(qt + ((size_t)tt * H + h) * (L + DS) + L + c * 8, ld16(q + (size_t)tt * ldq + h * DQK + DN + c * 8));
-    }
+    if (t0 + ctok < B) st16(qt + ((size_t)(t0 + ctok) * H + h) * (L + DS) + L + cch * 8, sh);
+#pragma unroll
+    for (int ks = 0; ks < DN / 16; ++ks) qb[ks] = qn[ks];
+    sh = shn;
   }
 }
 
@@ -555,77 +565,78 @@ __global__ __launch_bounds__(256) void vup_gate_k3_lds_kernel(const float* __res
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g2 = lane >> 5, l32 = lane & 31;
   stage_rows_512(wv_s, kVupPitch, wkvb + ((size_t)h * (DN + DV) + DN) * L, DV, wave, lane);
-  const int t0 = (blockIdx.y * 4 + wave) * 32;
-  if (t0 >= B) return;  // after the workgroup's only barrier
-  const int tok = min(t0 + l32, B - 1);
-  const float* orow = o + ((size_t)tok * H + h) * L + g2 * 8;
-  const uint16_t* arow = wv_s + l32 * kVupPitch + g2 * 8;
-  f32x16 acc[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};
-  constexpr int U = 8;  // k-steps of o~ loaded together
-  f32x4 ov[U][2];
-#pragma unroll
-  for (int i = 0; i < U; ++i) {
-    ov[i][0] = *(const f32x4*)(orow + i * 16);
-    ov[i][1] = *(const f32x4*)(orow + i * 16 + 4);
-  }
-#pragma unroll 1
-  for (int k0 = 0; k0 < L / 16; k0 += U) {
-    u32x4 bh[U], bl[U];
+  // wave w takes the 32-token blocks 4 blockIdx.y + w, + 4 gridDim.y, ... (W^V_h staged once)
+  for (int t0 = (blockIdx.y * 4 + wave) * 32; t0 < B; t0 += gridDim.y * 128) {
+    const int tok = min(t0 + l32, B - 1);
+    const float* orow = o + ((size_t)tok * H + h) * L + g2 * 8;
+    const uint16_t* arow = wv_s + l32 * kVupPitch + g2 * 8;
+    f32x16 acc[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};
+    constexpr int U = 8;  // k-steps of o~ loaded together
+    f32x4 ov[U][2];
 #pragma unroll
     for (int i = 0; i < U; ++i) {
-      const float x[8] = {ov[i][0][0], ov[i][0][1], ov[i][0][2], ov[i][0][3],
-                          ov[i][1][0], ov[i][1][1], ov[i][1][2], ov[i][1][3]};
-      uint32_t hi[4], lo[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        hi[e] = pack_bf16x2(x[2 * e], x[2 * e + 1]);
-        lo[e] = pack_bf16x2(x[2 * e] - lo_bf16(hi[e]), x[2 * e + 1] - hi_bf16(hi[e]));
-      }
-      bh[i] = u32x4{hi[0], hi[1], hi[2], hi[3]};
-      bl[i] = u32x4{lo[0], lo[1], lo[2], lo[3]};
+      ov[i][0] = *(const f32x4*)(orow + i * 16);
+      ov[i][1] = *(const f32x4*)(orow + i * 16 + 4);
     }
-    if (k0 + U < L / 16) {  // the next U k-steps of o~ while these run
+#pragma unroll 1
+    for (int k0 = 0; k0 < L / 16; k0 += U) {
+      u32x4 bh[U], bl[U];
 #pragma unroll
       for (int i = 0; i < U; ++i) {
-        ov[i][0] = *(const f32x4*)(orow + (k0 + U + i) * 16);
-        ov[i][1] = *(const f32x4*)(orow + (k0 + U + i) * 16 + 4);
-      }
-    }
+        const float x[8] = {ov[i][0][0], ov[i][0][1], ov[i][0][2], ov[i][0][3],
+                            ov[i][1][0], ov[i][1][1], ov[i][1][2], ov[i][1][3]};
+        uint32_t hi[4], lo[4];
 #pragma unroll
-    for (int i = 0; i < U; ++i)
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
-        const u32x4 wa = *(const u32x4*)(arow + dt * 32 * kVupPitch + (k0 + i) * 16);
-        acc[dt] = mfma32(wa, bh[i], acc[dt]);
-        acc[dt] = mfma32(wa, bl[i], acc[dt]);
-      }
-  }
-  if (t0 + l32 < B) {
-    const size_t ub = (size_t)(t0 + l32) * H * DV + (size_t)h * DV;
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-      for (int jg = 0; jg < 4; ++jg) {
-        const int d = dt * 32 + jg * 8 + g2 * 4;
-        float z[4] = {acc[dt][jg * 4], acc[dt][jg * 4 + 1], acc[dt][jg * 4 + 2], acc[dt][jg * 4 + 3]};
-        if (g_pre) {
-          const f32x4 gv = *(const f32x4*)(g_pre + ub + d);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) z[e] *= sigmoidf_(gv[e]);
+        for (int e = 0; e < 4; ++e) {
+          hi[e] = pack_bf16x2(x[2 * e], x[2 * e + 1]);
+          lo[e] = pack_bf16x2(x[2 * e] - lo_bf16(hi[e]), x[2 * e + 1] - hi_bf16(hi[e]));
         }
-        if (u_f32)
-          *(f32x4*)((float*)u + ub + d) = f32x4{z[0], z[1], z[2], z[3]};
-        else
-          *(u32x2*)((uint16_t*)u + ub + d) = u32x2{pack_bf16x2(z[0], z[1]), pack_bf16x2(z[2], z[3])};
+        bh[i] = u32x4{hi[0], hi[1], hi[2], hi[3]};
+        bl[i] = u32x4{lo[0], lo[1], lo[2], lo[3]};
       }
+      if (k0 + U < L / 16) {  // the next U k-steps of o~ while these run
+#pragma unroll
+        for (int i = 0; i < U; ++i) {
+          ov[i][0] = *(const f32x4*)(orow + (k0 + U + i) * 16);
+          ov[i][1] = *(const f32x4*)(orow + (k0 + U + i) * 16 + 4);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < U; ++i)
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          const u32x4 wa = *(const u32x4*)(arow + dt * 32 * kVupPitch + (k0 + i) * 16);
+          acc[dt] = mfma32(wa, bh[i], acc[dt]);
+          acc[dt] = mfma32(wa, bl[i], acc[dt]);
+        }
+    }
+    if (t0 + l32 < B) {
+      const size_t ub = (size_t)(t0 + l32) * H * DV + (size_t)h * DV;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int jg = 0; jg < 4; ++jg) {
+          const int d = dt * 32 + jg * 8 + g2 * 4;
+          float z[4] = {acc[dt][jg * 4], acc[dt][jg * 4 + 1], acc[dt][jg * 4 + 2], acc[dt][jg * 4 + 3]};
+          if (g_pre) {
+            const f32x4 gv = *(const f32x4*)(g_pre + ub + d);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) z[e] *= sigmoidf_(gv[e]);
+          }
+          if (u_f32)
+            *(f32x4*)((float*)u + ub + d) = f32x4{z[0], z[1], z[2], z[3]};
+          else
+            *(u32x2*)((uint16_t*)u + ub + d) = u32x2{pack_bf16x2(z[0], z[1]), pack_bf16x2(z[2], z[3])};
+        }
+    }
   }
 }
 
 hipError_t launch_absorb_q(Shape s, const uint16_t* q, int ldq, const uint16_t* wkvb, int B,
                            uint16_t* qt, hipStream_t st) {
   if (B <= 0) return hipSuccess;
-  if (s == Shape::K3)  // up to four token blocks per workgroup (W^K_h is staged once per workgroup)
-    absorb_q_k3_kernel<<<dim3(ShapeK3::H, cdiv(B, 128)), 256, 0, st>>>(q, ldq, wkvb, B, qt);
+  if (s == Shape::K3)  // up to eight token blocks per workgroup (W^K_h is staged once per workgroup)
+    absorb_q_k3_kernel<<<dim3(ShapeK3::H, cdiv(B, 256)), 256, 0, st>>>(q, ldq, wkvb, B, qt);
   else
     absorb_q_kernel<ShapeTiny><<<ShapeTiny::H, 256, 0, st>>>(q, ldq, wkvb, B, qt);
   return hipGetLastError();
@@ -634,8 +645,8 @@ hipError_t launch_absorb_q(Shape s, const uint16_t* q, int ldq, const uint16_t* 
 hipError_t launch_vup_gate(Shape s, const float* o, const uint16_t* wkvb, const float* g_pre,
                            int B, void* u, int u_f32, hipStream_t st) {
   if (B <= 0) return hipSuccess;
-  if (s == Shape::K3 && B > 32)  // many tokens: W^V_h staged once per 128 tokens
-    vup_gate_k3_lds_kernel<<<dim3(ShapeK3::H, cdiv(B, 128)), 256, 0, st>>>(o, wkvb, g_pre, B, u, u_f32);
+  if (s == Shape::K3 && B > 32)  // many tokens: W^V_h staged once per up to 256 tokens
+    vup_gate_k3_lds_kernel<<<dim3(ShapeK3::H, cdiv(B, 256)), 256, 0, st>>>(o, wkvb, g_pre, B, u, u_f32);
   else if (s == Shape::K3)  // one wave per (head, row group): 384 workgroups stream W^V
     vup_gate_k3_kernel<<<dim3(ShapeK3::H * 4, cdiv(B, 32)), 64, 0, st>>>(o, wkvb, g_pre, B, u, u_f32);
   else
