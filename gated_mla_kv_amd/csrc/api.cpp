@@ -607,10 +607,20 @@ static int prefill_front(const mla_dims* d, const mla_weights* w, const mla_cach
     if (idx_query) push(g, seg(w->w_idx_q, d->n_idx_heads * d->d_idx, wsp.qidx, d->n_idx_heads * d->d_idx, false, n));
     CHECK_HIP(launch_gemm(g, wsp.gemm_ws, wsp.gemm_ws_bytes, stream));
   }
+  // the kv up-projection writes k_nope and v straight into the expanded cache when its large-M
+  // kernel runs (kv_append then adds the shared-key part of each head's k row); otherwise it
+  // writes them to the workspace for kv_append to copy
+  bool kv_scattered = false;
   if (expanded_cache) {
     GemmArgs g = gemm_args(wsp.c, d->kv_lora, M, d->kv_lora);
     int n = 0;
     push(g, seg(w->w_kv_b, H * (d->d_nope + d->d_v), wsp.kv, H * (d->d_nope + d->d_v), false, n));
+    if (!cache->block_table) {
+      g.cs = CacheScatter{(uint16_t*)cache->k, (uint16_t*)cache->v, start_pos, T, cache->T_cap, H, d->d_nope, d->d_v,
+                          d->d_nope + d->d_shared};
+      kv_scattered = gemm_scatter_ok(g);
+      if (!kv_scattered) g.cs = CacheScatter{};
+    }
     CHECK_HIP(launch_gemm(g, wsp.gemm_ws, wsp.gemm_ws_bytes, stream));
   }
   if (with_idx)
@@ -622,7 +632,9 @@ static int prefill_front(const mla_dims* d, const mla_weights* w, const mla_cach
   a.r = wsp.r;
   a.ld_r = d->d_shared;
   a.latent = (uint16_t*)cache->latent;
-  if (expanded_cache) {
+  if (expanded_cache && kv_scattered) {
+    a.k = (uint16_t*)cache->k;  // shared-key part only (k_nope null)
+  } else if (expanded_cache) {
     a.k_nope = wsp.kv;
     a.ld_k_tok = H * (d->d_nope + d->d_v);
     a.ld_k_head = d->d_nope + d->d_v;

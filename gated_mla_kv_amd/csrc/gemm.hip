@@ -368,6 +368,16 @@ __global__ __launch_bounds__(NWV * 64) void gemm_nt_dma(GemmArgs g) {
   // column's segment type (fp32: 16 bytes, bf16: 8 bytes per lane).
   __syncthreads();  // every wave is done with the ring
   GMLA_LDS float* stg = (GMLA_LDS float*)(smem0) + wave * (WM * PITCH);
+  // cache scatter: when all of the tile's rows belong to one sequence (the usual case), its start
+  // is read once and row m goes to position m + sp0
+  int sb = -1, sp0 = 0;
+  if (g.cs.k) {
+    const int bf = m0 / g.cs.T, bl = min(m0 + BM - 1, g.M - 1) / g.cs.T;
+    if (bf == bl) {
+      sb = bf;
+      sp0 = g.cs.start[bf] - bf * g.cs.T;
+    }
+  }
   const int nl = 4 * (lane & 15);
 #pragma unroll
   for (int pass = 0; pass < TI / 2; ++pass) {
@@ -382,7 +392,27 @@ __global__ __launch_bounds__(NWV * 64) void gemm_nt_dma(GemmArgs g) {
               f32x4{a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]};
         }
     const int n = n0 + wn0 + 64 * pass + nl;
-    if (n < g.N) {
+    if (g.cs.k && n < g.N) {
+      // expanded-cache rows: 4 columns of one head's k or v row (dn, dv multiples of 4)
+      const CacheScatter& cs = g.cs;
+      const int h = n / (cs.dn + cs.dv), j = n - h * (cs.dn + cs.dv);
+      const bool isk = j < cs.dn;
+      const int rowlen = isk ? cs.dk : cs.dv;
+      uint16_t* base = (isk ? cs.k + j : cs.v + (j - cs.dn)) + (size_t)h * cs.T_cap * rowlen;
+#pragma unroll
+      for (int k = 0; k < WM / 4; ++k) {
+        const int ml = (lane >> 4) + 4 * k;
+        const int m = m0 + wm0 + ml;
+        const f32x4 v = *(GMLA_LDS const f32x4*)(stg + ml * PITCH + nl);
+        if (m < g.M) {
+          const int b = sb >= 0 ? sb : m / cs.T;
+          const int p = sb >= 0 ? sp0 + m : cs.start[b] + (m - b * cs.T);
+          if (p >= 0 && p < cs.T_cap)
+            *(u32x2*)(base + ((size_t)b * cs.H * cs.T_cap + p) * rowlen) =
+                u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+        }
+      }
+    } else if (n < g.N) {
       // this lane's segment (a 4-column chunk never straddles one: segments start at multiples of 8)
       const GemmSeg& s0 = g.seg[0];
       char* outp = (char*)s0.out;
@@ -580,8 +610,16 @@ size_t gemm_ws_bytes(int M, int N, int K) {
   return ks > 1 ? (size_t)ks * M * N * sizeof(float) : 0;
 }
 
+bool gemm_scatter_ok(const GemmArgs& g) {
+  const CacheScatter& cs = g.cs;
+  return g.nseg == 1 && dma_gemm_ok(g, 64) && cs.k && cs.v && cs.start && cs.T > 0 && cs.T_cap > 0 && cs.H > 0 &&
+         cs.dn % 4 == 0 && cs.dv % 4 == 0 && cs.dk % 4 == 0 && cs.dn <= cs.dk && g.N == cs.H * (cs.dn + cs.dv) &&
+         ((uintptr_t)cs.k & 7) == 0 && ((uintptr_t)cs.v & 7) == 0;
+}
+
 hipError_t launch_gemm(const GemmArgs& g, void* ws, size_t ws_bytes, hipStream_t stream) {
   if (g.M <= 0 || g.N <= 0) return hipSuccess;
+  if (g.cs.k && !gemm_scatter_ok(g)) return hipErrorInvalidValue;
   if (g.M <= 32) {
     const int ks = ws ? skinny_ksplit(g.M, g.N, g.K) : 1;  // no workspace: one K split
     const int nsteps = cdiv(g.K, 16);

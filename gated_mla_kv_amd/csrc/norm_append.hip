@@ -131,7 +131,13 @@ __global__ __launch_bounds__(256) void kv_append_kernel(KvAppendArgs a) {
       st16(dst + i * 8, ld16(src));
     }
   }
-  if (a.k) {
+  if (a.k && !a.k_nope) {  // k_nope and v already in the cache (written by the kv up-projection)
+    for (int i = threadIdx.x; i < a.H * cS; i += blockDim.x) {
+      const int h = i / cS, j = i % cS;
+      uint16_t* dst = a.k + (((size_t)b * a.H + h) * a.T_cap + p) * (a.DN + a.DS) + (cN + j) * 8;
+      st16(dst, ld16(a.r + bt * a.ld_r + j * 8));
+    }
+  } else if (a.k) {
     const int per_head = cN + cS;
     for (int i = threadIdx.x; i < a.H * per_head; i += blockDim.x) {
       const int h = i / per_head, j = i % per_head;

@@ -58,6 +58,40 @@ def test_prefill_then_decode(dims, dist, B, T, steps, path):
     assert np.mean(lat_err > 0) < 0.02
 
 
+def test_prefill_expanded_cache_rows():
+    """At more than 128 token rows the kv up-projection writes k_nope and v straight into the
+    expanded cache; every written row equals, bit for bit, the same GEMM's output for the cached
+    latents (run through the stage entry point), and the shared-key part of each head's k row is the
+    cached r. Rows of positions that were not written stay untouched."""
+    d = K3
+    lw, L = _layer(d, 92, "k3")
+    B, T, T_cap = 2, 150, 200
+    starts = [0, 37]
+    cache = L.new_cache(B, T_cap, expanded=True)
+    cache.k.fill_(7)
+    cache.v.fill_(7)
+    x = make_tokens(d, B, T, seed=92)
+    L.prefill(cache, dev_bf16(x), i32(starts), max(starts) + T)
+    torch.cuda.synchronize()
+    H, dn, dv = d.n_heads, d.d_nope, d.d_v
+    lat = torch.stack([cache.latent[b, starts[b]:starts[b] + T] for b in range(B)]).reshape(B * T, -1)
+    c = lat[:, :d.kv_lora].contiguous()
+    kvb = torch.empty((B * T, H * (dn + dv)), dtype=torch.bfloat16, device="cuda")
+    gm.mla_gemm(c, d.kv_lora, L.w["w_kv_b"], B * T, H * (dn + dv), d.kv_lora, kvb, H * (dn + dv))
+    torch.cuda.synchronize()
+    kvb = kvb.reshape(B, T, H, dn + dv)
+    for b in range(B):
+        p0 = starts[b]
+        k = cache.k[b, :, p0:p0 + T]  # [H, T, dn + d_shared]
+        v = cache.v[b, :, p0:p0 + T]
+        assert torch.equal(k[..., :dn], kvb[b, :, :, :dn].transpose(0, 1)), f"k_nope b={b}"
+        assert torch.equal(v, kvb[b, :, :, dn:].transpose(0, 1)), f"v b={b}"
+        r = cache.latent[b, p0:p0 + T, d.kv_lora:]
+        assert torch.equal(k[..., dn:], r.unsqueeze(0).expand(H, -1, -1)), f"shared key b={b}"
+        # positions before this sequence's start were not written
+        assert bool((cache.k[b, :, :p0] == 7).all()) and bool((cache.v[b, :, :p0] == 7).all())
+
+
 def test_prefill_bf16_output_and_chunked_start():
     """Two prefill calls (P = 0 then P = 24) equal one 40-token prefill."""
     d = K3
