@@ -157,18 +157,21 @@ __global__ __launch_bounds__(kScoreWaves * 64) void index_scores_kernel(IndexSco
 }
 
 // Prefill rows of one sequence see nested prefixes of one index cache, so a workgroup takes 8
-// consecutive rows (one per wave) and a 256-position block of keys, staged once in LDS for all
+// consecutive rows (one per wave) and a 128-position block of keys, staged once in LDS for all
 // of them (256-byte rows, 16-byte chunk c at c ^ (row & 15); FP8 codes: 128-byte rows, chunk c
 // at c ^ (row & 7), widened when read, and the block's scales). Each wave scores its row's
 // visible positions of the block as index_scores_kernel does; the top digits go to per-row LDS
-// histograms of 16-bit counters (two bins per word: at most 256 per bin), added to the rows'
-// histograms at the end.
-constexpr int kRowsPerWg = 8, kRowBlock = 256;
+// histograms of 8-bit counters (four bins per word: at most 128 per bin), added to the rows'
+// histograms at the end. 66 KB of LDS: two workgroups per CU, so one's key loads and histogram
+// flush overlap the other's scoring.
+constexpr int kRowsPerWg = 8, kRowBlock = 128;
 
 __global__ __launch_bounds__(kRowsPerWg * 64) void index_scores_rows_kernel(IndexScoreArgs a) {
   constexpr int NIH = 32, DI = 128, KS = DI / 16;
   __shared__ __attribute__((aligned(16))) uint8_t keys_s[kRowBlock * DI * 2];
-  __shared__ uint32_t hist2[kRowsPerWg * kHistBins / 2];
+  // per-row histograms with 8-bit counters, four bins per word (a block puts at most 128 keys in a
+  // bin): with the 32 KB key block this leaves room for two workgroups per CU
+  __shared__ uint32_t hist4[kRowsPerWg * kHistBins / 4];
   __shared__ float kscale_s[kRowBlock];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g2 = lane >> 5, l32 = lane & 31;
@@ -184,7 +187,7 @@ __global__ __launch_bounds__(kRowsPerWg * 64) void index_scores_rows_kernel(Inde
   if (p0 >= t_last) return;
   const int t = b < a.B ? visible(b) : 0;
   const bool fp8 = a.idx_scale != nullptr;
-  for (int i = tid; i < kRowsPerWg * kHistBins / 2; i += kRowsPerWg * 64) hist2[i] = 0;
+  for (int i = tid; i < kRowsPerWg * kHistBins / 4; i += kRowsPerWg * 64) hist4[i] = 0;
   // the block's keys (positions past t_last repeat its last one; never scored)
   constexpr int NT = kRowsPerWg * 64;
   if (!fp8) {
@@ -248,17 +251,18 @@ __global__ __launch_bounds__(kRowsPerWg * 64) void index_scores_rows_kernel(Inde
     if (pos < t && g2 == 0) {
       a.scores[(size_t)b * a.score_stride + pos] = sc;
       const uint32_t bin = order_key(sc) >> 20;
-      atomicAdd(&hist2[wave * (kHistBins / 2) + (bin >> 1)], (bin & 1) ? 65536u : 1u);
+      atomicAdd(&hist4[wave * (kHistBins / 4) + (bin >> 2)], 1u << (8 * (bin & 3)));
     }
   }
   __syncthreads();
-  for (int i = tid; i < kRowsPerWg * kHistBins / 2; i += NT) {
-    const uint32_t w = hist2[i];
-    const int row = blockIdx.y * kRowsPerWg + i / (kHistBins / 2), bin = 2 * (i % (kHistBins / 2));
+  for (int i = tid; i < kRowsPerWg * kHistBins / 4; i += NT) {
+    const uint32_t w = hist4[i];
+    const int row = blockIdx.y * kRowsPerWg + i / (kHistBins / 4), bin = 4 * (i % (kHistBins / 4));
     if (w && row < a.B) {
       int* gh = a.hist + (size_t)row * kHistBins + bin;
-      if (w & 0xFFFFu) atomicAdd(gh, (int)(w & 0xFFFFu));
-      if (w >> 16) atomicAdd(gh + 1, (int)(w >> 16));
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if ((w >> (8 * e)) & 0xFFu) atomicAdd(gh + e, (int)((w >> (8 * e)) & 0xFFu));
     }
   }
 }
