@@ -169,6 +169,36 @@ def _oracle_row_with_selection(d, w, x_row, qt_row, latent, S):
     return y[0]
 
 
+def test_dsa_sparse_prefill_equal_prefix_keys():
+    """A prefix of 400 identical index keys: every row scores them equally, so each 128-position
+    key block puts all its positions in one histogram bin (the largest count the row-blocked
+    kernel's 8-bit counters hold), and the top-k must take the tied prefix positions lowest
+    first (the tie rule the selection uses throughout): the selected prefix positions are
+    exactly 0 .. m-1."""
+    d = K3_SMALL_TOPK
+    lw, L = _layer(d, 95, "k3")
+    B, P, T = 1, 400, 8
+    cache = L.new_cache(B, P + T + 3, expanded=False, index=True)
+    cache.latent[0, :P] = dev_bf16(make_latent_prefix(d, B, P, seed=95)[0])
+    key = make_index_prefix(d, 1, 1, seed=95)[0, 0]
+    cache.idx[0, :P] = dev_bf16(np.ascontiguousarray(np.broadcast_to(key, (P, d.d_idx))))
+    x = make_tokens(d, B, T, seed=95)
+    sel = torch.empty((B, T, d.topk), dtype=torch.int32, device="cuda")
+    cnt = torch.empty((B, T), dtype=torch.int32, device="cuda")
+    y = L.prefill_sparse(cache, dev_bf16(x), i32([P]), P + T, out_dtype=gm.OUT_F32, sel_idx=sel, sel_cnt=cnt)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(y).all())
+    sel_np, cnt_np = sel.cpu().numpy(), cnt.cpu().numpy()
+    for i in range(T):
+        t = P + i + 1
+        k = min(d.topk, t)
+        assert cnt_np[0, i] == k
+        got = sel_np[0, i, :k]
+        assert np.all(np.diff(got) > 0) and got[-1] < t
+        pre = got[got < P]
+        assert np.array_equal(pre, np.arange(len(pre))), f"row {i}: tied prefix keys not taken lowest first"
+
+
 @pytest.mark.parametrize("starts,T", [([100, 37], 150), ([0], 90)])
 def test_dsa_sparse_prefill(starts, T):
     """mla_prefill_sparse against the oracle's dsa_prefill, per sequence (ragged starts): the
