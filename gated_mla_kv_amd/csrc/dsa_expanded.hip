@@ -5,7 +5,7 @@
 // The dot products are a [32 heads x 128] . [128 x 32 positions] bf16 MFMA per wave, with the
 // index keys loaded from HBM straight into the B operand (one 16-byte load per lane and k-step,
 // 256 bytes per position, each read once; two 32-position tiles in flight per wave, eight waves
-// per 2048-position workgroup). Lane l ends with position l%32 and 16 heads, so the
+// per workgroup, chunks sized to fill the CUs once). Lane l ends with position l%32 and 16 heads, so the
 // head-weighted ReLU sum is in-lane plus one xor-32 shuffle. 1/sqrt(32*128) = 1/64 is folded
 // into a exactly. FP8 index keys (128 E4M3 codes and one scale s >= 0 per position, the blog's
 // cache section) load 8 bytes per lane and k-step, widen exactly to bf16, and the position's
