@@ -415,28 +415,22 @@ def attention_absorbed_subset(q_tilde, latent, positions, scale: float, dims):
     return o, (m + np.log(l))[:, 0]
 
 
-def dsa_decode_step(x, w, cache: Cache, dims, index_query_bf16: bool = True):
+def dsa_decode_step(x, w, cache: Cache, dims):
     """One decode token per sequence through the Gated DSA layer (the per-query pseudocode).
 
     x [B, hidden]. The main latent and the index key of the current token are appended
     first, so t includes it; scores, top-k, then sparse MLA with the main q and latent
     cache, then the gate and o_proj. Returns (y [B, hidden], extras).
 
-    With ``index_query_bf16`` the indexer's query side is held in bfloat16 (c^Q as it enters
-    W_q^I, and q^I itself) before scoring: the top-k is an integer decision taken on scores,
-    and the blog's eq. (5) leaves out the low-precision quantisation that the deployed path
-    applies to the index query (text after eq. (5)); bf16 is the precision the library's
-    kernels hold it in. The index keys are held in the index cache's bf16 either way.
+    The index score is eq. (5) as written, with no quantisation or intermediate rounding of
+    its query side: q^I comes from the float64 c^Q and a from x. The only rounding on the
+    indexer path is the index cache's storage type (bf16, or FP8 when the cache is FP8).
     """
     x = np.asarray(x, dtype=F64)
     B = x.shape[0]
     cq, q_nope, q_shared = query_path(x, w, dims)
     c, r = kv_down_path(x, w, dims)
-    if index_query_bf16:
-        qi, ki, a = index_projections(x, round_to_bf16(cq), w, dims)
-        qi = round_to_bf16(qi)
-    else:
-        qi, ki, a = index_projections(x, cq, w, dims)
+    qi, ki, a = index_projections(x, cq, w, dims)
     H = dims.n_heads
     if cache.expanded:
         k_nope, v = kv_up(cache._store(c), w, dims)
@@ -462,7 +456,7 @@ def dsa_decode_step(x, w, cache: Cache, dims, index_query_bf16: bool = True):
                "q_tilde": qt, "z": z, "u": u, "lse": np.stack(lse)}
 
 
-def dsa_prefill(x, w, cache: Cache, dims, index_query_bf16: bool = True):
+def dsa_prefill(x, w, cache: Cache, dims):
     """T new tokens per sequence through the Gated DSA layer (eq. (6) applied at every t).
 
     x [B, T, hidden]. The main latent, the index keys (and the expanded K/V when the cache
@@ -471,19 +465,15 @@ def dsa_prefill(x, w, cache: Cache, dims, index_query_bf16: bool = True):
     scores the index keys 0..P+i (eq. (5)), keeps S = TopK(I, min(k, t)) (eq. (6)) and
     attends over S only in the absorbed form (eq. (9) over S), followed by the gate and
     o_proj. Appending all T keys before scoring is the per-query pseudocode's order for every
-    token, since token i only reads positions up to its own. ``index_query_bf16`` as in
-    ``dsa_decode_step``. Returns (y [B, T, hidden], extras).
+    token, since token i only reads positions up to its own. The index score is unrounded
+    eq. (5), as in ``dsa_decode_step``. Returns (y [B, T, hidden], extras).
     """
     x = np.asarray(x, dtype=F64)
     B, T = x.shape[:2]
     P = cache.length
     cq, q_nope, q_shared = query_path(x, w, dims)
     c, r = kv_down_path(x, w, dims)
-    if index_query_bf16:
-        qi, ki, a = index_projections(x, round_to_bf16(cq), w, dims)
-        qi = round_to_bf16(qi)
-    else:
-        qi, ki, a = index_projections(x, cq, w, dims)
+    qi, ki, a = index_projections(x, cq, w, dims)
     if cache.expanded:
         k_nope, v = kv_up(cache._store(c), w, dims)
         cache.append(c, r, expand_keys(k_nope, cache._store(r)), v.transpose(0, 2, 1, 3), ki)

@@ -68,3 +68,23 @@ def brute_index_scores(qi, a, keys, t):
             acc += a[h] * (z + abs(z)) / 2.0
         out.append(acc / (math.sqrt(nh) * math.sqrt(d)))
     return out
+
+
+def brute_index_projections(x, W, dims):
+    """The indexer's projections of ONE token x (a list of hidden values), eqs. (2)-(4) of the
+    K3.1 Gated DSA blog, as scalar loops:
+      q^I: the normalised query latent c^Q (the main query path's RMSNorm with its gain) times
+           W_q^I, read head-major: q[h][e] = (W_q^I c^Q)[h * d_idx + e]          (eq. (2))
+      k^I: LayerNorm of W_k^I x with the population variance, then gain and bias    (eq. (3))
+      a:   W_a^I x, used raw (no sigmoid, no softmax)                               (eq. (4))
+    Returns (q [n_idx][d_idx], k [d_idx], a [n_idx])."""
+    nh, d = dims.n_idx_heads, dims.d_idx
+    cq = _rms(_matvec(W["w_q_a"], x), W["g_q_a"], dims.rms_eps)
+    qf = _matvec(W["w_idx_q"], cq)
+    q = [[qf[h * d + e] for e in range(d)] for h in range(nh)]
+    v = _matvec(W["w_idx_k"], x)
+    mean = sum(v) / d
+    var = sum((e - mean) * (e - mean) for e in v) / d
+    k = [(v[e] - mean) / math.sqrt(var + dims.ln_eps) * W["g_idx_k"][e] + W["b_idx_k"][e] for e in range(d)]
+    a = _matvec(W["w_idx_w"], x)
+    return q, k, a

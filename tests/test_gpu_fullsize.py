@@ -105,8 +105,7 @@ def test_dsa_prefill_T4096_selecting_rows(k3_weights):
     x = bf16_bits_to_f32(x_bits[:, :R]).astype(np.float64)
     cq, q_nope, q_shared = O.query_path(x, w64, D)
     c, r = O.kv_down_path(x, w64, D)
-    qi, ki, a = O.index_projections(x, O.round_to_bf16(cq), w64, D)
-    qi = O.round_to_bf16(qi)
+    qi, ki, a = O.index_projections(x, cq, w64, D)
     oc = O.Cache(D, 1, expanded=False)
     oc.append(c, r, idx_k=ki)
     qt = O.absorbed_query(q_nope, q_shared, w64, D)

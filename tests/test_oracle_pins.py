@@ -261,6 +261,57 @@ def test_index_scores_brute_force_relu_identity_and_scale_folding():
     np.testing.assert_array_equal(O.index_scores(qi, a, keys, 40), folded)
 
 
+def test_index_projections_match_explicit_loops():
+    """Eqs. (2)-(4) of the Gated DSA blog against scalar loops (tests/brute_force.py): q^I from
+    the normalised query latent c^Q read head-major, k^I = LayerNorm(W_k^I x) * gamma + beta,
+    a = W_a^I x raw; on the oracle's function and on what its decode step and prefill use.
+    Gains and the bias are perturbed, and each plausible slip (q^I from the un-normalised
+    latent, a transposed head reshape, RMSNorm for the LayerNorm, a dropped bias, a sigmoid on
+    a) is shown to move the result, so the pin would catch it."""
+    from brute_force import brute_index_projections
+    d = TINY_DSA
+    lw = make_layer_weights(d, seed=18, dist="fan_in", perturb_norms=True)
+    w = _weights_f64(lw)
+    Wl = {k: v.tolist() for k, v in w.items()}
+    B, T = 2, 3
+    x = _x(d, B, T, seed=18)
+    cq, _, _ = O.query_path(x, w, d)
+    qi, ki, a = O.index_projections(x, cq, w, d)
+    assert qi.shape == (B, T, d.n_idx_heads, d.d_idx) and ki.shape == (B, T, d.d_idx)
+    assert a.shape == (B, T, d.n_idx_heads)
+    ref = [[brute_index_projections(x[b, t].tolist(), Wl, d) for t in range(T)] for b in range(B)]
+    q_ref = np.array([[r[0] for r in row] for row in ref])
+    k_ref = np.array([[r[1] for r in row] for row in ref])
+    a_ref = np.array([[r[2] for r in row] for row in ref])
+    np.testing.assert_allclose(qi, q_ref, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(ki, k_ref, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(a, a_ref, rtol=1e-12, atol=1e-13)
+    # what the decode step and the prefill feed the score (no rounding of the query side)
+    y, ex = O.dsa_decode_step(x[:, 0], w, O.Cache(d, B, expanded=False), d)
+    np.testing.assert_allclose(ex["q_idx"], q_ref[:, 0], rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(ex["k_idx"], k_ref[:, 0], rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(ex["a"], a_ref[:, 0], rtol=1e-12, atol=1e-13)
+    _, exp_ = O.dsa_prefill(x, w, O.Cache(d, B, expanded=False), d)
+    np.testing.assert_allclose(exp_["q_idx"], q_ref, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(exp_["k_idx"], k_ref, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(exp_["a"], a_ref, rtol=1e-12, atol=1e-13)
+    # the slips the pin must catch all change the numbers
+    raw = x @ w["w_q_a"].T
+    slips = {
+        "q from the un-normalised latent": ((raw @ w["w_idx_q"].T).reshape(qi.shape), q_ref),
+        "q from x-side RMSNorm without the gain": (
+            ((raw / np.sqrt(np.mean(raw ** 2, -1, keepdims=True) + d.rms_eps)) @ w["w_idx_q"].T).reshape(qi.shape),
+            q_ref),
+        "q reshaped feature-major": (
+            (cq @ w["w_idx_q"].T).reshape(B, T, d.d_idx, d.n_idx_heads).swapaxes(-1, -2), q_ref),
+        "k with RMSNorm": (O.rms_norm(x @ w["w_idx_k"].T, w["g_idx_k"], d.ln_eps) + w["b_idx_k"], k_ref),
+        "k without the bias": (ki - w["b_idx_k"], k_ref),
+        "a through a sigmoid": (O.sigmoid(a), a_ref),
+    }
+    for what, (slip, good) in slips.items():
+        assert np.max(np.abs(slip - good)) > 1e-3 * np.max(np.abs(good)), what
+
+
 def test_select_topk_matches_stable_sort():
     rng = np.random.default_rng(12)
     for trial in range(200):
