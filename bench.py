@@ -125,6 +125,7 @@ def decode_benches(args, d, lw, log):
     """Decode-side configurations: batched decode (absorbed and expanded caches, and the whole
     mla_decode step), long-context absorbed decode with split-K and merge, and Gated DSA decode
     (index scores + top-k, then sparse latent attention)."""
+    import numpy as np
     import torch
 
     import gated_mla_kv_amd as gm
@@ -297,7 +298,9 @@ def decode_benches(args, d, lw, log):
     idx5 = bf16_tensor(make_index_prefix(dd, B5, nv5, seed=0), dev)
     c5 = gm.MlaCache(lat5.data_ptr(), None, None, idx5.data_ptr(), B5, nv5)
     f32 = lambda bits: torch.from_numpy((bits.astype("uint32") << 16).view("float32")).to(dev)  # noqa: E731
-    qi = bf16_tensor(normal_bf16((B5, dd.n_idx_heads, dd.d_idx), 0.5, 0, 25), dev)  # bf16, as the kernels take it
+    # the index query in fp32, as the indexer produces it (the library takes it unrounded)
+    qi = torch.from_numpy(np.random.default_rng(25).standard_normal((B5, dd.n_idx_heads, dd.d_idx))
+                          .astype(np.float32) * np.float32(0.5)).to(dev)
     wi = f32(normal_bf16((B5, dd.n_idx_heads), 1.0, 0, 26))
     n5 = torch.full((B5,), nv5, dtype=torch.int32, device=dev)
     sel = torch.empty((B5, dd.topk), dtype=torch.int32, device=dev)
@@ -404,7 +407,7 @@ def counter_pass(log):
     import torch
 
     import gated_mla_kv_amd as gm
-    from workloads import K3, device_normal_bf16
+    from workloads import K3, device_normal_bf16, device_normal_f32
 
     dev = "cuda"
     d, dd = K3.replace(n_idx_heads=0), K3
@@ -459,7 +462,7 @@ def counter_pass(log):
     B, nv = 8, 65537
     lat = device_normal_bf16((B, nv, dd.d_latent), 1.0, 9, 10)
     idx = device_normal_bf16((B, nv, dd.d_idx), 1.0, 9, 11)
-    qi = device_normal_bf16((B, dd.n_idx_heads, dd.d_idx), 0.5, 9, 12)
+    qi = device_normal_f32((B, dd.n_idx_heads, dd.d_idx), 0.5, 9, 12)
     wi = torch.ones((B, dd.n_idx_heads), device=dev)
     qt = device_normal_bf16((B, H, dd.d_latent), 0.05, 9, 13)
     c = gm.MlaCache(lat.data_ptr(), None, None, idx.data_ptr(), B, nv)

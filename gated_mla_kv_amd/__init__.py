@@ -13,7 +13,8 @@ import os
 __all__ = [
     "GmlaError", "lib", "MlaDims", "MlaWeights", "MlaCache", "make_dims", "OUT_BF16", "OUT_F32",
     "PATH_ABSORBED", "PATH_EXPANDED", "PATH_SPARSE", "status_string", "dims_supported",
-    "workspace_bytes", "workspace_bytes_prefill_sparse", "mla_prefill", "mla_prefill_sparse", "mla_decode", "kv_append", "dsa_index_topk", "mla_gemm",
+    "workspace_bytes", "workspace_bytes_prefill_sparse", "mla_prefill", "mla_prefill_sparse", "mla_decode",
+    "kv_append", "dsa_index_topk", "dsa_index_topk_fp8", "mla_index_projections", "mla_gemm",
     "mla_rmsnorm", "mla_layernorm", "mla_prefill_attention", "mla_absorb_query",
     "mla_decode_attention", "mla_sparse_attention", "mla_expanded_attention", "mla_value_up_gate",
     "LIB_PATH",
@@ -67,7 +68,8 @@ _SIGS = {
     "mla_workspace_bytes_ex": (_SZ, [_P, _I, _I, _I, _I, _I]),
     "mla_prefill": (ctypes.c_int, [_P, _P, _P, _P, _I, _P, _I, _I, _P, _I, _P, _P, _SZ, _P]),
     "mla_workspace_bytes_prefill_sparse": (_SZ, [_P, _I, _I, _I]),
-    "mla_prefill_sparse": (ctypes.c_int, [_P, _P, _P, _P, _I, _P, _I, _I, _P, _I, _P, _P, _P, _SZ, _P]),
+    "mla_prefill_sparse": (ctypes.c_int, [_P, _P, _P, _P, _I, _P, _I, _I, _P, _I, _P, _P, _P, _P, _SZ, _P]),
+    "mla_index_projections": (ctypes.c_int, [_P, _P, _P, _I, _P, _P, _P, _P, _SZ, _P]),
     "mla_decode": (ctypes.c_int, [_P, _P, _P, _P, _I, _P, _I, _I, _I, _P, _P, _P, _I, _P, _SZ, _P]),
     "kv_append": (ctypes.c_int, [_P, _P, _P, _I, _I, _I, _P, _P, _P, _P, _P, _P]),
     "dsa_index_topk": (ctypes.c_int, [_P, _P, _P, _P, _I, _P, _I, _I, _P, _P, _P, _P, _SZ, _P]),
@@ -165,12 +167,18 @@ def workspace_bytes_prefill_sparse(dims: MlaDims, B: int, T: int, max_end: int) 
 
 
 def mla_prefill_sparse(dims, weights: MlaWeights, cache: MlaCache, start_pos, max_end, x, B, T, y,
-                       out_dtype=OUT_BF16, sel_idx=None, sel_cnt=None, ws=None, stream=None):
+                       out_dtype=OUT_BF16, sel_idx=None, sel_cnt=None, ws=None, stream=None, scores=None):
     wp, wn = _ws(ws)
     _check(lib().mla_prefill_sparse(ctypes.byref(dims), ctypes.byref(weights), ctypes.byref(cache),
                                     _p(start_pos), max_end, _p(x), B, T, _p(y), out_dtype, _p(sel_idx),
-                                    _p(sel_cnt), wp, wn, _stream(stream)),
+                                    _p(sel_cnt), _p(scores), wp, wn, _stream(stream)),
            "mla_prefill_sparse")
+
+
+def mla_index_projections(dims, weights: MlaWeights, x, M, q_idx, w_idx, k_idx, ws=None, stream=None):
+    wp, wn = _ws(ws)
+    _check(lib().mla_index_projections(ctypes.byref(dims), ctypes.byref(weights), _p(x), M, _p(q_idx), _p(w_idx),
+                                       _p(k_idx), wp, wn, _stream(stream)), "mla_index_projections")
 
 
 def mla_decode(dims, weights: MlaWeights, cache: MlaCache, seq_len, max_len, x, B, path, y,

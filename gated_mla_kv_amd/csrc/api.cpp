@@ -67,13 +67,14 @@ struct Ws {
   float* xc;       // [M, kv_lora]  latent before its norm
   uint16_t* r;     // [M, d_shared] shared key
   float* gpre;     // [M, H*d_v]    gate pre-activation (fp32)
-  float* kpre;     // [M, d_idx]    index key before its LayerNorm
+  double* kpart;   // [splits, M, d_idx]  index-key split-K partial sums (fp64)
   float* aw;       // [M, n_idx]    index head weights
-  uint16_t* cq;    // [M, q_lora]
+  uint16_t* cq;    // [M, ldcq]     normalised query latent: bf16 hi, then (DSA) bf16 lo
+  int ldcq;        // q_lora, or 2 q_lora with the indexer (the split operand of the q^I GEMM)
   uint16_t* c;     // [M, kv_lora]
   uint16_t* kidx;  // [M, d_idx]
   uint16_t* q;     // [M, H*(d_nope+d_shared)]
-  uint16_t* qidx;  // [M, n_idx*d_idx]
+  float* qidx;     // [M, n_idx*d_idx]  index query (fp32)
   uint16_t* kv;    // [M, H*(d_nope+d_v)]
   uint16_t* u;     // [M, H*d_v]
   uint16_t* qt;    // [M, H, kv_lora+d_shared]   (decode)
@@ -99,13 +100,14 @@ Ws carve(const mla_dims* d, int M, bool decode, int max_len, int path, int split
   w.xc = cv.take<float>((size_t)M * d->kv_lora);
   w.r = cv.take<uint16_t>((size_t)M * d->d_shared);
   w.gpre = cv.take<float>((size_t)M * H * d->d_v);
-  w.kpre = cv.take<float>(dsa ? (size_t)M * d->d_idx : 0);
+  w.kpart = cv.take<double>(dsa ? (size_t)index_key_splits(M, d->hidden) * M * d->d_idx : 0);
   w.aw = cv.take<float>(dsa ? (size_t)M * d->n_idx_heads : 0);
-  w.cq = cv.take<uint16_t>((size_t)M * d->q_lora);
+  w.ldcq = dsa ? 2 * d->q_lora : d->q_lora;
+  w.cq = cv.take<uint16_t>((size_t)M * w.ldcq);
   w.c = cv.take<uint16_t>((size_t)M * d->kv_lora);
   w.kidx = cv.take<uint16_t>(dsa ? (size_t)M * d->d_idx : 0);
   w.q = cv.take<uint16_t>((size_t)M * H * dqk);
-  w.qidx = cv.take<uint16_t>(dsa ? (size_t)M * d->n_idx_heads * d->d_idx : 0);
+  w.qidx = cv.take<float>(dsa ? (size_t)M * d->n_idx_heads * d->d_idx : 0);
   w.kv = cv.take<uint16_t>((size_t)M * H * (d->d_nope + d->d_v));
   w.u = cv.take<uint16_t>((size_t)M * H * d->d_v);
   if (decode) {
@@ -124,11 +126,11 @@ Ws carve(const mla_dims* d, int M, bool decode, int max_len, int path, int split
   }
   // split-K partials of the small-M GEMMs (the largest of the layer's GEMMs)
   size_t g = 0;
-  const int Nx = d->q_lora + d->kv_lora + d->d_shared + H * d->d_v + (dsa ? d->d_idx + d->n_idx_heads : 0);
-  const int Nq = H * dqk + (dsa ? d->n_idx_heads * d->d_idx : 0);
-  const size_t cand[4] = {gemm_ws_bytes(M, Nx, d->hidden), gemm_ws_bytes(M, Nq, d->q_lora),
+  const int Nx = d->q_lora + d->kv_lora + d->d_shared + H * d->d_v + (dsa ? d->n_idx_heads : 0);
+  const size_t cand[5] = {gemm_ws_bytes(M, Nx, d->hidden), gemm_ws_bytes(M, H * dqk, d->q_lora),
                           gemm_ws_bytes(M, H * (d->d_nope + d->d_v), d->kv_lora),
-                          gemm_ws_bytes(M, d->hidden, H * d->d_v)};
+                          gemm_ws_bytes(M, d->hidden, H * d->d_v),
+                          dsa ? gemm_ws_bytes(M, d->n_idx_heads * d->d_idx, d->q_lora) : 0};
   for (size_t c : cand) g = c > g ? c : g;
   w.gemm_ws_bytes = g;
   w.gemm_ws = g ? cv.take<char>(g) : nullptr;
@@ -167,7 +169,7 @@ void push(GemmArgs& g, GemmSeg s) {
   g.N = s.n1;
 }
 
-// x -> [q_a | latent | shared key | gate | index key | index weights] in one GEMM (x read once).
+// x -> [q_a | latent | shared key | gate | index head weights] in one GEMM (x read once).
 int run_x_gemm(const mla_dims* d, const mla_weights* w, const void* x, int M, const Ws& ws,
                bool with_idx, hipStream_t st) {
   GemmArgs g = gemm_args(x, d->hidden, M, d->hidden);
@@ -177,11 +179,43 @@ int run_x_gemm(const mla_dims* d, const mla_weights* w, const void* x, int M, co
   push(g, seg((const uint16_t*)w->w_kv_a + (size_t)d->kv_lora * d->hidden, d->d_shared, ws.r,
               d->d_shared, false, n));
   if (d->use_gate) push(g, seg(w->w_g, d->n_heads * d->d_v, ws.gpre, d->n_heads * d->d_v, true, n));
-  if (with_idx) {
-    push(g, seg(w->w_idx_k, d->d_idx, ws.kpre, d->d_idx, true, n));
-    push(g, seg(w->w_idx_w, d->n_idx_heads, ws.aw, d->n_idx_heads, true, n));
-  }
+  if (with_idx) push(g, seg(w->w_idx_w, d->n_idx_heads, ws.aw, d->n_idx_heads, true, n));
   CHECK_HIP(launch_gemm(g, ws.gemm_ws, ws.gemm_ws_bytes, st));
+  return MLA_OK;
+}
+
+// The projections of M new tokens (everything the attention and the indexer read, before any
+// cache append): the x-GEMM, the two RMSNorms, q = c^Q W_qb^T and, with the indexer,
+//   q^I = c^Q W_q^I^T in fp32 ([DSA] eq. (2)): c^Q (fp32 after its RMSNorm) enters the GEMM as a
+//         bf16 hi + lo pair (GemmArgs::a_split), when idx_query;
+//   a   = x W_a^I^T in fp32 ([DSA] eq. (4)), a segment of the x-GEMM;
+//   k^I = bf16(LayerNorm(x W_k^I^T) * gain + bias) computed in fp64 ([DSA] eq. (3)).
+int run_projections(const mla_dims* d, const mla_weights* w, const void* x, int M, const Ws& wsp,
+                    bool with_idx, bool idx_query, hipStream_t st) {
+  const int H = d->n_heads, dqk = d->d_nope + d->d_shared;
+  int rc = run_x_gemm(d, w, x, M, wsp, with_idx, st);
+  if (rc) return rc;
+  CHECK_HIP(launch_rmsnorm(wsp.xq, d->q_lora, (const uint16_t*)w->g_q_a, M, d->q_lora, d->rms_eps, wsp.cq,
+                           wsp.ldcq, idx_query ? wsp.cq + d->q_lora : nullptr, st));
+  CHECK_HIP(launch_rmsnorm(wsp.xc, d->kv_lora, (const uint16_t*)w->g_kv_a, M, d->kv_lora, d->rms_eps, wsp.c,
+                           d->kv_lora, nullptr, st));
+  {
+    GemmArgs g = gemm_args(wsp.cq, wsp.ldcq, M, d->q_lora);
+    int n = 0;
+    push(g, seg(w->w_q_b, H * dqk, wsp.q, H * dqk, false, n));
+    CHECK_HIP(launch_gemm(g, wsp.gemm_ws, wsp.gemm_ws_bytes, st));
+  }
+  if (idx_query) {
+    GemmArgs g = gemm_args(wsp.cq, wsp.ldcq, M, d->q_lora);
+    g.a_split = 1;
+    int n = 0;
+    push(g, seg(w->w_idx_q, d->n_idx_heads * d->d_idx, wsp.qidx, d->n_idx_heads * d->d_idx, true, n));
+    CHECK_HIP(launch_gemm(g, wsp.gemm_ws, wsp.gemm_ws_bytes, st));
+  }
+  if (with_idx)
+    CHECK_HIP(launch_index_key_f64((const uint16_t*)x, d->hidden, (const uint16_t*)w->w_idx_k,
+                                   (const uint16_t*)w->g_idx_k, (const uint16_t*)w->b_idx_k, M, d->hidden,
+                                   (double)d->ln_eps, wsp.kpart, wsp.kidx, d->d_idx, st));
   return MLA_OK;
 }
 
@@ -320,7 +354,7 @@ int mla_rmsnorm(const float* x, int32_t ldx, const void* gain, int32_t M, int32_
   if (M == 0 || N == 0) return MLA_OK;
   if (!x || !gain || !out) return MLA_ERR_NULL;
   if (N % 4 != 0 || ldx < N || ldx % 4 != 0 || ldo < N || ldo % 4 != 0) return MLA_ERR_SHAPE;
-  CHECK_HIP(launch_rmsnorm(x, ldx, (const uint16_t*)gain, M, N, eps, (uint16_t*)out, ldo, stream));
+  CHECK_HIP(launch_rmsnorm(x, ldx, (const uint16_t*)gain, M, N, eps, (uint16_t*)out, ldo, nullptr, stream));
   return MLA_OK;
 }
 
@@ -477,6 +511,27 @@ int mla_value_up_gate(const mla_dims* d, const float* o_latent, const void* w_kv
   return MLA_OK;
 }
 
+int mla_index_projections(const mla_dims* d, const mla_weights* w, const void* x, int32_t M, float* q_idx,
+                          float* w_idx, void* k_idx, void* ws, size_t ws_bytes, hipStream_t stream) {
+  Shape s;
+  if (!d) return MLA_ERR_NULL;
+  if (!shape_of(d, &s)) return MLA_ERR_UNSUPPORTED;
+  if (!has_dsa(d)) return MLA_ERR_UNSUPPORTED;
+  if (M < 0) return MLA_ERR_SHAPE;
+  if (M == 0) return MLA_OK;
+  int rc = check_weights(d, w);
+  if (rc) return rc;
+  if (!idx_weights(w) || !w->w_idx_q) return MLA_ERR_NULL;
+  if (!x || !q_idx || !w_idx || !k_idx || !ws) return MLA_ERR_NULL;
+  // the workspace of a sparse decode step of M sequences, which runs these same launches
+  Ws wsp = carve(d, M, true, 1, MLA_PATH_SPARSE, auto_splits(M, d->topk, 0), ws);
+  if (wsp.total > ws_bytes) return MLA_ERR_WORKSPACE;
+  wsp.qidx = q_idx;
+  wsp.aw = w_idx;
+  wsp.kidx = (uint16_t*)k_idx;
+  return run_projections(d, w, x, M, wsp, true, true, stream);
+}
+
 int kv_append(const mla_dims* d, const mla_cache* cache, const int32_t* pos, int32_t max_end,
               int32_t B, int32_t T, const void* c, const void* r, const void* k_nope, const void* v,
               const void* idx_k, hipStream_t stream) {
@@ -518,7 +573,7 @@ int kv_append(const mla_dims* d, const mla_cache* cache, const int32_t* pos, int
   return MLA_OK;
 }
 
-static int index_topk_common(const mla_dims* d, const void* q_idx, const float* w_idx,
+static int index_topk_common(const mla_dims* d, const float* q_idx, const float* w_idx,
                              const void* idx_k_cache, const float* idx_k_scales, int32_t T_cap,
                              const int32_t* n_visible, int32_t max_visible, int32_t B, int32_t* out_idx,
                              int32_t* out_cnt, float* out_scores, void* ws, size_t ws_bytes,
@@ -542,7 +597,7 @@ static int index_topk_common(const mla_dims* d, const void* q_idx, const float* 
   int32_t* scratch = cv.take<int32_t>(index_topk_scratch_words(B, stride));
   if (cv.off > ws_bytes) return MLA_ERR_WORKSPACE;
   IndexScoreArgs sa{};
-  sa.q_idx = (const uint16_t*)q_idx;
+  sa.q_idx = q_idx;
   sa.w_idx = w_idx;
   sa.idx_k = (const uint16_t*)idx_k_cache;
   sa.idx_scale = idx_k_scales;
@@ -565,7 +620,7 @@ static int index_topk_common(const mla_dims* d, const void* q_idx, const float* 
   return MLA_OK;
 }
 
-int dsa_index_topk(const mla_dims* d, const void* q_idx, const float* w_idx, const void* idx_k_cache,
+int dsa_index_topk(const mla_dims* d, const float* q_idx, const float* w_idx, const void* idx_k_cache,
                    int32_t T_cap, const int32_t* n_visible, int32_t max_visible, int32_t B,
                    int32_t* out_idx, int32_t* out_cnt, float* out_scores, void* ws, size_t ws_bytes,
                    hipStream_t stream) {
@@ -573,7 +628,7 @@ int dsa_index_topk(const mla_dims* d, const void* q_idx, const float* w_idx, con
                            out_idx, out_cnt, out_scores, ws, ws_bytes, stream);
 }
 
-int dsa_index_topk_fp8(const mla_dims* d, const void* q_idx, const float* w_idx, const void* idx_k_codes,
+int dsa_index_topk_fp8(const mla_dims* d, const float* q_idx, const float* w_idx, const void* idx_k_codes,
                        const float* idx_k_scales, int32_t T_cap, const int32_t* n_visible,
                        int32_t max_visible, int32_t B, int32_t* out_idx, int32_t* out_cnt,
                        float* out_scores, void* ws, size_t ws_bytes, hipStream_t stream) {
@@ -592,21 +647,10 @@ int dsa_index_topk_fp8(const mla_dims* d, const void* q_idx, const float* w_idx,
 static int prefill_front(const mla_dims* d, const mla_weights* w, const mla_cache* cache,
                          const int32_t* start_pos, const void* x, int B, int T, const Ws& wsp, bool with_idx,
                          bool idx_query, hipStream_t stream) {
-  const int M = B * T, H = d->n_heads, dqk = d->d_nope + d->d_shared;
+  const int M = B * T, H = d->n_heads;
   const bool expanded_cache = cache->k && cache->v;
-  int rc = run_x_gemm(d, w, x, M, wsp, with_idx, stream);
+  int rc = run_projections(d, w, x, M, wsp, with_idx, idx_query, stream);
   if (rc) return rc;
-  CHECK_HIP(launch_rmsnorm(wsp.xq, d->q_lora, (const uint16_t*)w->g_q_a, M, d->q_lora, d->rms_eps, wsp.cq,
-                           d->q_lora, stream));
-  CHECK_HIP(launch_rmsnorm(wsp.xc, d->kv_lora, (const uint16_t*)w->g_kv_a, M, d->kv_lora, d->rms_eps, wsp.c,
-                           d->kv_lora, stream));
-  {
-    GemmArgs g = gemm_args(wsp.cq, d->q_lora, M, d->q_lora);
-    int n = 0;
-    push(g, seg(w->w_q_b, H * dqk, wsp.q, H * dqk, false, n));
-    if (idx_query) push(g, seg(w->w_idx_q, d->n_idx_heads * d->d_idx, wsp.qidx, d->n_idx_heads * d->d_idx, false, n));
-    CHECK_HIP(launch_gemm(g, wsp.gemm_ws, wsp.gemm_ws_bytes, stream));
-  }
   // the kv up-projection writes k_nope and v straight into the expanded cache when its large-M
   // kernel runs (kv_append then adds the shared-key part of each head's k row); otherwise it
   // writes them to the workspace for kv_append to copy
@@ -623,9 +667,6 @@ static int prefill_front(const mla_dims* d, const mla_weights* w, const mla_cach
     }
     CHECK_HIP(launch_gemm(g, wsp.gemm_ws, wsp.gemm_ws_bytes, stream));
   }
-  if (with_idx)
-    CHECK_HIP(launch_layernorm(wsp.kpre, d->d_idx, (const uint16_t*)w->g_idx_k, (const uint16_t*)w->b_idx_k, M,
-                               d->d_idx, d->ln_eps, wsp.kidx, d->d_idx, stream));
   KvAppendArgs a = append_args(d, cache, start_pos, B, T);
   a.c = wsp.c;
   a.ld_c = d->kv_lora;
@@ -752,7 +793,8 @@ size_t mla_workspace_bytes_prefill_sparse(const mla_dims* d, int32_t B, int32_t 
 
 int mla_prefill_sparse(const mla_dims* d, const mla_weights* w, const mla_cache* cache, const int32_t* start_pos,
                        int32_t max_end, const void* x, int32_t B, int32_t T, void* y, int32_t out_dtype,
-                       int32_t* sel_idx, int32_t* sel_cnt, void* ws, size_t ws_bytes, hipStream_t stream) {
+                       int32_t* sel_idx, int32_t* sel_cnt, float* scores, void* ws, size_t ws_bytes,
+                       hipStream_t stream) {
   Shape s;
   if (!d) return MLA_ERR_NULL;
   if (!shape_of(d, &s)) return MLA_ERR_UNSUPPORTED;
@@ -791,12 +833,13 @@ int mla_prefill_sparse(const mla_dims* d, const mla_weights* w, const mla_cache*
     sa.B = n;
     sa.T_cap = cache->T_cap;
     sa.scale = 1.0f / sqrtf((float)(d->n_idx_heads * d->d_idx));
-    sa.scores = sw.scores;
+    float* row_scores = scores ? scores + (size_t)r0 * max_end : sw.scores;
+    sa.scores = row_scores;
     sa.score_stride = max_end;
     sa.row0 = r0;
     sa.rows_per_seq = T;
     TopkArgs ta{};
-    ta.scores = sw.scores;
+    ta.scores = row_scores;
     ta.score_stride = max_end;
     ta.n_vis = start_pos;
     ta.vis_offset = 1;
@@ -870,28 +913,14 @@ int mla_decode(const mla_dims* d, const mla_weights* w, const mla_cache* cache, 
   if (wsp.total > ws_bytes) return MLA_ERR_WORKSPACE;
 
   // projections of the new token
-  rc = run_x_gemm(d, w, x, B, wsp, with_idx, stream);
+  rc = run_projections(d, w, x, B, wsp, with_idx, sparse, stream);
   if (rc) return rc;
-  CHECK_HIP(launch_rmsnorm(wsp.xq, d->q_lora, (const uint16_t*)w->g_q_a, B, d->q_lora, d->rms_eps, wsp.cq,
-                           d->q_lora, stream));
-  CHECK_HIP(launch_rmsnorm(wsp.xc, d->kv_lora, (const uint16_t*)w->g_kv_a, B, d->kv_lora, d->rms_eps, wsp.c,
-                           d->kv_lora, stream));
-  {
-    GemmArgs g = gemm_args(wsp.cq, d->q_lora, B, d->q_lora);
-    int n = 0;
-    push(g, seg(w->w_q_b, H * dqk, wsp.q, H * dqk, false, n));
-    if (sparse) push(g, seg(w->w_idx_q, d->n_idx_heads * d->d_idx, wsp.qidx, d->n_idx_heads * d->d_idx, false, n));
-    CHECK_HIP(launch_gemm(g, wsp.gemm_ws, wsp.gemm_ws_bytes, stream));
-  }
   if (expanded_cache) {
     GemmArgs g = gemm_args(wsp.c, d->kv_lora, B, d->kv_lora);
     int n = 0;
     push(g, seg(w->w_kv_b, H * (d->d_nope + d->d_v), wsp.kv, H * (d->d_nope + d->d_v), false, n));
     CHECK_HIP(launch_gemm(g, wsp.gemm_ws, wsp.gemm_ws_bytes, stream));
   }
-  if (with_idx)
-    CHECK_HIP(launch_layernorm(wsp.kpre, d->d_idx, (const uint16_t*)w->g_idx_k, (const uint16_t*)w->b_idx_k, B,
-                               d->d_idx, d->ln_eps, wsp.kidx, d->d_idx, stream));
   // append the new token to every cache present, before attending (it sees itself)
   {
     KvAppendArgs a = append_args(d, cache, seq_len, B, 1);

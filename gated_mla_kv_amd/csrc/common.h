@@ -34,6 +34,16 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
 }
 __device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+// Eight fp32 values as two bf16 MFMA operands: hi = bf16(f) (nearest even) and lo = bf16(f - hi).
+// f - hi is exact in fp32 and lo rounds it with error <= 2^-9 |f - hi| <= 2^-18 |f|, so an MFMA
+// pair hi.b + lo.b carries f to about 17 bits, with every product exact.
+__device__ __forceinline__ void split_bf16x8(const float* f, uint32_t* hi, uint32_t* lo) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    hi[i] = pack_bf16x2(f[2 * i], f[2 * i + 1]);
+    lo[i] = pack_bf16x2(f[2 * i] - lo_bf16(hi[i]), f[2 * i + 1] - hi_bf16(hi[i]));
+  }
+}
 typedef _Float16 f16x2_ __attribute__((ext_vector_type(2)));
 // two floats -> packed fp16 pair, round to nearest even (lo in bits 0..15)
 __device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {

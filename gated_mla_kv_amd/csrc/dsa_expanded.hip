@@ -2,6 +2,9 @@
 //
 // index_scores_kernel (K3.1 Gated DSA blog, eq. (5)):
 //   I[b, s] = (1/sqrt(n_idx d_idx)) sum_h a[b,h] ReLU(q^I[b,h] . k^I[b,s]),  s < t
+// The query q^I is fp32, as eq. (5) leaves it unrounded: each of its values enters the MFMA as a
+// bf16 pair hi + lo (split_bf16x8), so a key tile takes two MFMAs per k-step on the same keys and
+// the dot products carry the query to about 17 bits (fp32 accumulation, exact products).
 // The dot products are a [32 heads x 128] . [128 x 32 positions] bf16 MFMA per wave, with the
 // index keys loaded from HBM straight into the B operand (one 16-byte load per lane and k-step,
 // 256 bytes per position, each read once; two 32-position tiles in flight per wave, eight waves
@@ -99,11 +102,22 @@ __global__ __launch_bounds__(kScoreWaves * 64) void index_scores_kernel(IndexSco
       ks = 1.f;
     }
   };
-  // A operand (loaded before the keys, whose loads then stay in flight past its wait): q^I rows (heads) for this lane's head l32
-  u32x4 qa[KS];
-  const uint16_t* qrow = a.q_idx + ((size_t)b * NIH + l32) * DI;
+  // A operand (loaded before the keys, whose loads then stay in flight past its wait): q^I of
+  // this lane's head l32 as bf16 hi + lo pairs
+  u32x4 qa[KS], ql[KS];
+  {
+    const float* qrow = a.q_idx + ((size_t)b * NIH + l32) * DI;
 #pragma unroll
-  for (int s = 0; s < KS; ++s) qa[s] = ld16(qrow + s * 16 + g2 * 8);
+    for (int s = 0; s < KS; ++s) {
+      float f[8];
+      *(u32x4*)&f[0] = ld16(qrow + s * 16 + g2 * 8);
+      *(u32x4*)&f[4] = ld16(qrow + s * 16 + g2 * 8 + 4);
+      uint32_t h[4], l[4];
+      split_bf16x8(f, h, l);
+      qa[s] = u32x4{h[0], h[1], h[2], h[3]};
+      ql[s] = u32x4{l[0], l[1], l[2], l[3]};
+    }
+  }
   // head weights of the 16 heads this lane's accumulators hold: (r/4)*8 + g2*4 + r%4
   float wgt[16];
 #pragma unroll
@@ -120,12 +134,18 @@ __global__ __launch_bounds__(kScoreWaves * 64) void index_scores_kernel(IndexSco
       for (int s = 0; s < KS; s += 2) {
         const u32x2 a0 = e4m3x4_to_bf16(kf[s].x), a1 = e4m3x4_to_bf16(kf[s].y);
         const u32x2 b0 = e4m3x4_to_bf16(kf[s].z), b1 = e4m3x4_to_bf16(kf[s].w);
-        acc = mfma32(qa[s], u32x4{a0.x, a0.y, a1.x, a1.y}, acc);
-        acc = mfma32(qa[s + 1], u32x4{b0.x, b0.y, b1.x, b1.y}, acc);
+        const u32x4 k0 = u32x4{a0.x, a0.y, a1.x, a1.y}, k1 = u32x4{b0.x, b0.y, b1.x, b1.y};
+        acc = mfma32(qa[s], k0, acc);
+        acc = mfma32(ql[s], k0, acc);
+        acc = mfma32(qa[s + 1], k1, acc);
+        acc = mfma32(ql[s + 1], k1, acc);
       }
     } else {
 #pragma unroll
-      for (int s = 0; s < KS; ++s) acc = mfma32(qa[s], kf[s], acc);
+      for (int s = 0; s < KS; ++s) {
+        acc = mfma32(qa[s], kf[s], acc);
+        acc = mfma32(ql[s], kf[s], acc);
+      }
     }
     float sc = 0.f;
 #pragma unroll
@@ -217,12 +237,20 @@ __global__ __launch_bounds__(kRowsPerWg * 64) void index_scores_rows_kernel(Inde
     for (int i = tid; i < kRowBlock; i += NT)
       kscale_s[i] = a.idx_scale[cache_row(a.pages, a.T_cap, seq, min(p0 + i, t_last - 1))];
   }
-  u32x4 qa[KS];
+  u32x4 qa[KS], ql[KS];  // q^I as bf16 hi + lo pairs, as in index_scores_kernel
   float wgt[16];
   if (b < a.B) {
-    const uint16_t* qrow = a.q_idx + ((size_t)b * NIH + l32) * DI;
+    const float* qrow = a.q_idx + ((size_t)b * NIH + l32) * DI;
 #pragma unroll
-    for (int s = 0; s < KS; ++s) qa[s] = ld16(qrow + s * 16 + g2 * 8);
+    for (int s = 0; s < KS; ++s) {
+      float f[8];
+      *(u32x4*)&f[0] = ld16(qrow + s * 16 + g2 * 8);
+      *(u32x4*)&f[4] = ld16(qrow + s * 16 + g2 * 8 + 4);
+      uint32_t h[4], l[4];
+      split_bf16x8(f, h, l);
+      qa[s] = u32x4{h[0], h[1], h[2], h[3]};
+      ql[s] = u32x4{l[0], l[1], l[2], l[3]};
+    }
 #pragma unroll
     for (int r = 0; r < 16; ++r) wgt[r] = a.w_idx[(size_t)b * NIH + (r >> 2) * 8 + g2 * 4 + (r & 3)] * a.scale;
   }
@@ -235,12 +263,17 @@ __global__ __launch_bounds__(kRowsPerWg * 64) void index_scores_rows_kernel(Inde
       for (int s = 0; s < KS; ++s) {
         const u32x2 w = ld8(keys_s + r * 128 + ((s ^ (r & 7)) << 4) + g2 * 8);
         const u32x2 lo = e4m3x4_to_bf16(w.x), hi = e4m3x4_to_bf16(w.y);
-        acc = mfma32(qa[s], u32x4{lo.x, lo.y, hi.x, hi.y}, acc);
+        const u32x4 kv = u32x4{lo.x, lo.y, hi.x, hi.y};
+        acc = mfma32(qa[s], kv, acc);
+        acc = mfma32(ql[s], kv, acc);
       }
     } else {
 #pragma unroll
-      for (int s = 0; s < KS; ++s)
-        acc = mfma32(qa[s], ld16(keys_s + r * 256 + (((2 * s + g2) ^ (r & 15)) << 4)), acc);
+      for (int s = 0; s < KS; ++s) {
+        const u32x4 kv = ld16(keys_s + r * 256 + (((2 * s + g2) ^ (r & 15)) << 4));
+        acc = mfma32(qa[s], kv, acc);
+        acc = mfma32(ql[s], kv, acc);
+      }
     }
     float sc = 0.f;
 #pragma unroll

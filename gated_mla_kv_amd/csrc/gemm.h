@@ -32,12 +32,16 @@ struct CacheScatter {
 };
 
 struct GemmArgs {
-  const uint16_t* a;  // [M, lda], first K columns used
+  const uint16_t* a;  // [M, lda], first K columns used (2K with a_split)
   int lda;
-  int M, N, K;        // N = n1 of the last segment
+  int M, N, K;        // N = n1 of the last segment; K = weight row length
   int nseg;
   GemmSeg seg[kMaxSegs];
   CacheScatter cs;
+  // Split operand: row m of a holds K bf16 values a_hi then K values a_lo (an fp32 activation
+  // written as hi + lo), and out = (a_hi + a_lo) . w^T, both products accumulated in fp32. The
+  // weight is read once per k step and used by two MFMAs. Needs K % 256 == 0 and lda >= 2K.
+  int a_split;
 };
 
 // Workspace bytes the launcher may use (split-K partial sums for small M).

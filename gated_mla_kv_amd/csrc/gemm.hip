@@ -113,13 +113,16 @@ __global__ __launch_bounds__(256) void gemm_nt_big(GemmArgs g) {
   }
 
   u32x4 ra[CA], rb[CB];
+  // split operand: A columns K..2K-1 (the lo half) meet the weight columns 0..K-1 again
+  const int KA = g.a_split ? 2 * g.K : g.K;
   auto load_tile = [&](int k0) {
-    const bool kin = k0 + kc < g.K;
+    const int kw = k0 >= g.K ? k0 - g.K : k0;
+    const bool kin = kw + kc < g.K;
 #pragma unroll
     for (int i = 0; i < CA; ++i)
       ra[i] = (kin && ((a_ok >> i) & 1u)) ? ld16(pa0 + i * a_step + k0) : zero16();
 #pragma unroll
-    for (int i = 0; i < CB; ++i) rb[i] = (kin && pb[i]) ? ld16(pb[i] + k0) : zero16();
+    for (int i = 0; i < CB; ++i) rb[i] = (kin && pb[i]) ? ld16(pb[i] + kw) : zero16();
   };
   auto store_tile = [&](int buf) {
 #pragma unroll
@@ -135,7 +138,7 @@ __global__ __launch_bounds__(256) void gemm_nt_big(GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x16{};
 
-  const int KT = cdiv(g.K, BK);
+  const int KT = g.a_split ? cdiv(KA, BK) : cdiv(g.K, BK);
   load_tile(0);
   store_tile(0);
   __syncthreads();
@@ -281,17 +284,19 @@ __global__ __launch_bounds__(NWV * 64) void gemm_nt_dma(GemmArgs g) {
   }
   const uint32_t smem0 = lds_addr(smem);
   const uint32_t dst0 = smem0 + iw * LOADS_W * 1024;
-  const int KT = g.K / BK;
+  const int KTW = g.K / BK;                    // weight slabs
+  const int KT = g.a_split ? 2 * KTW : KTW;    // operand slabs: the lo half follows the hi half
 
   auto issue = [&](int kt) __attribute__((always_inline)) {
     if (wave >= NIW) return;
     const uint32_t sa = dst0 + (kt % NST) * STAGE;
     const int k0b = kt * BK * 2;
+    const int kw0b = (kt < KTW ? kt : kt - KTW) * BK * 2;
 #pragma unroll
     for (int k = 0; k < LOADS_W; ++k) lds_dma16_sbase(aoffs[k], abase + k0b, sa + k * 1024);
 #pragma unroll
     for (int k = 0; k < LOADS_W; ++k)
-      lds_dma16_sbase(woff[(iw * LOADS_W + k) & 1], wbase[k] + k0b, sa + ABYTES + k * 1024);
+      lds_dma16_sbase(woff[(iw * LOADS_W + k) & 1], wbase[k] + kw0b, sa + ABYTES + k * 1024);
   };
 
   // ---- fragment addresses: row 32b + (lane % 32) of a region, chunk (2s + lane/32) ^ f(row)
@@ -447,6 +452,7 @@ __global__ __launch_bounds__(NWV * 64) void gemm_nt_dma(GemmArgs g) {
 static bool dma_gemm_ok(const GemmArgs& g, int BK) {
   const int rpl = 1024 / (2 * BK);
   if (g.M <= 128 || g.K % BK != 0 || g.lda % 8 != 0 || g.N % rpl != 0 || g.N < rpl) return false;
+  if (g.lda < (g.a_split ? 2 * g.K : g.K)) return false;
   for (int i = 0; i < g.nseg; ++i) {
     const GemmSeg& s = g.seg[i];
     if (s.n0 % rpl != 0 || s.ldo % 4 != 0) return false;
@@ -515,8 +521,12 @@ __global__ __launch_bounds__(256) void gemm_nt_skinny(GemmArgs g, float* partial
 // chunk's MFMAs.
 constexpr int kSkChunk = 256, kSkXPitch = kSkChunk + 8;  // LDS row pitch (bf16): no bank-aligned rows
 
+// SPLIT: the split operand (GemmArgs::a_split): each chunk stages the hi and the lo activations
+// and every weight fragment feeds two MFMAs, so the weights are still read once.
+template <bool SPLIT>
 __global__ __launch_bounds__(256) void gemm_nt_skinny_lds(GemmArgs g, float* partial, int kr) {
-  __shared__ __attribute__((aligned(16))) uint16_t xs[2][32 * kSkXPitch];
+  constexpr int NX = SPLIT ? 2 : 1;
+  __shared__ __attribute__((aligned(16))) uint16_t xs[2][NX][32 * kSkXPitch];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5;
   const int n0 = blockIdx.x * 128 + wave * 32;
   const int k1 = blockIdx.y * kr;
@@ -527,10 +537,12 @@ __global__ __launch_bounds__(256) void gemm_nt_skinny_lds(GemmArgs g, float* par
   const int tt = tid >> 3, part = tid & 7;
   const uint16_t* xg = g.a + (size_t)(tt < g.M ? tt : 0) * g.lda + k1 + part * 32;
   const int nch = kr / kSkChunk;
-  u32x4 xr[4], wa[16], wb[16];
+  u32x4 xr[NX][4], wa[16], wb[16];
   auto load_x = [&](int ch) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) xr[i] = ld16(xg + ch * kSkChunk + i * 8);
+    for (int h = 0; h < NX; ++h)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) xr[h][i] = ld16(xg + h * g.K + ch * kSkChunk + i * 8);
   };
   auto load_w = [&](int ch, u32x4* v) __attribute__((always_inline)) {
 #pragma unroll
@@ -538,9 +550,10 @@ __global__ __launch_bounds__(256) void gemm_nt_skinny_lds(GemmArgs g, float* par
   };
   f32x16 acc = f32x16{};
   auto step = [&](int ch, const u32x4* wcur, u32x4* wnext) __attribute__((always_inline)) {
-    uint16_t* xb = xs[ch & 1];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) st16(xb + tt * kSkXPitch + part * 32 + i * 8, xr[i]);
+    for (int h = 0; h < NX; ++h)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) st16(&xs[ch & 1][h][tt * kSkXPitch + part * 32 + i * 8], xr[h][i]);
     // the next chunk (the last one again after the last: unused), with no branch, so that the
     // MFMAs below wait only for this chunk's weights (at a branch the compiler waits for all loads)
     const int cn = min(ch + 1, nch - 1);
@@ -549,8 +562,11 @@ __global__ __launch_bounds__(256) void gemm_nt_skinny_lds(GemmArgs g, float* par
     __syncthreads();
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
-      const u32x4 xv = *(const u32x4*)(xb + (lane & 31) * kSkXPitch + u * 16 + half * 8);
-      acc = mfma32(wcur[u], xv, acc);
+#pragma unroll
+      for (int h = 0; h < NX; ++h) {
+        const u32x4 xv = *(const u32x4*)(&xs[ch & 1][h][(lane & 31) * kSkXPitch + u * 16 + half * 8]);
+        acc = mfma32(wcur[u], xv, acc);
+      }
     }
   };
   load_x(0);
@@ -620,6 +636,9 @@ bool gemm_scatter_ok(const GemmArgs& g) {
 hipError_t launch_gemm(const GemmArgs& g, void* ws, size_t ws_bytes, hipStream_t stream) {
   if (g.M <= 0 || g.N <= 0) return hipSuccess;
   if (g.cs.k && !gemm_scatter_ok(g)) return hipErrorInvalidValue;
+  // the split operand runs on the skinny LDS kernel (M <= 32), the DMA kernel or the 64-wide
+  // k tiles of the large-M kernel
+  if (g.a_split && (g.K % kSkChunk != 0 || g.lda < 2 * g.K || g.cs.k)) return hipErrorInvalidValue;
   if (g.M <= 32) {
     const int ks = ws ? skinny_ksplit(g.M, g.N, g.K) : 1;  // no workspace: one K split
     const int nsteps = cdiv(g.K, 16);
@@ -629,8 +648,10 @@ hipError_t launch_gemm(const GemmArgs& g, void* ws, size_t ws_bytes, hipStream_t
       if (ws_bytes < (size_t)ks * g.M * g.N * sizeof(float)) return hipErrorInvalidValue;
       partial = (float*)ws;
     }
-    if (skinny_lds_ok(g.M, g.K))
-      gemm_nt_skinny_lds<<<dim3(cdiv(g.N, 128), ks), 256, 0, stream>>>(g, partial, g.K / ks);
+    if (skinny_lds_ok(g.M, g.K) && g.a_split)
+      gemm_nt_skinny_lds<true><<<dim3(cdiv(g.N, 128), ks), 256, 0, stream>>>(g, partial, g.K / ks);
+    else if (skinny_lds_ok(g.M, g.K))
+      gemm_nt_skinny_lds<false><<<dim3(cdiv(g.N, 128), ks), 256, 0, stream>>>(g, partial, g.K / ks);
     else
       gemm_nt_skinny<<<dim3(cdiv(g.N, 32), ks), 256, 0, stream>>>(g, partial, spw);
     if (ks > 1) {

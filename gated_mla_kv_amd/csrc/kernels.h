@@ -9,10 +9,17 @@ namespace gmla {
 
 enum class Shape { K3, Tiny };
 
+// out_lo (or null): the bf16 residual f - hi of every output, at the same ldo
 hipError_t launch_rmsnorm(const float* x, int ldx, const uint16_t* gain, int M, int N, float eps,
-                          uint16_t* out, int ldo, hipStream_t s);
+                          uint16_t* out, int ldo, uint16_t* out_lo, hipStream_t s);
 hipError_t launch_layernorm(const float* x, int ldx, const uint16_t* gain, const uint16_t* bias,
                             int M, int N, float eps, uint16_t* out, int ldo, hipStream_t s);
+// The DSA index key of M tokens in fp64: out[m] = bf16(LayerNorm(w . x[m]) * gain + bias) with a
+// 128-row w [128, K] (K a multiple of 32). partial: index_key_splits(M, K) * M * 128 doubles.
+int index_key_splits(int M, int K);
+hipError_t launch_index_key_f64(const uint16_t* x, int ldx, const uint16_t* w, const uint16_t* gain,
+                                const uint16_t* bias, int M, int K, double eps, double* partial, uint16_t* out,
+                                int ldo, hipStream_t s);
 
 // Paged latent and index caches: position p of sequence s lives in cache row
 //   table[s * max_blocks + p / page_size] * page_size + p % page_size
@@ -112,7 +119,7 @@ __device__ __forceinline__ RowMap row_map(int row0, int rows_per_seq, int b) {
 }
 
 struct IndexScoreArgs {
-  const uint16_t* q_idx;  // [B, 32, 128]
+  const float* q_idx;     // [B, 32, 128] fp32 (fed to the MFMA as bf16 hi + lo)
   const float* w_idx;     // [B, 32]
   const uint16_t* idx_k;  // [B, T_cap, 128] bf16, or E4M3 codes when idx_scale is set
   const float* idx_scale; // [B, T_cap] FP8 key scales, or null

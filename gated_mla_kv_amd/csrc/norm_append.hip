@@ -1,7 +1,9 @@
 // Row normalisations and the cache append.
 //
 // * rmsnorm_rows: KimiRMSNorm ("Kimi K3" attention code page): x * rsqrt(mean(x^2) + eps) in
-//   fp32, times the gain, rounded once to bf16. One wave per row.
+//   fp32, times the gain, rounded once to bf16. One wave per row. With out_lo, the fp32 result
+//   is also written as the bf16 pair (hi, lo), hi + lo within 2^-17 of it (the split operand of
+//   the index-query GEMM).
 // * layernorm_rows: the index-key LayerNorm with gain and bias (K3.1 Gated DSA blog, eq. (3)),
 //   fp32 statistics (population variance), rounded once to bf16. One wave per row.
 // * kv_append_kernel: the cache update of the KV cache card, with preallocated capacity in
@@ -19,7 +21,8 @@ namespace gmla {
 
 __global__ __launch_bounds__(256) void rmsnorm_rows(const float* __restrict__ x, int ldx,
                                                     const uint16_t* __restrict__ gain, int M, int N,
-                                                    float eps, uint16_t* __restrict__ out, int ldo) {
+                                                    float eps, uint16_t* __restrict__ out, int ldo,
+                                                    uint16_t* __restrict__ out_lo) {
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= M) return;
@@ -35,10 +38,18 @@ __global__ __launch_bounds__(256) void rmsnorm_rows(const float* __restrict__ x,
   for (int i = lane * 4; i < N; i += 256) {
     const float4 v = *(const float4*)(xr + i);
     const uint2 gw = *(const uint2*)(gain + i);
+    const float f0 = v.x * inv * lo_bf16(gw.x), f1 = v.y * inv * hi_bf16(gw.x);
+    const float f2 = v.z * inv * lo_bf16(gw.y), f3 = v.w * inv * hi_bf16(gw.y);
     uint2 o;
-    o.x = pack_bf16x2(v.x * inv * lo_bf16(gw.x), v.y * inv * hi_bf16(gw.x));
-    o.y = pack_bf16x2(v.z * inv * lo_bf16(gw.y), v.w * inv * hi_bf16(gw.y));
+    o.x = pack_bf16x2(f0, f1);
+    o.y = pack_bf16x2(f2, f3);
     *(uint2*)(orow + i) = o;
+    if (out_lo) {  // f - hi is exact in fp32; its bf16 rounding leaves at most 2^-17 |f|
+      uint2 r;
+      r.x = pack_bf16x2(f0 - lo_bf16(o.x), f1 - hi_bf16(o.x));
+      r.y = pack_bf16x2(f2 - lo_bf16(o.y), f3 - hi_bf16(o.y));
+      *(uint2*)(out_lo + (size_t)row * ldo + i) = r;
+    }
   }
 }
 
@@ -76,6 +87,154 @@ __global__ __launch_bounds__(256) void layernorm_rows(const float* __restrict__ 
                       (v.w - mean) * inv * hi_bf16(gw.y) + hi_bf16(bw.y));
     *(uint2*)(orow + i) = o;
   }
+}
+
+// ---------------------------------------------------------------------------------------------
+// The index key in fp64 (K3.1 Gated DSA blog, eq. (3) and the LayerNorm paragraph after it):
+// k^I = LayerNorm(W_k^I x) * gain + bias, computed in fp64 and rounded once to bf16, the index
+// cache type. The key's only rounding is then the storage rounding of an fp64 value, so the
+// cached key is the bf16 rounding of the exact LayerNorm output (an fp32 computation lands a
+// few keys per thousand features one bf16 step away from it).
+//
+// index_key_partial_f64: partial[ks][m][j] = sum of x[m][k] w[j][k] over split ks's k range, on
+//   the fp64 MFMA (v_mfma_f64_16x16x4_f64): bf16 inputs and their products are exact in fp64.
+//   A workgroup takes 32 token rows and all 128 features, wave w the features [32w, 32w + 32)
+//   as 2 x 2 tiles of 16 x 16. Per 32-wide k chunk every lane loads 8 consecutive k (16 bytes)
+//   of its two x rows and its two weight rows; the chunk's 8 MFMA steps give MFMA k slot g
+//   (lane group g = lane / 16) the chunk index 8 g + step.
+// index_key_finalize: one wave per row: the splits summed in order, the mean and the population
+//   variance in fp64, then the gain, the bias and one rounding to bf16 (nearest, ties to even).
+// ---------------------------------------------------------------------------------------------
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+constexpr int kIkRows = 32, kIkChunk = 32;
+
+__device__ __forceinline__ double bf16_to_f64(uint32_t bits16) {
+  return (double)__uint_as_float(bits16 << 16);
+}
+
+// bf16 bits of an fp64 value: 8 significant bits, round to nearest, ties to even (normal range)
+__device__ __forceinline__ uint16_t f64_to_bf16_bits(double v) {
+  const uint64_t u = (uint64_t)__double_as_longlong(v);
+  const uint32_t sign = (uint32_t)(u >> 63) << 15;
+  uint64_t mag = u & 0x7FFFFFFFFFFFFFFFull;
+  if (mag == 0) return (uint16_t)sign;
+  mag += ((mag >> 45) & 1ull) + ((1ull << 44) - 1ull);  // a carry into the exponent is right
+  mag >>= 45;                                            // 11 exponent bits, 7 mantissa bits
+  const int e = (int)(mag >> 7) - 1023 + 127;
+  if (e >= 255) return (uint16_t)(sign | 0x7F80u);
+  if (e <= 0) return (uint16_t)sign;                     // below bf16's normal range
+  return (uint16_t)(sign | ((uint32_t)e << 7) | (uint32_t)(mag & 0x7Fu));
+}
+
+__global__ __launch_bounds__(256) void index_key_partial_f64(const uint16_t* __restrict__ x, int ldx,
+                                                             const uint16_t* __restrict__ w, int M, int K,
+                                                             int chunks_per_split, double* __restrict__ partial) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int m0 = blockIdx.x * kIkRows, ks = blockIdx.y;
+  const int c0 = ks * chunks_per_split, c1 = min(c0 + chunks_per_split, K / kIkChunk);
+  const int r = lane & 15, g = lane >> 4;
+  // rows past M re-read row M - 1 (computed, never stored)
+  const uint16_t* xr0 = x + (size_t)min(m0 + r, M - 1) * ldx + 8 * g;
+  const uint16_t* xr1 = x + (size_t)min(m0 + 16 + r, M - 1) * ldx + 8 * g;
+  const uint16_t* wr0 = w + (size_t)(32 * wave + r) * K + 8 * g;
+  const uint16_t* wr1 = w + (size_t)(32 * wave + 16 + r) * K + 8 * g;
+  f64x4 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f64x4{0.0, 0.0, 0.0, 0.0};
+  u32x4 cur[4], nxt[4];
+  auto load = [&](int c, u32x4* v) __attribute__((always_inline)) {
+    const int k = c * kIkChunk;
+    v[0] = ld16(xr0 + k);
+    v[1] = ld16(xr1 + k);
+    v[2] = ld16(wr0 + k);
+    v[3] = ld16(wr1 + k);
+  };
+  if (c0 < c1) load(c0, cur);
+  for (int c = c0; c < c1; ++c) {
+    load(min(c + 1, c1 - 1), nxt);  // the last chunk again after the last: unused
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+      const int word = st >> 1;
+      const bool hi = st & 1;
+      double a[2], b[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const uint32_t wa = cur[i][word], wb = cur[2 + i][word];
+        a[i] = bf16_to_f64(hi ? (wa >> 16) : (wa & 0xFFFFu));
+        b[i] = bf16_to_f64(hi ? (wb >> 16) : (wb & 0xFFFFu));
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) cur[i] = nxt[i];
+  }
+  // D lane l, item v: row l / 16 + 4 v, column l % 16 of the 16 x 16 tile (the fp64 MFMA's
+  // output layout, measured: unlike the fp32 16x16x4 one, the item steps over rows by 4)
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int m = m0 + 16 * i + g + 4 * v;
+      if (m >= M) continue;
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        partial[((size_t)ks * M + m) * 128 + 32 * wave + 16 * j + r] = acc[i][j][v];
+    }
+}
+
+__global__ __launch_bounds__(256) void index_key_finalize(const double* __restrict__ partial, int ksplit, int M,
+                                                          const uint16_t* __restrict__ gain,
+                                                          const uint16_t* __restrict__ bias, double eps,
+                                                          uint16_t* __restrict__ out, int ldo) {
+  const int lane = threadIdx.x & 63;
+  const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (m >= M) return;
+  double v0 = 0.0, v1 = 0.0;
+  for (int s = 0; s < ksplit; ++s) {
+    const double* p = partial + ((size_t)s * M + m) * 128 + 2 * lane;
+    v0 += p[0];
+    v1 += p[1];
+  }
+  double sum = v0 + v1;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o, 64);
+  const double mean = sum / 128.0;
+  const double d0 = v0 - mean, d1 = v1 - mean;
+  double ss = d0 * d0 + d1 * d1;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 64);
+  const double inv = 1.0 / sqrt(ss / 128.0 + eps);
+  const uint32_t gw = *(const uint32_t*)(gain + 2 * lane), bw = *(const uint32_t*)(bias + 2 * lane);
+  const uint16_t o0 = f64_to_bf16_bits(d0 * inv * bf16_to_f64(gw & 0xFFFFu) + bf16_to_f64(bw & 0xFFFFu));
+  const uint16_t o1 = f64_to_bf16_bits(d1 * inv * bf16_to_f64(gw >> 16) + bf16_to_f64(bw >> 16));
+  *(uint32_t*)(out + (size_t)m * ldo + 2 * lane) = (uint32_t)o0 | ((uint32_t)o1 << 16);
+}
+
+static int index_key_chunks_per_split(int M, int K) {
+  const int chunks = K / kIkChunk, blocks = cdiv(M, kIkRows);
+  const int ks = max(1, min(cdiv(256, blocks), 56));  // about one workgroup per CU
+  return cdiv(chunks, ks);
+}
+
+int index_key_splits(int M, int K) {
+  if (M <= 0 || K <= 0) return 0;
+  return cdiv(K / kIkChunk, index_key_chunks_per_split(M, K));
+}
+
+hipError_t launch_index_key_f64(const uint16_t* x, int ldx, const uint16_t* w, const uint16_t* gain,
+                                const uint16_t* bias, int M, int K, double eps, double* partial, uint16_t* out,
+                                int ldo, hipStream_t s) {
+  if (M <= 0) return hipSuccess;
+  if (K % kIkChunk != 0 || ldx % 8 != 0 || ldo % 2 != 0) return hipErrorInvalidValue;
+  const int cps = index_key_chunks_per_split(M, K), ks = index_key_splits(M, K);
+  index_key_partial_f64<<<dim3(cdiv(M, kIkRows), ks), 256, 0, s>>>(x, ldx, w, M, K, cps, partial);
+  index_key_finalize<<<cdiv(M, 4), 256, 0, s>>>(partial, ks, M, gain, bias, eps, out, ldo);
+  return hipGetLastError();
 }
 
 // E4M3 codes of n = 8 * lanes values v (8 per lane, lanes in groups of `group` sharing a scale):
@@ -170,9 +329,9 @@ __global__ __launch_bounds__(256) void kv_append_kernel(KvAppendArgs a) {
 }
 
 hipError_t launch_rmsnorm(const float* x, int ldx, const uint16_t* gain, int M, int N, float eps,
-                          uint16_t* out, int ldo, hipStream_t s) {
+                          uint16_t* out, int ldo, uint16_t* out_lo, hipStream_t s) {
   if (M <= 0) return hipSuccess;
-  rmsnorm_rows<<<cdiv(M, 4), 256, 0, s>>>(x, ldx, gain, M, N, eps, out, ldo);
+  rmsnorm_rows<<<cdiv(M, 4), 256, 0, s>>>(x, ldx, gain, M, N, eps, out, ldo, out_lo);
   return hipGetLastError();
 }
 

@@ -55,7 +55,7 @@ class LayerBuffers:
         return y
 
     def prefill_sparse(self, cache: "CacheBuffers", x: torch.Tensor, start_pos: torch.Tensor, max_end: int,
-                       out_dtype=OUT_BF16, sel_idx=None, sel_cnt=None, ws=None):
+                       out_dtype=OUT_BF16, sel_idx=None, sel_cnt=None, ws=None, scores=None):
         B, T, _ = x.shape
         y = torch.empty((B, T, self.shape.hidden), device=self.device,
                         dtype=torch.bfloat16 if out_dtype == OUT_BF16 else torch.float32)
@@ -63,7 +63,7 @@ class LayerBuffers:
             ws = torch.empty(workspace_bytes_prefill_sparse(self.dims, B, T, max_end), dtype=torch.uint8,
                              device=self.device)
         mla_prefill_sparse(self.dims, self.cw, cache.c, start_pos, max_end, x, B, T, y, out_dtype, sel_idx, sel_cnt,
-                           ws)
+                           ws, scores=scores)
         return y
 
     def decode(self, cache: "CacheBuffers", x: torch.Tensor, seq_len: torch.Tensor, max_len: int,

@@ -171,12 +171,14 @@ int mla_prefill(const mla_dims* dims, const mla_weights* w, const mla_cache* cac
  *   (eq. (5)), keeps S = the min(topk, t) largest (eq. (6), ties to the lower position),
  *   attends over S only in the absorbed form, and goes through the gate and o_proj.
  *   sel_idx [B,T,topk] i32 (ascending, -1 padded) and sel_cnt [B,T] i32, or NULL, receive S.
+ *   scores [B,T,max_end] f32 or NULL receives each token's index scores I_s for s < t (eq. (5));
+ *   entries at s >= t are left unwritten.
  *   ws: device workspace of at least mla_workspace_bytes_prefill_sparse(dims, B, T, max_end)
  *   bytes. Errors as mla_prefill; MLA_ERR_UNSUPPORTED without the indexer. */
 int mla_prefill_sparse(const mla_dims* dims, const mla_weights* w, const mla_cache* cache,
                        const int32_t* start_pos, int32_t max_end, const void* x, int32_t B,
                        int32_t T, void* y, int32_t out_dtype, int32_t* sel_idx, int32_t* sel_cnt,
-                       void* ws, size_t ws_bytes, hipStream_t stream);
+                       float* scores, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* [host] Workspace bytes of mla_prefill_sparse; 0 on bad input or without the indexer. */
 size_t mla_workspace_bytes_prefill_sparse(const mla_dims* dims, int32_t B, int32_t T, int32_t max_end);
@@ -198,6 +200,19 @@ int mla_decode(const mla_dims* dims, const mla_weights* w, const mla_cache* cach
                int32_t num_splits, int32_t* sel_idx, int32_t* sel_cnt, void* y,
                int32_t out_dtype, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* The DSA indexer's projections of M tokens, with the launches a decode or prefill step runs
+ * ([DSA] eqs. (2)-(4) and the LayerNorm paragraph after eq. (3)):
+ *   q_idx [M,n_idx,d_idx] f32 = reshape(c^Q W_q^I^T), c^Q the normalised query latent (fp32,
+ *         entering the GEMM as a bf16 hi + lo pair);
+ *   w_idx [M,n_idx] f32 = x W_a^I^T, raw (no sigmoid);
+ *   k_idx [M,d_idx] bf16 = LayerNorm(x W_k^I^T) * gain + bias, computed in fp64 and rounded once
+ *         (the value mla_decode / mla_prefill_sparse append to the index cache).
+ *   x [M,hidden] bf16. ws: at least mla_workspace_bytes(dims, M, 1, 1, MLA_PATH_SPARSE) bytes.
+ *   Requires the indexer (MLA_ERR_UNSUPPORTED without it) and every w_idx_* weight. */
+int mla_index_projections(const mla_dims* dims, const mla_weights* w, const void* x, int32_t M,
+                          float* q_idx, float* w_idx, void* k_idx, void* ws, size_t ws_bytes,
+                          hipStream_t stream);
+
 /* Cache append ([KV] update; [SK]; [DSA] eq. (7) and pseudocode).
  *   For b < B and i < T, at position p = pos[b] + i:
  *     latent[b,p] = c[b,i] ‖ r[b,i]
@@ -211,14 +226,16 @@ int kv_append(const mla_dims* dims, const mla_cache* cache, const int32_t* pos, 
               const void* v, const void* idx_k, hipStream_t stream);
 
 /* DSA index scores and top-k for one query per sequence ([DSA] eqs. (5)-(6)).
- *   q_idx [B,n_idx,d_idx] bf16; w_idx [B,n_idx] f32 raw head weights a_t (eq. (4));
+ *   q_idx [B,n_idx,d_idx] f32 index query (eq. (2)), unrounded as eq. (5) takes it: each value
+ *   enters the bf16 MFMA as a hi + lo pair, so the scores carry it to about 17 bits;
+ *   w_idx [B,n_idx] f32 raw head weights a_t (eq. (4));
  *   idx_k_cache [B,T_cap,d_idx] bf16; n_visible [B] i32 = t (current token included);
  *   max_visible [host] >= max t, <= T_cap.
  *   I_s = (1/sqrt(n_idx*d_idx)) sum_h a_h ReLU(q_h . k_s) for s < t; the min(topk, t) largest
  *   (ties to the lower position) are written ascending to out_idx [B,topk] i32, -1 padded,
  *   with out_cnt [B] i32. out_scores [B,T_cap] f32 or NULL receives I for s < t.
  *   ws: at least mla_workspace_bytes(dims, B, 1, max_visible, MLA_PATH_SPARSE). */
-int dsa_index_topk(const mla_dims* dims, const void* q_idx, const float* w_idx,
+int dsa_index_topk(const mla_dims* dims, const float* q_idx, const float* w_idx,
                    const void* idx_k_cache, int32_t T_cap, const int32_t* n_visible,
                    int32_t max_visible, int32_t B, int32_t* out_idx, int32_t* out_cnt,
                    float* out_scores, void* ws, size_t ws_bytes, hipStream_t stream);
@@ -226,7 +243,7 @@ int dsa_index_topk(const mla_dims* dims, const void* q_idx, const float* w_idx,
 /* As dsa_index_topk over FP8 index keys ([DSA] cache section): idx_k_codes [B, T_cap, 128] OCP
  * E4M3 codes, idx_k_scales [B, T_cap] fp32 (>= 0); key s reads back as decode(code) * scale,
  * so its score is scale times the score of the decoded codes. d_idx must be 128. */
-int dsa_index_topk_fp8(const mla_dims* dims, const void* q_idx, const float* w_idx,
+int dsa_index_topk_fp8(const mla_dims* dims, const float* q_idx, const float* w_idx,
                        const void* idx_k_codes, const float* idx_k_scales, int32_t T_cap,
                        const int32_t* n_visible, int32_t max_visible, int32_t B, int32_t* out_idx,
                        int32_t* out_cnt, float* out_scores, void* ws, size_t ws_bytes,

@@ -5,7 +5,8 @@ Tolerances (written out here, used by every parity test):
 * floating-point outputs: max |got - ref| <= 2e-2 * rms(ref row) per output row (one token's
   feature vector or one (b, h) row), plus half a bf16 ulp of ref when the output is bf16;
 * scores and log-sum-exps: |got - ref| <= 1e-3 * (|ref| + rms(ref row));
-* cache appends and selected indices: bit-exact (selection boundary rule in the DSA tests).
+* cache appends and selected indices: bit-exact, except top-k positions swapped across the
+  oracle's k-th index score when their oracle scores lie within 1e-4 of it (check_selection).
 """
 import numpy as np
 import torch
@@ -76,28 +77,48 @@ def i32(a):
     return torch.tensor(np.asarray(a, np.int32), device="cuda")
 
 
-def index_score_ulp_bound(qi, a, keys):
-    """Per position s, how far the index score I_s (eq. (5)) can move when every element of the
-    bf16 index query sits one bf16 ulp (<= 2^-7 |q|) from the oracle's: scale * sum_h |a_h|
-    sum_d 2^-7 |q_hd| |k_sd| (ReLU is 1-Lipschitz). End to end, the GPU rounds q^I to bf16 from
-    its own fp32 c^Q and the oracle from its float64 one, so single elements may round apart."""
-    q = np.abs(np.asarray(qi, np.float64))
-    k = np.abs(np.asarray(keys, np.float64))
-    scale = 1.0 / np.sqrt(q.shape[0] * q.shape[1])
-    return scale * 2.0 ** -7 * (np.abs(np.asarray(a, np.float64)) @ (q @ k.T))
+def rand_f32(shape, seed, std=1.0):
+    """Seeded fp32 values (not bf16-representable in general): the DSA index query enters the
+    library in fp32, as eq. (5) takes it unrounded."""
+    rng = np.random.default_rng(seed)
+    return (rng.standard_normal(shape) * std).astype(np.float32)
 
 
-def check_selection_end_to_end(got, I, k, bound):
-    """The GPU's top-k set against the oracle's scores I: equal to select_topk(I, k) except for
-    swapped positions whose scores lie within 1e-4 plus their ulp bounds of the k-th largest.
-    Kernel-boundary tests (identical index inputs) use the plain 1e-4 rule instead."""
+def dev_f32(a):
+    return torch.tensor(np.ascontiguousarray(a, np.float32), device="cuda")
+
+
+SEL_TOL = 1e-4
+
+
+def check_selection(got, I, k, what=""):
+    """A top-k set (ascending positions) against the oracle's float64 index scores I ([DSA]
+    eq. (6)): it must equal the oracle's own selection except for positions swapped across the
+    oracle's k-th largest score tau, each with an oracle score within 1e-4 of tau (the
+    selection-boundary rule). Returns True when the sets are equal, False for a legal swap."""
     import oracle as O
+    I = np.asarray(I, np.float64)
+    got = np.asarray(got)
     exp = O.select_topk(I, k)
-    order = np.argsort(-I, kind="stable")
-    tau_pos = order[k - 1]
-    tau = I[tau_pos]
+    assert len(got) == len(exp), (what, len(got), len(exp))
+    assert np.all(np.diff(got) > 0) and got[0] >= 0 and got[-1] < len(I), (what, "not ascending positions < t")
+    if np.array_equal(got, exp):
+        return True
+    tau = I[exp].min()
     extra, missing = np.setdiff1d(got, exp), np.setdiff1d(exp, got)
-    assert len(extra) == len(missing), (extra, missing)
-    for s_ in np.concatenate([extra, missing]):
-        assert abs(I[s_] - tau) < 1e-4 + bound[s_] + bound[tau_pos], (s_, I[s_], tau, bound[s_], bound[tau_pos])
-    return exp
+    assert len(extra) == len(missing), (what, extra, missing)
+    far = [int(s_) for s_ in np.concatenate([extra, missing]) if not abs(I[s_] - tau) < SEL_TOL]
+    assert not far, f"{what}: positions {far} swapped across the k-th score {tau!r} by more than {SEL_TOL}: " \
+                    f"{[float(I[s_] - tau) for s_ in far]}"
+    return False
+
+
+def oracle_row_for_selection(d, w, x_row, qt_row, latent, S):
+    """The oracle's layer output row for one token over a given selected set S: the sparse core
+    in the absorbed form ([DSA] eq. (9) over S), the value up-projection, the gate and o_proj,
+    as dsa_decode_step / dsa_prefill compute them for their own selection. Used for rows whose
+    GPU selection is a legal boundary swap of the oracle's (check_selection returned False)."""
+    import oracle as O
+    o, _ = O.attention_absorbed_subset(qt_row, latent, S, O.softmax_scale(d), d)
+    _, y = O.gate_output(O.value_up(o, w, d)[None], np.asarray(x_row, np.float64)[None], w, d)
+    return y[0]

@@ -152,7 +152,7 @@ def test_prefill_sparse_validation():
     w = gm.MlaWeights(*([FAKE] * 13))
     call = lambda dims=d, c=None, ws_bytes=1 << 40, B=2, T=10, max_end=50, ww=w: L.mla_prefill_sparse(  # noqa: E731
         ctypes.byref(dims), ctypes.byref(ww), ctypes.byref(c or _cache(idx=FAKE)), FAKE, max_end, FAKE, B, T, FAKE,
-        0, None, None, FAKE, ws_bytes, None)
+        0, None, None, None, FAKE, ws_bytes, None)
     assert call(dims=gm.make_dims(K3.replace(n_idx_heads=0))) == ERR_UNSUPPORTED   # needs the indexer
     assert call(c=_cache(idx=None)) == ERR_NULL
     assert call(ww=_weights()) == ERR_NULL                                            # no index weights
@@ -204,3 +204,19 @@ def test_paged_cache_validation():
     assert call(paged(k=FAKE, v=FAKE)) == ERR_UNSUPPORTED
     assert call(paged(), gm.make_dims(TINY)) == ERR_UNSUPPORTED
     assert _call_prefill(d, paged(k=None, v=None), max_end=50) == ERR_UNSUPPORTED
+
+
+def test_index_projections_validation():
+    L = gm.lib()
+    d = gm.make_dims(K3)
+    w = gm.MlaWeights(*([FAKE] * 13))
+    call = lambda dims=d, ww=w, M=4, q=FAKE, ws_bytes=1 << 40: L.mla_index_projections(  # noqa: E731
+        ctypes.byref(dims), ctypes.byref(ww), FAKE, M, q, FAKE, FAKE, FAKE, ws_bytes, None)
+    assert call(dims=gm.make_dims(K3.replace(n_idx_heads=0))) == ERR_UNSUPPORTED   # needs the indexer
+    assert call(dims=gm.make_dims(TINY)) == ERR_UNSUPPORTED
+    assert call(ww=_weights()) == ERR_NULL                                            # no index weights
+    assert call(q=None) == ERR_NULL
+    assert call(M=-1) == ERR_SHAPE
+    assert call(M=0) == OK
+    assert call(ws_bytes=100) == ERR_WORKSPACE
+    assert call(ws_bytes=gm.workspace_bytes(d, 4, 1, 1, gm.PATH_SPARSE) - 1) == ERR_WORKSPACE

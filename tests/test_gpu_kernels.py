@@ -5,7 +5,7 @@ import pytest
 import torch
 
 import oracle as O
-from gpu_helpers import check_rows, check_scores, dev_bf16, f64, i32, rand_bf16, to_np
+from gpu_helpers import check_rows, check_scores, check_selection, dev_bf16, dev_f32, f64, i32, rand_bf16, rand_f32, to_np
 from workloads import K3, K3_SMALL_TOPK, TINY, bf16_bits_to_f32
 
 pytestmark = pytest.mark.gpu
@@ -267,7 +267,7 @@ def test_index_scores_and_topk(topk, t_vis):
     print(f"index_topk k={topk} t={t_vis}", flush=True)
     B = len(t_vis)
     T_cap = max(t_vis) + 7
-    qi = rand_bf16((B, d.n_idx_heads, d.d_idx), 70, std=0.1)
+    qi = rand_f32((B, d.n_idx_heads, d.d_idx), 70, std=0.1)    # fp32, not bf16-representable
     a = np.random.default_rng(71).standard_normal((B, d.n_idx_heads)).astype(np.float32)
     keys = rand_bf16((B, T_cap, d.d_idx), 72)
     dims_c = gm.make_dims(d)
@@ -275,7 +275,7 @@ def test_index_scores_and_topk(topk, t_vis):
     out_cnt = torch.empty((B,), dtype=torch.int32, device="cuda")
     scores = torch.full((B, T_cap), float("nan"), dtype=torch.float32, device="cuda")
     ws = torch.empty(gm.workspace_bytes(dims_c, B, 1, T_cap, gm.PATH_SPARSE), dtype=torch.uint8, device="cuda")
-    gm.dsa_index_topk(dims_c, dev_bf16(qi), torch.tensor(a, device="cuda"), dev_bf16(keys), T_cap, i32(t_vis),
+    gm.dsa_index_topk(dims_c, dev_f32(qi), dev_f32(a), dev_bf16(keys), T_cap, i32(t_vis),
                       max(t_vis), B, out_idx, out_cnt, scores, ws)
     _sync()
     sel = out_idx.cpu().numpy()
@@ -283,8 +283,10 @@ def test_index_scores_and_topk(topk, t_vis):
     sc_gpu = scores.cpu().numpy()
     for b in range(B):
         t = t_vis[b]
-        ref = O.index_scores(f64(qi[b]), a[b].astype(np.float64), f64(keys[b]), t)
+        ref = O.index_scores(qi[b].astype(np.float64), a[b].astype(np.float64), f64(keys[b]), t)
         check_scores(sc_gpu[b, :t], ref, f"index scores b={b}")
+        # the hi + lo query keeps the scores far inside the selection rule's 1e-4
+        assert np.max(np.abs(sc_gpu[b, :t] - ref)) < 2e-5, np.max(np.abs(sc_gpu[b, :t] - ref))
         k = min(topk, t)
         assert cnt[b] == k
         assert (sel[b, k:] == -1).all()
@@ -292,25 +294,19 @@ def test_index_scores_and_topk(topk, t_vis):
         # exact: the oracle's selection rule applied to the GPU's own fp32 scores
         np.testing.assert_array_equal(got, O.select_topk(sc_gpu[b, :t].astype(np.float64), topk))
         # against the oracle's float64 scores: equal except swaps across the k-th score within 1e-4
-        exp = O.select_topk(ref, topk)
-        if k < t:
-            tau = np.sort(ref)[::-1][k - 1]
-            extra = np.setdiff1d(got, exp)
-            missing = np.setdiff1d(exp, got)
-            assert len(extra) == len(missing)
-            assert np.all(np.abs(ref[extra] - tau) < 1e-4) and np.all(np.abs(ref[missing] - tau) < 1e-4)
+        check_selection(got, ref, k, f"b={b}")
 
 
 def test_topk_ties_take_lowest_positions():
     d = K3.replace(topk=16)
     B, T_cap, t = 2, 100, 90
-    qi = np.zeros((B, d.n_idx_heads, d.d_idx), np.uint16)      # all scores exactly zero (+0 or -0)
+    qi = np.zeros((B, d.n_idx_heads, d.d_idx), np.float32)     # all scores exactly zero (+0 or -0)
     a = np.random.default_rng(80).standard_normal((B, d.n_idx_heads)).astype(np.float32)
     keys = rand_bf16((B, T_cap, d.d_idx), 81)
     out_idx = torch.empty((B, 16), dtype=torch.int32, device="cuda")
     out_cnt = torch.empty((B,), dtype=torch.int32, device="cuda")
     ws = torch.empty(gm.workspace_bytes(gm.make_dims(d), B, 1, t, gm.PATH_SPARSE), dtype=torch.uint8, device="cuda")
-    gm.dsa_index_topk(gm.make_dims(d), dev_bf16(qi), torch.tensor(a, device="cuda"), dev_bf16(keys), T_cap,
+    gm.dsa_index_topk(gm.make_dims(d), dev_f32(qi), dev_f32(a), dev_bf16(keys), T_cap,
                       i32([t, t]), t, B, out_idx, out_cnt, None, ws)
     _sync()
     np.testing.assert_array_equal(out_idx.cpu().numpy(), np.tile(np.arange(16, dtype=np.int32), (B, 1)))
@@ -327,7 +323,7 @@ def test_topk_many_equal_scores(t, n_pos):
     print(f"topk ties t={t} n_pos={n_pos}", flush=True)
     B, T_cap = 2, t + 5
     rng = np.random.default_rng(90 + n_pos)
-    qi = rand_bf16((B, d.n_idx_heads, d.d_idx), 91, std=0.1)
+    qi = rand_f32((B, d.n_idx_heads, d.d_idx), 91, std=0.1)
     a = np.abs(rng.standard_normal((B, d.n_idx_heads))).astype(np.float32) + 0.1  # positive weights
     keys = rand_bf16((B, T_cap, d.d_idx), 92)
     keys_z = keys.copy()
@@ -341,7 +337,7 @@ def test_topk_many_equal_scores(t, n_pos):
     out_cnt = torch.empty((B,), dtype=torch.int32, device="cuda")
     scores = torch.full((B, T_cap), float("nan"), dtype=torch.float32, device="cuda")
     ws = torch.empty(gm.workspace_bytes(dims_c, B, 1, T_cap, gm.PATH_SPARSE), dtype=torch.uint8, device="cuda")
-    gm.dsa_index_topk(dims_c, dev_bf16(qi), torch.tensor(a, device="cuda"), dev_bf16(keys_z), T_cap,
+    gm.dsa_index_topk(dims_c, dev_f32(qi), dev_f32(a), dev_bf16(keys_z), T_cap,
                       i32([t, t]), t, B, out_idx, out_cnt, scores, ws)
     _sync()
     sel = out_idx.cpu().numpy()

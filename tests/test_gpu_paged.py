@@ -2,14 +2,16 @@
 page table. Filled by the library's kv_append from the same rows, a paged cache holds, read
 back through its table, exactly the bytes of the contiguous cache; attention, DSA decode and
 DSA prefill over it give results equal bit for bit to the contiguous cache's (same arithmetic,
-other addresses), and the contiguous results are checked against the oracle elsewhere; one
-case is checked against the oracle here as well."""
+other addresses), and the paged results are checked against the oracle here as well: attention
+outputs within the row tolerance, DSA selections equal to the oracle's except swaps across its
+k-th index score within 1e-4, and the layer outputs of the DSA steps."""
 import numpy as np
 import pytest
 import torch
 
 import oracle as O
-from gpu_helpers import check_rows, check_scores, dev_bf16, f64, i32, rand_bf16, to_np
+from gpu_helpers import (check_rows, check_scores, check_selection, dev_bf16, f64, i32, oracle_row_for_selection,
+                         rand_bf16, to_np)
 from workloads import K3, K3_SMALL_TOPK, make_index_prefix, make_latent_prefix, make_layer_weights, make_tokens
 
 pytestmark = pytest.mark.gpu
@@ -89,8 +91,10 @@ def test_paged_dsa_decode_step(fp8):
     L = LayerBuffers(d, lw.w)
     B, T, T_cap, page = 2, 300, 320, 32
     paged, flat, table = _caches(d, B, T_cap, page, 3, 181, index=True, fp8_latent=fp8, fp8_index=fp8)
-    _append(d, (paged, flat), make_latent_prefix(d, B, T, seed=181), make_index_prefix(d, B, T, seed=181))
-    x = dev_bf16(make_tokens(d, B, 1, seed=181, step=0)[:, 0])
+    lat, idx = make_latent_prefix(d, B, T, seed=181), make_index_prefix(d, B, T, seed=181)
+    _append(d, (paged, flat), lat, idx)
+    x_bits = make_tokens(d, B, 1, seed=181, step=0)[:, 0]
+    x = dev_bf16(x_bits)
     res = []
     for c in (paged, flat):
         sel = torch.empty((B, d.topk), dtype=torch.int32, device="cuda")
@@ -103,6 +107,19 @@ def test_paged_dsa_decode_step(fp8):
     # the new token's rows went to the right pool row
     got = _through_table(paged.latent, table, page)
     assert torch.equal(got[:, :T + 1], flat.latent[:, :T + 1])
+    # the paged step against the oracle's DSA decode step over the same caches
+    w = {k: f64(v) for k, v in lw.w.items()}
+    oc = O.Cache(d, B, expanded=False, fp8_latent=fp8, fp8_index=fp8)
+    oc.set_prefix(f64(lat), f64(idx))
+    y_ref, ex = O.dsa_decode_step(f64(x_bits), w, oc, d)
+    y, sel, cnt = res[0]
+    sel_np = sel.cpu().numpy()
+    assert (cnt.cpu().numpy() == d.topk).all()
+    for b in range(B):
+        y_row = y_ref[b]
+        if not check_selection(sel_np[b], ex["scores"][b], d.topk, f"paged dsa decode b={b}"):
+            y_row = oracle_row_for_selection(d, w, f64(x_bits[b]), ex["q_tilde"][b], oc.latent[b], sel_np[b])
+        check_rows(to_np(y[b]), y_row, f"paged dsa decode y b={b}")
 
 
 @pytest.mark.parametrize("B", [1, 2])
@@ -114,8 +131,10 @@ def test_paged_dsa_prefill(B):
     L = LayerBuffers(d, lw.w)
     P, T, T_cap, page = 40, 300, 352, 32
     paged, flat, table = _caches(d, B, T_cap, page, 4, 191, index=True)
-    _append(d, (paged, flat), make_latent_prefix(d, B, P, seed=191), make_index_prefix(d, B, P, seed=191))
-    x = dev_bf16(make_tokens(d, B, T, seed=191))
+    lat, idx = make_latent_prefix(d, B, P, seed=191), make_index_prefix(d, B, P, seed=191)
+    _append(d, (paged, flat), lat, idx)
+    x_bits = make_tokens(d, B, T, seed=191)
+    x = dev_bf16(x_bits)
     res = []
     for c in (paged, flat):
         sel = torch.empty((B, T, d.topk), dtype=torch.int32, device="cuda")
@@ -125,3 +144,20 @@ def test_paged_dsa_prefill(B):
     torch.cuda.synchronize()
     for a, b in zip(res[0], res[1]):
         assert torch.equal(a, b)
+    # the paged prefill against the oracle's DSA prefill
+    w = {k: f64(v) for k, v in lw.w.items()}
+    y, sel, cnt = (t.cpu().numpy() if t.dtype != torch.float32 else to_np(t) for t in res[0])
+    for b in range(B):
+        oc = O.Cache(d, 1, expanded=False)
+        oc.set_prefix(f64(lat[b:b + 1]), f64(idx[b:b + 1]))
+        y_ref, ex = O.dsa_prefill(f64(x_bits[b:b + 1]), w, oc, d)
+        y_cmp = y_ref[0].copy()
+        for i in range(T):
+            t = P + i + 1
+            k = min(d.topk, t)
+            assert cnt[b, i] == k
+            I = O.index_scores(ex["q_idx"][0, i], ex["a"][0, i], oc.idx[0], t)
+            if not check_selection(sel[b, i, :k], I, k, f"paged dsa prefill b={b} row {i}"):
+                y_cmp[i] = oracle_row_for_selection(d, w, f64(x_bits[b, i]), ex["q_tilde"][0, i], oc.latent[0],
+                                                    sel[b, i, :k])
+        check_rows(y[b], y_cmp, f"paged dsa prefill y b={b}")

@@ -26,7 +26,8 @@ import numpy as np
 __all__ = [
     "MLADims", "K3", "K2_SHAPE", "TINY", "TINY_DSA", "K3_SMALL_TOPK",
     "bf16_bits", "bf16_bits_to_f32", "normal_bf16", "LayerInputs", "make_layer_weights",
-    "make_tokens", "make_latent_prefix", "make_index_prefix", "TensorId",
+    "make_tokens", "make_latent_prefix", "make_index_prefix", "TensorId", "device_normal_bf16",
+    "device_normal_f32",
 ]
 
 
@@ -215,6 +216,18 @@ def make_latent_prefix(dims: MLADims, B: int, T: int, seed: int = 0) -> np.ndarr
 def make_index_prefix(dims: MLADims, B: int, T: int, seed: int = 0) -> np.ndarray:
     """Cached index keys [B, T, d_idx] ~ N(0, 1), bf16 bits."""
     return normal_bf16((B, T, dims.d_idx), 1.0, seed, TensorId.INDEX_PREFIX)
+
+
+def device_normal_f32(shape, std: float, seed: int, tensor_id: int, device="cuda"):
+    """N(0, std^2) float32 tensor drawn on the device by torch's seeded generator (fp32 inputs such
+    as the DSA index query, which the library takes unrounded)."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed) * 1_000_003 + int(tensor_id))
+    t = torch.randn(tuple(shape), generator=g, device=device, dtype=torch.float32)
+    if std != 1.0:
+        t.mul_(std)
+    return t
 
 
 def device_normal_bf16(shape, std: float, seed: int, tensor_id: int, device="cuda"):
