@@ -14,7 +14,7 @@ __all__ = [
     "GmlaError", "lib", "MlaDims", "MlaWeights", "MlaCache", "make_dims", "OUT_BF16", "OUT_F32",
     "PATH_ABSORBED", "PATH_EXPANDED", "PATH_SPARSE", "status_string", "dims_supported",
     "workspace_bytes", "workspace_bytes_prefill_sparse", "mla_prefill", "mla_prefill_sparse", "mla_decode",
-    "kv_append", "dsa_index_topk", "dsa_index_topk_fp8", "mla_index_projections", "mla_gemm",
+    "mla_decode_noalloc", "NOALLOC_SCRATCH_BYTES", "kv_append", "dsa_index_topk", "dsa_index_topk_fp8", "mla_index_projections", "mla_gemm",
     "mla_rmsnorm", "mla_layernorm", "mla_prefill_attention", "mla_absorb_query",
     "mla_decode_attention", "mla_sparse_attention", "mla_expanded_attention", "mla_value_up_gate",
     "LIB_PATH",
@@ -71,6 +71,7 @@ _SIGS = {
     "mla_prefill_sparse": (ctypes.c_int, [_P, _P, _P, _P, _I, _P, _I, _I, _P, _I, _P, _P, _P, _P, _SZ, _P]),
     "mla_index_projections": (ctypes.c_int, [_P, _P, _P, _I, _P, _P, _P, _P, _SZ, _P]),
     "mla_decode": (ctypes.c_int, [_P, _P, _P, _P, _I, _P, _I, _I, _I, _P, _P, _P, _I, _P, _SZ, _P]),
+    "mla_decode_noalloc": (ctypes.c_int, [_P, _P, _P, _P, _I, _P, _I, _I, _I, _P, _P, _P, _I, _P]),
     "kv_append": (ctypes.c_int, [_P, _P, _P, _I, _I, _I, _P, _P, _P, _P, _P, _P]),
     "dsa_index_topk": (ctypes.c_int, [_P, _P, _P, _P, _I, _P, _I, _I, _P, _P, _P, _P, _SZ, _P]),
     "dsa_index_topk_fp8": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _P, _I, _I, _P, _P, _P, _P, _SZ, _P]),
@@ -188,6 +189,17 @@ def mla_decode(dims, weights: MlaWeights, cache: MlaCache, seq_len, max_len, x, 
                             max_len, _p(x), B, path, num_splits, _p(sel_idx), _p(sel_cnt), _p(y),
                             out_dtype, wp, wn, _stream(stream)),
            "mla_decode")
+
+
+NOALLOC_SCRATCH_BYTES = 64 * 1024 * 1024
+
+
+def mla_decode_noalloc(dims, weights: MlaWeights, cache: MlaCache, seq_len, max_len, x, B, path, y,
+                       out_dtype=OUT_BF16, sel_idx=None, sel_cnt=None, num_splits=0, stream=None):
+    _check(lib().mla_decode_noalloc(ctypes.byref(dims), ctypes.byref(weights), ctypes.byref(cache), _p(seq_len),
+                                    max_len, _p(x), B, path, num_splits, _p(sel_idx), _p(sel_cnt), _p(y),
+                                    out_dtype, _stream(stream)),
+           "mla_decode_noalloc")
 
 
 def kv_append(dims, cache: MlaCache, pos, max_end, B, T, c, r, k_nope=None, v=None, idx_k=None, stream=None):

@@ -4,6 +4,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/gmla.h"
 #include "gemm.h"
 #include "kernels.h"
@@ -1023,3 +1025,55 @@ int mla_decode(const mla_dims* d, const mla_weights* w, const mla_cache* cache, 
 }
 
 }  // extern "C"
+
+// ------------------------------------------------------------------------------------------
+// Decode without allocation: mla_decode's workspace in a static device array of the library
+// (one copy per GPU, kept until the process ends). In host code `scratch` only names the symbol;
+// its device address on each GPU comes from hipGetSymbolAddress, looked up once per device with
+// that device current, and only that address is ever passed to a kernel.
+// ------------------------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[MLA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+struct ScratchSlot {
+  std::once_flag once;
+  void* ptr = nullptr;
+  hipError_t err = hipSuccess;
+};
+ScratchSlot g_scratch[kMaxDevices];
+
+// this device's address of `scratch`, or null (err set) if the lookup failed
+void* scratch_on_current_device(hipError_t* err) {
+  int dev = -1;
+  if ((*err = hipGetDevice(&dev)) != hipSuccess) return nullptr;
+  if (dev < 0 || dev >= kMaxDevices) {
+    *err = hipErrorInvalidDevice;
+    return nullptr;
+  }
+  ScratchSlot& s = g_scratch[dev];
+  std::call_once(s.once, [&s]() {
+    void* p = nullptr;
+    s.err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    s.ptr = s.err == hipSuccess ? p : nullptr;
+  });
+  *err = s.err;
+  return s.ptr;
+}
+}  // namespace
+
+extern "C" int mla_decode_noalloc(const mla_dims* d, const mla_weights* w, const mla_cache* cache,
+                                  const int32_t* seq_len, int32_t max_len, const void* x, int32_t B, int32_t path,
+                                  int32_t num_splits, int32_t* sel_idx, int32_t* sel_cnt, void* y,
+                                  int32_t out_dtype, hipStream_t stream) {
+  // the size check comes first and touches no device
+  if (d && B > 0) {
+    const size_t need = mla_workspace_bytes_ex(d, B, 1, max_len, path, num_splits);
+    if (need > (size_t)MLA_NOALLOC_SCRATCH_BYTES) return MLA_ERR_WORKSPACE;
+  }
+  hipError_t err;
+  void* ws = scratch_on_current_device(&err);
+  if (!ws) return MLA_ERR_HIP;
+  return mla_decode(d, w, cache, seq_len, max_len, x, B, path, num_splits, sel_idx, sel_cnt, y, out_dtype, ws,
+                    (size_t)MLA_NOALLOC_SCRATCH_BYTES, stream);
+}

@@ -213,6 +213,25 @@ int mla_index_projections(const mla_dims* dims, const mla_weights* w, const void
                           float* q_idx, float* w_idx, void* k_idx, void* ws, size_t ws_bytes,
                           hipStream_t stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, serving loops
+ * and harnesses that forbid hipMalloc): mla_decode with the same arguments minus the
+ * workspace, which comes from a static device buffer of the library instead,
+ * MLA_NOALLOC_SCRATCH_BYTES (64 MiB) on each GPU the library runs on, held until the process
+ * ends. The call allocates nothing. Its first call on a device looks the buffer's address up
+ * (hipGetSymbolAddress, with that device current); MLA_ERR_HIP if that fails.
+ *   Returns MLA_ERR_WORKSPACE, before touching the device, when the call would need more than
+ *   that (mla_workspace_bytes_ex(dims, B, 1, max_len, path, num_splits) > the buffer): e.g.
+ *   B = 32 at max_len 8193 needs 47 MiB, B = 4 at 131073 27 MiB, the DSA path at B = 8,
+ *   65537 25 MiB. Other errors as mla_decode.
+ *   Every call on one GPU shares the buffer: calls that overlap in time on one GPU (other
+ *   streams, other threads) race and must be serialised by the caller. Nothing in the buffer
+ *   needs to start at zero; the kernels clear what they count into. */
+#define MLA_NOALLOC_SCRATCH_BYTES (64 * 1024 * 1024)
+int mla_decode_noalloc(const mla_dims* dims, const mla_weights* w, const mla_cache* cache,
+                       const int32_t* seq_len, int32_t max_len, const void* x, int32_t B, int32_t path,
+                       int32_t num_splits, int32_t* sel_idx, int32_t* sel_cnt, void* y,
+                       int32_t out_dtype, hipStream_t stream);
+
 /* Cache append ([KV] update; [SK]; [DSA] eq. (7) and pseudocode).
  *   For b < B and i < T, at position p = pos[b] + i:
  *     latent[b,p] = c[b,i] ‖ r[b,i]
