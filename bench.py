@@ -501,6 +501,54 @@ def counter_pass(log):
     log("[counters] FP8 caches done")
 
 
+def cpu_decode_baselines(log):
+    """The oracle on sampled sequences of the decode workloads, in the GPU lines' unit (GB/s of
+    algorithmic bytes: 1,152 B per visible latent position; DSA: 256 B per index key plus 1,152 B
+    per selected position). Each sample is the first sequences of the GPU workload's own inputs
+    (the generators draw sequences in order)."""
+    import numpy as np
+
+    import oracle as O
+    from workloads import K3, bf16_bits_to_f32, make_index_prefix, make_latent_prefix, normal_bf16
+
+    d = K3
+    out = {}
+    for key, B, n_s, T, q_id in (("B32_T8192", 32, 4, 8192, 22), ("B4_T131072", 4, 1, 131072, 24)):
+        nv = T + 1
+        lat = bf16_bits_to_f32(make_latent_prefix(d, n_s, nv, seed=0)).astype(np.float64)
+        qt = bf16_bits_to_f32(normal_bf16((B, d.n_heads, d.d_latent), 0.05, 0, q_id)).astype(np.float64)[:n_s]
+        t0 = time.perf_counter()
+        for b in range(n_s):
+            O.attention_absorbed(qt[b][None, None], lat[b][None], O.softmax_scale(d), nv - 1, d)
+        dt = time.perf_counter() - t0
+        nbytes = n_s * nv * d.d_latent * 2
+        out[key] = {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "kind": "oracle",
+                    "sample": f"absorbed decode attention (oracle.attention_absorbed) of {n_s} of the {B} sequences, "
+                              f"{nv} visible positions each, {dt:.1f} s"}
+        log(f"[bench] CPU oracle decode {key}: {dt:.1f} s, {out[key]['value']} GB/s")
+        del lat
+    B, nv = 8, 65537
+    lat = bf16_bits_to_f32(make_latent_prefix(d, B, nv, seed=0)).astype(np.float64)
+    idx = bf16_bits_to_f32(make_index_prefix(d, B, nv, seed=0)).astype(np.float64)
+    rng = np.random.default_rng(25)
+    qi = rng.standard_normal((B, d.n_idx_heads, d.d_idx)).astype(np.float32) * np.float32(0.5)
+    wi = bf16_bits_to_f32(normal_bf16((B, d.n_idx_heads), 1.0, 0, 26)).astype(np.float64)
+    qt = bf16_bits_to_f32(normal_bf16((B, d.n_heads, d.d_latent), 0.05, 0, 27)).astype(np.float64)
+    t0 = time.perf_counter()
+    for b in range(B):
+        I = O.index_scores(qi[b].astype(np.float64), wi[b], idx[b], nv)
+        S = O.select_topk(I, d.topk)
+        O.attention_absorbed_subset(qt[b], lat[b], S, O.softmax_scale(d), d)
+    dt = time.perf_counter() - t0
+    nbytes = B * (nv * d.d_idx * 2 + d.topk * d.d_latent * 2)
+    out["dsa_B8_T65536"] = {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "kind": "oracle",
+                            "sample": f"index scores, top-{d.topk} and sparse attention (oracle.index_scores, "
+                                      f"select_topk, attention_absorbed_subset) of all {B} sequences, {nv} visible "
+                                      f"positions each, {dt:.1f} s"}
+    log(f"[bench] CPU oracle DSA decode: {dt:.1f} s, {out['dsa_B8_T65536']['value']} GB/s")
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -632,19 +680,23 @@ def main():
         log(f"[bench] CPU baseline: oracle prefill of the first {Ts} tokens")
         w64 = {k: bf16_bits_to_f32(v).astype(np.float64) for k, v in lw.w.items()}
         xs = bf16_bits_to_f32(x_bits[:, :Ts]).astype(np.float64)
+        cores = len(os.sched_getaffinity(0))
         try:
             from threadpoolctl import threadpool_info
-            threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+            blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
         except Exception:
-            threads = len(os.sched_getaffinity(0))
+            blas_threads = None
         t_a = time.perf_counter()
         O.layer_forward(xs, w64, O.Cache(d, 1), d)
         dt = time.perf_counter() - t_a
         pf, af = prefill_flops(d, Ts)
-        cpu = {"value": round((pf + af) / dt / 1e12, 5), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+        cpu = {"value": round((pf + af) / dt / 1e12, 5), "unit": "TFLOP/s", "cores": cores,
+               "blas_threads": blas_threads, "kind": "oracle",
                "sample": f"float64 NumPy oracle, full K3 layer prefill of the first {Ts} of the 4096 tokens "
-                         f"(B=1, same weights), {dt:.1f} s"}
-        log(f"[bench] CPU oracle: {dt:.1f} s, {cpu['value']} TFLOP/s on {threads} threads")
+                         f"(B=1, same weights), {dt:.1f} s; a sample, not the whole step"}
+        log(f"[bench] CPU oracle: {dt:.1f} s, {cpu['value']} TFLOP/s ({cores} cores, {blas_threads} BLAS threads)")
+        if not args.no_decode:
+            cpu["decode"] = cpu_decode_baselines(log)
 
     line = {
         "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,

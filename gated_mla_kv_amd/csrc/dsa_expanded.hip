@@ -186,13 +186,16 @@ __global__ __launch_bounds__(kScoreWaves * 64) void index_scores_kernel(IndexSco
 // flush overlap the other's scoring.
 constexpr int kRowsPerWg = 8, kRowBlock = 128;
 
-__global__ __launch_bounds__(kRowsPerWg * 64) void index_scores_rows_kernel(IndexScoreArgs a) {
+// at most 128 VGPRs, so that two 8-wave workgroups share a CU (four waves per SIMD)
+__global__ __launch_bounds__(kRowsPerWg * 64) __attribute__((amdgpu_waves_per_eu(4))) void index_scores_rows_kernel(IndexScoreArgs a) {
   constexpr int NIH = 32, DI = 128, KS = DI / 16;
   __shared__ __attribute__((aligned(16))) uint8_t keys_s[kRowBlock * DI * 2];
   // per-row histograms with 8-bit counters, four bins per word (a block puts at most 128 keys in a
   // bin): with the 32 KB key block this leaves room for two workgroups per CU
   __shared__ uint32_t hist4[kRowsPerWg * kHistBins / 4];
   __shared__ float kscale_s[kRowBlock];
+  // the rows' head weights times the score scale, read per tile (not held in registers)
+  __shared__ __attribute__((aligned(16))) float wgt_s[kRowsPerWg][32];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g2 = lane >> 5, l32 = lane & 31;
   const int p0 = blockIdx.x * kRowBlock;
@@ -211,16 +214,20 @@ __global__ __launch_bounds__(kRowsPerWg * 64) void index_scores_rows_kernel(Inde
   // the block's keys (positions past t_last repeat its last one; never scored)
   constexpr int NT = kRowsPerWg * 64;
   if (!fp8) {
-    u32x4 v[kRowBlock * 16 / NT];
+    // two passes of two 16-byte loads each (fewer registers live next to the query below)
 #pragma unroll
-    for (int k = 0; k < kRowBlock * 16 / NT; ++k) {
-      const int i = k * NT + tid, r = i >> 4, c = i & 15;
-      v[k] = ld16(a.idx_k + cache_row(a.pages, a.T_cap, seq, min(p0 + r, t_last - 1)) * DI + c * 8);
-    }
+    for (int h = 0; h < kRowBlock * 16 / NT; h += 2) {
+      u32x4 v[2];
 #pragma unroll
-    for (int k = 0; k < kRowBlock * 16 / NT; ++k) {
-      const int i = k * NT + tid, r = i >> 4, c = i & 15;
-      st16(keys_s + r * 256 + ((c ^ (r & 15)) << 4), v[k]);
+      for (int k = 0; k < 2; ++k) {
+        const int i = (h + k) * NT + tid, r = i >> 4, c = i & 15;
+        v[k] = ld16(a.idx_k + cache_row(a.pages, a.T_cap, seq, min(p0 + r, t_last - 1)) * DI + c * 8);
+      }
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int i = (h + k) * NT + tid, r = i >> 4, c = i & 15;
+        st16(keys_s + r * 256 + ((c ^ (r & 15)) << 4), v[k]);
+      }
     }
   } else {
     u32x4 v[kRowBlock * 8 / NT];
@@ -237,8 +244,8 @@ __global__ __launch_bounds__(kRowsPerWg * 64) void index_scores_rows_kernel(Inde
     for (int i = tid; i < kRowBlock; i += NT)
       kscale_s[i] = a.idx_scale[cache_row(a.pages, a.T_cap, seq, min(p0 + i, t_last - 1))];
   }
+  if (b < a.B && lane < 32) wgt_s[wave][lane] = a.w_idx[(size_t)b * NIH + lane] * a.scale;
   u32x4 qa[KS], ql[KS];  // q^I as bf16 hi + lo pairs, as in index_scores_kernel
-  float wgt[16];
   if (b < a.B) {
     const float* qrow = a.q_idx + ((size_t)b * NIH + l32) * DI;
 #pragma unroll
@@ -251,10 +258,8 @@ __global__ __launch_bounds__(kRowsPerWg * 64) void index_scores_rows_kernel(Inde
       qa[s] = u32x4{h[0], h[1], h[2], h[3]};
       ql[s] = u32x4{l[0], l[1], l[2], l[3]};
     }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) wgt[r] = a.w_idx[(size_t)b * NIH + (r >> 2) * 8 + g2 * 4 + (r & 3)] * a.scale;
   }
-  __syncthreads();  // keys staged, histograms cleared
+  __syncthreads();  // keys staged, histograms cleared, head weights staged
   for (int j = 0; j < kRowBlock / 32 && p0 + 32 * j < t; ++j) {
     const int r = 32 * j + l32;  // key row of this lane
     f32x16 acc = f32x16{};
@@ -275,9 +280,14 @@ __global__ __launch_bounds__(kRowsPerWg * 64) void index_scores_rows_kernel(Inde
         acc = mfma32(ql[s], kv, acc);
       }
     }
+    // acc[4 qq + e] holds head 8 qq + 4 g2 + e
     float sc = 0.f;
 #pragma unroll
-    for (int q = 0; q < 16; ++q) sc += wgt[q] * fmaxf(acc[q], 0.f);
+    for (int qq = 0; qq < 4; ++qq) {
+      const f32x4 wv = *(const f32x4*)&wgt_s[wave][8 * qq + 4 * g2];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sc += wv[e] * fmaxf(acc[4 * qq + e], 0.f);
+    }
     sc += __shfl_xor(sc, 32, 64);
     if (fp8) sc *= kscale_s[r];
     const int pos = p0 + r;
