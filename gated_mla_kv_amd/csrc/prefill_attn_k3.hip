@@ -15,8 +15,8 @@
 //   B operand P^T of O^T = V^T P^T directly; V^T comes from row-major V through
 //   ds_read_b64_tr_b16.
 // * 64-key K/V tiles (24 KB + 16 KB) are copied HBM/L2 -> LDS by global_load_lds_dwordx4 into a
-//   3-slot ring (16-byte chunks XOR-swizzled per row), two tiles ahead of use; one barrier per
-//   tile.
+//   4-slot ring filling the CU's 160 KB (16-byte chunks XOR-swizzled per row), issued four tiles
+//   ahead of their P.V (the scores run two sub-tiles ahead of it); one barrier per tile.
 // * Software pipeline over 32-key sub-tiles u inside each wave: step u issues the score MFMAs of
 //   u+2 and the P.V MFMAs of u, and runs the softmax of u+1 on the VALU between them.
 // * The running max moves only when it grows by more than 8 (base 2); otherwise the rescale
@@ -38,7 +38,7 @@ constexpr int KCH = DQK / 8, VCH = DV / 8;    // 16-byte chunks per K / V row
 constexpr int KROWB = DQK * 2, VROWB = DV * 2;
 constexpr int KBYTES = BKV * KROWB, VBYTES = BKV * VROWB;
 constexpr int SLOT = KBYTES + VBYTES;         // 40 KB
-constexpr int NSLOT = 3;
+constexpr int NSLOT = 4;                      // the ring fills the CU's 160 KB of LDS
 constexpr int NLOAD_K = KBYTES / 1024;
 constexpr int KS = DQK / 16;                  // score k-steps
 constexpr float RESCALE_SLACK = 8.0f;
@@ -81,7 +81,7 @@ __device__ __forceinline__ int k3_job_tiles(const PrefillAttnArgs& a, int bh, in
 
 // One (b*H + h, query tile) job of a workgroup; `ring` is the workgroup's K/V ring. Every LDS
 // read of a job happens before its last barrier, so jobs can follow each other without one.
-// With `ahead` the job's first three K/V tiles are already in flight (issued by the previous job
+// With `ahead` the job's first NSLOT K/V tiles are already in flight (issued by the previous job
 // of this workgroup); with next_bh >= 0 this job issues the first tiles of job (next_bh, next_qt)
 // into the free ring right after its last barrier, ahead of its own epilogue.
 template <int QB>
@@ -178,9 +178,8 @@ __device__ __forceinline__ void prefill_k3_job(const PrefillAttnArgs& a, uint8_t
     for (int s = 0; s < KS; ++s) qf[qb][s] = ld16(qrow + s * 16);
   }
   if (!ahead) {
-    issue(0);
-    issue(1);
-    issue(2);
+#pragma unroll
+    for (int t = 0; t < NSLOT; ++t) issue(t);
   }
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb)
@@ -328,53 +327,62 @@ __device__ __forceinline__ void prefill_k3_job(const PrefillAttnArgs& a, uint8_t
 #pragma unroll
     for (int s = 0; s < KPF; ++s) kf[s] = kread(s);
     sacc[p][0] = f32x16{};
+    // (the scheduling barriers keep each read KPF / two MFMAs ahead of its use: left free, the
+    // compiler sank the reads next to their MFMAs, and every MFMA waited out an LDS latency)
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       const u32x4 cur = kf[s % KPF];
       if (s + KPF < KS) kf[s % KPF] = kread(s + KPF);
       else if (s + KPF - KS < 2) vf[s + KPF - KS] = vread(s + KPF - KS);
       sacc[p][0] = mfma32(cur, qf[0][s], sacc[p][0]);
+      __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const u32x4 cur = vf[i & 1];
       if (i + 2 < 8) vf[i & 1] = vread(i + 2);
       o[i & 3][0] = mfma32(cur, pb[p][i >> 2][0], o[i & 3][0]);
+      __builtin_amdgcn_sched_barrier(0);
     }
     softmax(u + 1, ic<1 - p>{});
     rescale();
   };
 
+  // vmcnt wait leaving at most n of this wave's most recent tiles in flight
+  auto wait_tiles = [&](int n) __attribute__((always_inline)) {
+    if (n >= 3)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * NLOAD_W) : "memory");
+    else if (n == 2)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * NLOAD_W) : "memory");
+    else if (n == 1)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NLOAD_W) : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  };
+  static_assert(NSLOT == 4, "wait_tiles covers three tiles in flight");
   // ---- prologue: tile 0 -> scores of sub-tiles 0 and 1, softmax of 0 ----
   // (tiles issued ahead precede this job's q loads in the wave's memory queue: wait for all)
+  const int issued0 = min(n_tiles, NSLOT);
   if (ahead)
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  else if (n_tiles >= 3)
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * NLOAD_W) : "memory");
-  else if (n_tiles == 2)
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NLOAD_W) : "memory");
   else
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    wait_tiles(issued0 - 1);
   __syncthreads();
   scores(0, ic<0>{});
   scores(1, ic<1>{});
   if (mv == 0) apply_mask(0, ic<0>{});
   softmax(0, ic<0>{});  // alpha = 0 here, on accumulators that are still 0
-  if (ahead)
-    ;
-  else if (n_tiles >= 3)
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NLOAD_W) : "memory");
-  else
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if (!ahead) wait_tiles(max(issued0 - 2, 0));
   __syncthreads();  // tile 1 is in LDS
 
-  // ---- main loop: tile t holds sub-tiles 2t, 2t+1; tile t+2 is in flight ----
+  // ---- main loop: tile t holds sub-tiles 2t, 2t+1; tiles t+2 and t+3 are in flight ----
   for (int t = 0; t < n_tiles; ++t) {
     step(2 * t, ic<0>{});
     step(2 * t + 1, ic<1>{});
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // own share of tile t+2 has landed
-    __syncthreads();                                   // ... everyone's; slot of tile t is free
-    issue(t + 3);
+    // own share of tile t+2 has landed (tiles up to t+3 are issued; t+3 may stay in flight)
+    wait_tiles(t + 3 < n_tiles ? 1 : 0);
+    __syncthreads();  // ... everyone's; slot of tile t is free
+    issue(t + NSLOT);
   }
 
   // ---- the next job's first tiles: the ring is free once every wave has passed the barrier ----
@@ -383,9 +391,8 @@ __device__ __forceinline__ void prefill_k3_job(const PrefillAttnArgs& a, uint8_t
     const int nt = k3_job_tiles(a, next_bh, next_qt, &nk);
     const uint16_t* kb = a.k + (size_t)next_bh * a.T_cap * DQK;
     const uint16_t* vb = a.v + (size_t)next_bh * a.T_cap * DV;
-    issue_for(kb, vb, nk, nt, 0);
-    issue_for(kb, vb, nk, nt, 1);
-    issue_for(kb, vb, nk, nt, 2);
+#pragma unroll
+    for (int t = 0; t < NSLOT; ++t) issue_for(kb, vb, nk, nt, t);
   }
 
   // ---- epilogue: normalise, gate, store ----
@@ -445,20 +452,23 @@ __global__ __launch_bounds__(k3pre::Cfg<QB>::NT) void prefill_attn_k3_kernel(Pre
     for (int p = blockIdx.x; p < n_pairs; p += n_wg) {
       const int xcd = p & 7, local = p >> 3;
       const int bh = (local / half) * 8 + xcd, j = local % half;
+      // odd workgroups take the short query tile of each pair first, so that the epilogues (gate
+      // loads, output stores) of neighbouring workgroups do not all fall at the same moment
+      const bool short_first = blockIdx.x & 8;
 #pragma unroll 1
       for (int k = 0; k < 2; ++k) {
         // the job after this one: the pair's second tile, else the first tile of the next pair
-        int nbh = bh, nq = j;
+        int nbh = bh, nq = (k == 0) != short_first ? j : nqt - 1 - j;
         if (k == 1) {
           const int pn = p + n_wg;
           nbh = -1;
           if (pn < n_pairs) {
             const int ln = pn >> 3;
             nbh = (ln / half) * 8 + (pn & 7);
-            nq = nqt - 1 - ln % half;
+            nq = short_first ? ln % half : nqt - 1 - ln % half;
           }
         }
-        prefill_k3_job<QB>(a, ring, bh, k == 0 ? nqt - 1 - j : j, !(p == (int)blockIdx.x && k == 0), nbh, nq);
+        prefill_k3_job<QB>(a, ring, bh, (k == 0) != short_first ? nqt - 1 - j : j, !(p == (int)blockIdx.x && k == 0), nbh, nq);
       }
     }
     return;
