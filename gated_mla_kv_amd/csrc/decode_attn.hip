@@ -130,13 +130,17 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeAttnArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int j = j0 + 16 * (r >> 3) + 8 * g2 + (r & 7);
-        const float x = (j < p1) ? sacc[r] * sl2 : -INFINITY;
+        // a gathered position outside the cache gets probability 0
+        const bool live = j < p1 && (!GATHER || (sel[j] >= 0 && sel[j] < a.T_cap));
+        const float x = live ? sacc[r] * sl2 : -INFINITY;
         sacc[r] = x;
         mt = fmaxf(mt, x);
       }
       mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
       const float m_new = fmaxf(m_run, mt);
-      const float alpha = fast_exp2(m_run - m_new);
+      // while no position has been live, every p is 0 (not exp2(-inf + inf))
+      const float m_ref = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = fast_exp2(m_run - m_ref);
       m_run = m_new;
       float ls = 0.f;
 #pragma unroll
@@ -144,7 +148,7 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeAttnArgs a) {
         float p[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          p[i] = fast_exp2(sacc[hh * 8 + i] - m_new);
+          p[i] = fast_exp2(sacc[hh * 8 + i] - m_ref);
           ls += p[i];
         }
         st16(&Ps[head * C::PROW + hh * 16 + g2 * 8],

@@ -105,6 +105,7 @@ __global__ __launch_bounds__(k3dec::NTHREADS) void decode_attn_k3_kernel(DecodeA
   __shared__ __attribute__((aligned(16))) uint16_t Ps[2][H * PROW];
   __shared__ float alpha_s[2][H];
   __shared__ int sel_s[GATHER ? MAX_SEL : 1];
+  __shared__ int wcnt_s[GATHER ? 8 : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g2 = lane >> 5, l32 = lane & 31;
@@ -114,8 +115,7 @@ __global__ __launch_bounds__(k3dec::NTHREADS) void decode_attn_k3_kernel(DecodeA
   const int n_vis = GATHER ? min(a.sel_cnt[b], a.sel_stride) : min(a.n_vis[b] + a.vis_offset, a.T_cap);
   const int p0 = split * a.chunk;
   const int p1 = min(p0 + a.chunk, n_vis);
-  const int n_pos = GATHER ? min(max(p1 - p0, 0), MAX_SEL) : max(p1 - p0, 0);
-  const int n_tiles = (n_pos + BT - 1) / BT;
+  int n_pos = GATHER ? min(max(p1 - p0, 0), MAX_SEL) : max(p1 - p0, 0);
   // cache rows: unpaged, position p of this sequence is row p past lat; paged, the page table
   // gives the row within the pool (lat = the pool)
   const int seq = row_map(a.row0, a.rows_per_seq, b).seq;
@@ -129,14 +129,27 @@ __global__ __launch_bounds__(k3dec::NTHREADS) void decode_attn_k3_kernel(DecodeA
   };
   const uint16_t* lat = a.latent + seq_rows * DL;
 
-  if (GATHER) {  // this split's selected positions, clamped into the cache, as cache rows
+  if (GATHER) {
+    // this split's selected positions as cache rows, in order, leaving out any outside [0, T_cap)
+    // (they get probability 0): a stable compaction by wave ballots, 448 entries per round
     const int32_t* sel = a.sel_idx + (size_t)b * a.sel_stride;
-    for (int i = tid; i < n_pos; i += NTHREADS) {
-      const int p = sel[p0 + i];
-      sel_s[i] = crow((p >= 0 && p < a.T_cap) ? p : 0);
+    int n_ok = 0;
+    for (int base = 0; base < n_pos; base += NTHREADS) {
+      const int i = base + tid;
+      const int p = i < n_pos ? sel[p0 + i] : -1;
+      const bool ok = p >= 0 && p < a.T_cap;
+      const uint64_t m = __ballot(ok);
+      if (lane == 0) wcnt_s[wave] = __popcll(m);
+      __syncthreads();
+      int before = n_ok;
+      for (int w = 0; w < wave; ++w) before += wcnt_s[w];
+      if (ok) sel_s[before + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u))] = crow(p);
+      for (int w = 0; w < NTHREADS / 64; ++w) n_ok += wcnt_s[w];
+      __syncthreads();
     }
-    __syncthreads();
+    n_pos = n_ok;
   }
+  const int n_tiles = (n_pos + BT - 1) / BT;
 
   const float sl2 = a.scale * 1.4426950408889634f;
   const size_t part = (size_t)b * a.n_splits + split;

@@ -315,8 +315,10 @@ int mla_decode_attention(const mla_dims* dims, const void* q_tilde, const mla_ca
                          size_t ws_bytes, hipStream_t stream);
 
 /* Sparse absorbed decode attention ([DSA] eq. (9) over S_t): as mla_decode_attention but over
- * the positions sel_idx[b, 0..sel_cnt[b]) only (sel_idx [B,topk] i32, every entry a valid
- * position < T_cap). ws: mla_workspace_bytes_ex(dims, B, 1, topk, MLA_PATH_SPARSE, num_splits). */
+ * the positions sel_idx[b, 0..sel_cnt[b]) only (sel_idx [B,topk] i32). An entry outside
+ * [0, T_cap) is left out of the softmax (probability 0); a row with no valid entry gives
+ * o_latent = 0 and lse = -inf. ws: mla_workspace_bytes_ex(dims, B, 1, topk, MLA_PATH_SPARSE,
+ * num_splits). */
 int mla_sparse_attention(const mla_dims* dims, const void* q_tilde, const mla_cache* cache,
                          const int32_t* sel_idx, const int32_t* sel_cnt, int32_t B,
                          int32_t num_splits, float* o_latent, float* lse, void* ws,

@@ -209,6 +209,47 @@ def test_sparse_attention():
         check_scores(to_np(lse[b]), lse_ref, f"sparse lse b={b}")
 
 
+@pytest.mark.parametrize("splits", [0, 2])
+def test_sparse_attention_leaves_out_positions_outside_the_cache(splits):
+    """Selected entries outside [0, T_cap) (-1, T_cap, larger) among the first sel_cnt get
+    probability 0: the result is the oracle's attention over the valid entries alone. A row with no
+    valid entry gives o = 0 and lse = -inf; with two splits, one split of a row can be all invalid."""
+    d = K3_SMALL_TOPK
+    B, H, T_cap = 4, d.n_heads, 300
+    rng = np.random.default_rng(43)
+    sel = np.full((B, d.topk), -1, np.int32)
+    cnts = [40, 64, 10, 64]
+    valid = []
+    for b, c in enumerate(cnts):
+        v = np.sort(rng.choice(T_cap, size=c, replace=False)).astype(np.int32)
+        bad = rng.random(c) < 0.3
+        v[bad] = rng.choice([-1, T_cap, T_cap + 7, -1000], size=int(bad.sum()))
+        if b == 2:
+            v[:] = -1                       # nothing valid
+        if b == 3:
+            v[:32] = T_cap                  # the first split (32 entries) all invalid
+        sel[b, :c] = v
+        valid.append(v[(v >= 0) & (v < T_cap)])
+    qt = rand_bf16((B, H, d.d_latent), 44, std=0.05)
+    lat = rand_bf16((B, T_cap, d.d_latent), 45)
+    dims_c = gm.make_dims(d)
+    Ld = dev_bf16(lat)
+    cache = gm.MlaCache(Ld.data_ptr(), None, None, None, B, T_cap)
+    o = torch.full((B, H, d.kv_lora), float("nan"), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, H), dtype=torch.float32, device="cuda")
+    ws = torch.empty(gm.workspace_bytes(dims_c, B, 1, d.topk, gm.PATH_SPARSE, splits), dtype=torch.uint8,
+                     device="cuda")
+    gm.mla_sparse_attention(dims_c, dev_bf16(qt), cache, i32(sel), i32(cnts), B, o, lse, splits, ws)
+    _sync()
+    for b in range(B):
+        if len(valid[b]) == 0:
+            assert torch.count_nonzero(o[b]) == 0 and bool(torch.isinf(lse[b]).all()) and bool((lse[b] < 0).all())
+            continue
+        o_ref, lse_ref = O.attention_absorbed_subset(f64(qt[b]), f64(lat[b]), valid[b], O.softmax_scale(d), d)
+        check_rows(to_np(o[b]), o_ref, f"sparse o b={b} (valid entries only)")
+        check_scores(to_np(lse[b]), lse_ref, f"sparse lse b={b}")
+
+
 @pytest.mark.parametrize("dims,n_vis", [(K3, [1, 300, 65]), (TINY, [1, 70])])
 def test_expanded_attention(dims, n_vis):
     d = dims
