@@ -368,15 +368,26 @@ __global__ __launch_bounds__(k3dec::NTHREADS) void decode_attn_k3_kernel(DecodeA
         }
         // rows past the end repeat a valid row (masked)
         if constexpr (GATHER) {
-          // gathered rows: all nine source rows are read from LDS together, then the nine loads
-          // (faster than three at a time although it spills a few registers)
-          int rows[NLOAD_W];
+          // gathered rows, three loads at a time: the lane's chunk geometry is recomputed on every
+          // call from an opaque copy of the lane id. Held across the loop, the nine offsets spill
+          // next to the accumulators, and reloading a spill waits for every load in flight,
+          // the tiles' DMA included.
+          int ln = lane;
+          asm volatile("" : "+v"(ln));
 #pragma unroll
-          for (int k = 0; k < NLOAD_W; ++k) rows[k] = sel_s[min(j0 + (int)(doff[k] >> 16), n_pos - 1)];
+          for (int k0 = 0; k0 < NLOAD_W; k0 += 3) {
+            int rows[3];
+            uint32_t coff[3];
 #pragma unroll
-          for (int k = 0; k < NLOAD_W; ++k) {
-            const uint32_t coff = (doff[k] & 0xFFFFu) - (doff[k] >> 16) * (DL * 2);  // the chunk's byte offset
-            lds_dma16((const char*)lat + (size_t)rows[k] * (DL * 2) + coff, slot_addr + (pw * NLOAD_W + k) * 1024);
+            for (int k = 0; k < 3; ++k) {
+              const int P = (pw * NLOAD_W + k0 + k) * 64 + ln;
+              const int r = P / CH;
+              coff[k] = (uint32_t)(((P - r * CH) ^ swz_row(r)) << 4);
+              rows[k] = sel_s[min(j0 + r, n_pos - 1)];
+            }
+#pragma unroll
+            for (int k = 0; k < 3; ++k)
+              lds_dma16((const char*)lat + (size_t)rows[k] * (DL * 2) + coff[k], slot_addr + (pw * NLOAD_W + k0 + k) * 1024);
           }
         } else {
           // the partial last tile of a split: consecutive rows (a rolled loop keeps the P.V waves'
@@ -514,19 +525,32 @@ __global__ __launch_bounds__(k3dec::NTHREADS) void decode_attn_k3_kernel(DecodeA
       }
       return;
     }
+    // The wave's 96 x 128 fp16 block is staged in LDS (every tile has landed and been read by
+    // now, so the ring is free), so that the stores are whole 256-byte head rows: written from the
+    // accumulators, a store covers 16 bytes of each of 32 head rows. Head h's 16-byte chunk c sits
+    // at h*256 + (c ^ (h & 15))*16 of the wave's 24 KB region.
+    uint8_t* stage = (FP8 ? f8_s[0] : lat_s[0]) + pw * (H * 256);
+    static_assert((FP8 ? NS8 * F8SLOT : NSLOT * TILE_BYTES) >= 4 * H * 256, "staging fits the ring");
 #pragma unroll
     for (int hs = 0; hs < 3; ++hs) {
-      const float inv = alpha_s[0][hs * 32 + l32];
-      uint16_t* dst = a.part_o + (part * H + hs * 32 + l32) * L;
+      const int h = hs * 32 + l32;
+      const float inv = alpha_s[0][h];
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
         for (int rb = 0; rb < 4; ++rb) {
-          const int f = (pw * 4 + dt) * 32 + rb * 8 + g2 * 4;
           const f32x4 v = f32x4{o[dt][hs][rb * 4 + 0], o[dt][hs][rb * 4 + 1], o[dt][hs][rb * 4 + 2],
                                 o[dt][hs][rb * 4 + 3]} * inv;
-          *(u32x2*)(dst + f) = u32x2{pack_f16x2(v[0], v[1]), pack_f16x2(v[2], v[3])};
+          *(u32x2*)(stage + h * 256 + (((dt * 4 + rb) ^ (h & 15)) << 4) + g2 * 8) =
+              u32x2{pack_f16x2(v[0], v[1]), pack_f16x2(v[2], v[3])};
         }
+    }
+    const int j = lane & 15;
+#pragma unroll 4
+    for (int i = 0; i < H / 4; ++i) {
+      const int h = i * 4 + (lane >> 4);
+      const u32x4 v = *(const u32x4*)(stage + h * 256 + ((j ^ (h & 15)) << 4));
+      *(u32x4*)(a.part_o + (part * H + h) * L + pw * 128 + j * 8) = v;
     }
   }
 }
