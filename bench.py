@@ -401,7 +401,8 @@ def dsa_prefill_bench(args, lw, log):
 
 
 def counter_pass(log):
-    """--counters: each measured kernel launched twice at the bench's shapes, and a plain device
+    """--counters: each measured kernel launched twice at the bench's shapes (the four prefill GEMMs
+    in the order x_proj, q_b, kv_b, o_proj, then the prefill attention and the decode kernels), and a plain device
     copy of 256 MiB (reads 256 MiB, writes 256 MiB) that calibrates rocprofv3's FETCH_SIZE and
     WRITE_SIZE, for counter runs (rocprofv3 --pmc ... -- python3 bench.py --counters)."""
     import torch
@@ -427,6 +428,18 @@ def counter_pass(log):
     for _ in range(2):
         gm.mla_gemm(x, d.hidden, w_x, T, w_x.shape[0], d.hidden, out_x, w_x.shape[0], gm.OUT_F32)
     del out_x, w_x
+    cq = device_normal_bf16((T, d.q_lora), 1.0, 9, 16)
+    w_qb = device_normal_bf16((H * d.d_qk, d.q_lora), 0.02, 9, 17)
+    qb = torch.empty((T, H * d.d_qk), dtype=torch.bfloat16, device=dev)
+    for _ in range(2):
+        gm.mla_gemm(cq, d.q_lora, w_qb, T, H * d.d_qk, d.q_lora, qb, H * d.d_qk)
+    del cq, w_qb, qb
+    c = device_normal_bf16((T, d.kv_lora), 1.0, 9, 18)
+    w_kvb = device_normal_bf16((H * (d.d_nope + d.d_v), d.kv_lora), 0.02, 9, 19)
+    kvb = torch.empty((T, H * (d.d_nope + d.d_v)), dtype=torch.bfloat16, device=dev)
+    for _ in range(2):
+        gm.mla_gemm(c, d.kv_lora, w_kvb, T, H * (d.d_nope + d.d_v), d.kv_lora, kvb, H * (d.d_nope + d.d_v))
+    del c, w_kvb, kvb
     u = device_normal_bf16((T, H * d.d_v), 1.0, 9, 3)
     w_o = device_normal_bf16((d.hidden, H * d.d_v), 0.02, 9, 4)
     y = torch.empty((T, d.hidden), dtype=torch.bfloat16, device=dev)
