@@ -17,7 +17,7 @@ __all__ = [
     "mla_decode_noalloc", "NOALLOC_SCRATCH_BYTES", "kv_append", "dsa_index_topk", "dsa_index_topk_fp8", "mla_index_projections", "mla_gemm",
     "mla_rmsnorm", "mla_layernorm", "mla_prefill_attention", "mla_absorb_query",
     "mla_decode_attention", "mla_sparse_attention", "mla_expanded_attention", "mla_value_up_gate",
-    "LIB_PATH",
+    "mla_debug_scores", "DEBUG_SCORES_MAX", "LIB_PATH",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgmla.so")
@@ -26,6 +26,7 @@ OUT_BF16, OUT_F32 = 0, 1
 PATH_ABSORBED, PATH_EXPANDED, PATH_SPARSE = 0, 1, 2
 CACHE_BF16, CACHE_FP8 = 0, 1
 FP8_LATENT_ROW_BYTES = 656  # 512 E4M3 codes, four fp32 scales, 64 bf16 shared-key values
+DEBUG_SCORES_MAX = 1 << 26  # MLA_DEBUG_SCORES_MAX: most logits one mla_debug_scores call writes
 
 
 class GmlaError(RuntimeError):
@@ -84,6 +85,7 @@ _SIGS = {
     "mla_sparse_attention": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _I, _P, _P, _P, _SZ, _P]),
     "mla_expanded_attention": (ctypes.c_int, [_P, _P, _P, _P, _I, _I, _P, _P, _P]),
     "mla_value_up_gate": (ctypes.c_int, [_P, _P, _P, _P, _I, _P, _I, _P]),
+    "mla_debug_scores": (ctypes.c_int, [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P]),
 }
 
 
@@ -273,3 +275,8 @@ def mla_expanded_attention(dims, q, cache: MlaCache, n_visible, max_visible, B, 
 def mla_value_up_gate(dims, o_latent, w_kv_b, g_pre, B, u, out_dtype=OUT_BF16, stream=None):
     _check(lib().mla_value_up_gate(ctypes.byref(dims), _p(o_latent), _p(w_kv_b), _p(g_pre), B, _p(u),
                                    out_dtype, _stream(stream)), "mla_value_up_gate")
+
+
+def mla_debug_scores(dims, q, k, k_heads, B, Tq, Tk, D, logits, stream=None):
+    _check(lib().mla_debug_scores(ctypes.byref(dims), _p(q), _p(k), k_heads, B, Tq, Tk, D, _p(logits),
+                                  _stream(stream)), "mla_debug_scores")

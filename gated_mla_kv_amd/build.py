@@ -27,7 +27,7 @@ FLAGS = [
 ]
 SOURCES = ["api.cpp", "gemm.hip", "norm_append.hip", "prefill_attn.hip", "prefill_attn_k3.hip",
            "decode_attn.hip",
-           "decode_attn_k3.hip", "dsa_expanded.hip"]
+           "decode_attn_k3.hip", "dsa_expanded.hip", "scores.hip"]
 
 
 def _hipcc() -> str:

@@ -499,6 +499,33 @@ int mla_expanded_attention(const mla_dims* d, const void* q, const mla_cache* ca
   return MLA_OK;
 }
 
+int mla_debug_scores(const mla_dims* d, const void* q, const void* k, int32_t k_heads, int32_t B, int32_t Tq,
+                     int32_t Tk, int32_t D, float* logits, hipStream_t stream) {
+  Shape s;
+  if (!d) return MLA_ERR_NULL;
+  if (!shape_of(d, &s)) return MLA_ERR_UNSUPPORTED;
+  if (B < 0 || Tq < 0 || Tk < 0) return MLA_ERR_SHAPE;
+  if (D != d->d_nope + d->d_shared && D != d->kv_lora + d->d_shared) return MLA_ERR_SHAPE;
+  if (k_heads != 1 && k_heads != d->n_heads) return MLA_ERR_SHAPE;
+  if ((size_t)B * d->n_heads * Tq * Tk > MLA_DEBUG_SCORES_MAX) return MLA_ERR_SHAPE;
+  if (B == 0 || Tq == 0 || Tk == 0) return MLA_OK;
+  if (!q || !k || !logits) return MLA_ERR_NULL;
+  if (((uintptr_t)q & 15) != 0 || ((uintptr_t)k & 15) != 0) return MLA_ERR_SHAPE;
+  ScoresArgs a{};
+  a.q = (const uint16_t*)q;
+  a.k = (const uint16_t*)k;
+  a.B = B;
+  a.H = d->n_heads;
+  a.Hk = k_heads;
+  a.Tq = Tq;
+  a.Tk = Tk;
+  a.D = D;
+  a.scale = d->softmax_scale;
+  a.logits = logits;
+  CHECK_HIP(launch_debug_scores(a, stream));
+  return MLA_OK;
+}
+
 int mla_value_up_gate(const mla_dims* d, const float* o_latent, const void* w_kv_b, const float* g_pre,
                       int32_t B, void* u, int32_t out_dtype, hipStream_t stream) {
   Shape s;

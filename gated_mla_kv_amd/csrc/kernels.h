@@ -170,6 +170,15 @@ struct ExpandedAttnArgs {
   float* z;    // [B, H, DV]
   float* lse;  // [B, H] or null
 };
+// Raw attention logits s[b,h,i,j] = scale * q[b,i,h,:] . k[b, Hk == 1 ? 0 : h, j, :] (unmasked)
+struct ScoresArgs {
+  const uint16_t* q;  // [B, Tq, H, D] bf16
+  const uint16_t* k;  // [B, Hk, Tk, D] bf16, Hk = H or 1
+  int B, H, Hk, Tq, Tk, D;  // D a multiple of 8
+  float scale;
+  float* logits;      // [B, H, Tq, Tk]
+};
+hipError_t launch_debug_scores(const ScoresArgs& a, hipStream_t st);
 hipError_t launch_expanded_attention(Shape s, const ExpandedAttnArgs& a, hipStream_t st);
 hipError_t launch_gate_mul(const float* z, const float* g_pre, int n, void* u, int u_f32,
                            hipStream_t st);

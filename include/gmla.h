@@ -337,6 +337,21 @@ int mla_value_up_gate(const mla_dims* dims, const float* o_latent, const void* w
                       const float* g_pre, int32_t B, void* u, int32_t out_dtype,
                       hipStream_t stream);
 
+/* Raw attention logits, for checking the score computation on small shapes: the argument of the
+ * softmax in [DSA] eq. (9) (the eager softmax(q k^T * scale) of the Kimi K2 KV-cache card), with
+ * no causal mask:
+ *   logits[b,h,i,j] = dims->softmax_scale * sum_d q[b,i,h,d] * k[b,hk,j,d],  hk = (k_heads == 1 ? 0 : h)
+ *   q [B,Tq,H,D] bf16; k [B,k_heads,Tk,D] bf16; logits [B,H,Tq,Tk] f32 (every (i, j) written).
+ *   D = d_nope + d_shared with per-head keys (k_heads = H: the expanded form [KV]), or
+ *   D = kv_lora + d_shared with k_heads = 1 (the absorbed form: q~ against the latent rows
+ *   [c ; r] every head shares, [DSA] note after eq. (10)). q and k 16-byte aligned.
+ *   Products as in the attention kernels: bf16 operands, fp32 accumulation.
+ *   B * H * Tq * Tk may not exceed MLA_DEBUG_SCORES_MAX (MLA_ERR_SHAPE): a debugging aid, not a
+ *   fast path. */
+#define MLA_DEBUG_SCORES_MAX ((size_t)1 << 26)
+int mla_debug_scores(const mla_dims* dims, const void* q, const void* k, int32_t k_heads, int32_t B,
+                     int32_t Tq, int32_t Tk, int32_t D, float* logits, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -38,7 +38,7 @@ from . import fp8
 
 __all__ = [
     "round_to_bf16", "rms_norm", "layer_norm", "linear", "sigmoid", "softmax_scale",
-    "Cache", "query_path", "kv_down_path", "kv_up", "expand_keys", "attention_expanded",
+    "Cache", "query_path", "kv_down_path", "kv_up", "expand_keys", "attention_expanded", "attention_logits",
     "absorbed_query", "attention_absorbed", "value_up", "gate_output", "layer_forward",
     "index_projections", "index_scores", "select_topk", "attention_absorbed_subset",
     "dsa_decode_step", "dsa_prefill", "cache_values_per_position",
@@ -269,6 +269,19 @@ def attention_expanded(q, k, v, scale: float, offset: int):
     z = np.einsum("bhtn,bhnd->bhtd", p / l, v)
     lse = (m + np.log(l))[..., 0]
     return z.transpose(0, 2, 1, 3), lse
+
+
+def attention_logits(q, k, scale: float):
+    """The attention logits before the mask and the softmax: s[b,h,i,j] = (q_{b,i,h} . k_{b,h,j})
+    * scale, the argument of the softmax in [DSA] eq. (9) ([K2] eager form q k^T * scale).
+
+    q [B,T,H,D]; k [B,H,N,D] (per-head keys, the expanded form) or [B,1,N,D] (one row per
+    position shared by every head: the latent [c ; r] of the absorbed form). Returns s [B,H,T,N]
+    for every (i, j), with no mask.
+    """
+    B, T, H, D = q.shape
+    kk = np.broadcast_to(k, (B, H) + k.shape[2:])
+    return np.einsum("bthd,bhnd->bhtn", q, kk) * scale
 
 
 def absorbed_query(q_nope, q_shared, w, dims):

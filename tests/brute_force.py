@@ -88,3 +88,25 @@ def brute_index_projections(x, W, dims):
     k = [(v[e] - mean) / math.sqrt(var + dims.ln_eps) * W["g_idx_k"][e] + W["b_idx_k"][e] for e in range(d)]
     a = _matvec(W["w_idx_w"], x)
     return q, k, a
+
+
+def brute_attention_logits(q, k, scale):
+    """s[b][h][i][j] = scale * sum_d q[b][i][h][d] * k[b][hk][j][d], where hk = h, or 0 when k
+    holds one key row per position for every head. q: nested lists [B][T][H][D]; k: [B][Hk][N][D]."""
+    out = []
+    for b in range(len(q)):
+        per_head = []
+        for h in range(len(q[b][0])):
+            hk = 0 if len(k[b]) == 1 else h
+            rows = []
+            for i in range(len(q[b])):
+                row = []
+                for j in range(len(k[b][hk])):
+                    acc = 0.0
+                    for e in range(len(q[b][i][h])):
+                        acc += q[b][i][h][e] * k[b][hk][j][e]
+                    row.append(scale * acc)
+                rows.append(row)
+            per_head.append(rows)
+        out.append(per_head)
+    return out

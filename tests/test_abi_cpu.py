@@ -220,3 +220,17 @@ def test_index_projections_validation():
     assert call(M=0) == OK
     assert call(ws_bytes=100) == ERR_WORKSPACE
     assert call(ws_bytes=gm.workspace_bytes(d, 4, 1, 1, gm.PATH_SPARSE) - 1) == ERR_WORKSPACE
+
+
+def test_debug_scores_validation():
+    L = gm.lib()
+    d = gm.make_dims(K3)
+
+    def call(q, k, hk, B, Tq, Tk, D, out):
+        return L.mla_debug_scores(ctypes.byref(d), q, k, hk, B, Tq, Tk, D, out, None)
+    assert call(FAKE, FAKE, 96, 1, 4, 4, 100, FAKE) == ERR_SHAPE        # D neither d_qk nor d_latent
+    assert call(FAKE, FAKE, 2, 1, 4, 4, 192, FAKE) == ERR_SHAPE         # key heads neither 1 nor H
+    assert call(FAKE, FAKE, 96, 1, 1024, 1024, 192, FAKE) == ERR_SHAPE  # more logits than the stage writes
+    assert call(FAKE, FAKE, 96, 1, 4, 4, 192, None) == ERR_NULL
+    assert call(FAKE + 2, FAKE, 1, 1, 4, 4, 576, FAKE) == ERR_SHAPE     # q not 16-byte aligned
+    assert call(None, None, 96, 0, 4, 4, 192, None) == 0                # empty: nothing launched

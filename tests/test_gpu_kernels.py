@@ -388,3 +388,35 @@ def test_topk_many_equal_scores(t, n_pos):
         np.testing.assert_array_equal(sel[b], O.select_topk(sc_gpu[b, :t].astype(np.float64), 2048))
         n_zero_kept = int((sc_gpu[b, sel[b]] == 0).sum())
         assert n_zero_kept >= 2048 - n_pos
+
+
+# ---------------------------------------------------------------------------------------------
+# Raw logits (stage entry point)
+# ---------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("form,B,Tq,Tk", [("expanded", 2, 37, 70), ("absorbed", 2, 33, 65), ("expanded", 1, 1, 1),
+                                          ("absorbed", 1, 64, 32)])
+def test_debug_scores_against_oracle(form, B, Tq, Tk):
+    """mla_debug_scores against the oracle's logits: per-head keys (D = 192) and the shared latent
+    rows of the absorbed form (D = 576), ragged tiles and a single (query, key) pair. The kernel
+    multiplies bf16 values exactly and accumulates D products in fp32: each logit is within
+    D * 2^-24 of the sum of the products' magnitudes (times the scale), plus the fp32 scale's rounding."""
+    d = K3
+    print(f"debug_scores {form} B={B} Tq={Tq} Tk={Tk}", flush=True)
+    H = d.n_heads
+    D = d.d_qk if form == "expanded" else d.d_latent
+    Hk = H if form == "expanded" else 1
+    q = rand_bf16((B, Tq, H, D), 120)
+    k = rand_bf16((B, Hk, Tk, D), 121)
+    logits = torch.full((B, H, Tq, Tk), float("nan"), dtype=torch.float32, device="cuda")
+    gm.mla_debug_scores(gm.make_dims(d), dev_bf16(q), dev_bf16(k), Hk, B, Tq, Tk, D, logits)
+    _sync()
+    scale = O.softmax_scale(d)
+    ref = O.attention_logits(f64(q), f64(k), scale)
+    mag = O.attention_logits(np.abs(f64(q)), np.abs(f64(k)), scale)
+    got = logits.cpu().numpy().astype(np.float64)
+    assert np.isfinite(got).all()
+    bound = D * 2.0 ** -24 * mag + 2.0 ** -23 * np.abs(ref)
+    err = np.abs(got - ref)
+    assert (err <= bound).all(), float(np.max(err - bound))
+

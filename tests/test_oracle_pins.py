@@ -154,6 +154,36 @@ def test_attention_matches_brute_force_and_library():
     np.testing.assert_allclose(z0, lib.numpy().transpose(0, 2, 1, 3), rtol=1e-12, atol=1e-13)
 
 
+def test_attention_logits_brute_force_one_hot_and_lse():
+    """The raw logits: scalar loops with per-head and shared keys (non-square B, T, H, N so that a
+    transposed operand or a wrong head index shows), one-hot features, and the expanded
+    attention's softmax denominators as the logsumexp of the masked logits."""
+    from brute_force import brute_attention_logits
+    rng = np.random.default_rng(41)
+    B, T, H, N, D = 2, 3, 4, 5, 24
+    q = rng.standard_normal((B, T, H, D))
+    k = rng.standard_normal((B, H, N, D))
+    kl = rng.standard_normal((B, 1, N, D))
+    scale = D ** -0.5
+    for kk in (k, kl):
+        s = O.attention_logits(q, kk, scale)
+        assert s.shape == (B, H, T, N)
+        np.testing.assert_allclose(s, np.array(brute_attention_logits(q.tolist(), kk.tolist(), scale)),
+                                   rtol=1e-12, atol=1e-13)
+    qo = np.zeros((1, 1, 1, D))
+    qo[0, 0, 0, 5] = 1.0
+    ko = np.zeros((1, 1, 2, D))
+    ko[0, 0, 0, 5] = 1.0
+    ko[0, 0, 1, 6] = 1.0
+    np.testing.assert_array_equal(O.attention_logits(qo, ko, 0.25)[0, 0, 0], [0.25, 0.0])
+    P = 2
+    v = rng.standard_normal((B, H, N, 16))
+    _, lse = O.attention_expanded(q, k, v, scale, P)
+    s = O.attention_logits(q, k, scale)
+    for i in range(T):
+        np.testing.assert_allclose(lse[:, :, i], np.log(np.exp(s[:, :, i, :P + i + 1]).sum(-1)), rtol=1e-12)
+
+
 def test_attention_special_cases():
     rng = np.random.default_rng(5)
     k = rng.standard_normal((1, 2, 9, 24))
