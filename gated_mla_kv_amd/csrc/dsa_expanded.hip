@@ -1003,6 +1003,106 @@ __global__ __launch_bounds__(256) void expanded_attn_kernel(ExpandedAttnArgs a) 
 }
 
 // u[i] = z[i] * sigmoid(g_pre[i]) over B*H*DV elements (z and g_pre f32; g_pre may be null).
+// The K3 shape (192-wide keys, 128-wide values) with the next 16-key step's K and V loaded while
+// the current one is scored: both loads of a step are issued together, a step ahead, into
+// registers (two buffers), so a step waits on neither. Lanes as in expanded_attn_kernel: key
+// base + lane/4, feature quarter lane%4 of the key; value features 2 lane, 2 lane + 1. At most
+// three workgroups per CU: the 3072 (b, h) workgroups of B = 32 then run in four full rounds.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 3))) void expanded_attn_k3_kernel(ExpandedAttnArgs a) {
+  constexpr int H = ShapeK3::H, DQK = 192, DV = 128, DQ4 = DQK / 4, KC = DQ4 / 8;
+  __shared__ float ms[4], lsum[4];
+  __shared__ float os[4][DV];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int kq = lane & 3, kk = lane >> 2;
+  const int bh = blockIdx.x, b = bh / H, h = bh % H;
+  const int n = min(a.n_vis[b] + a.vis_offset, a.T_cap);
+  float qv[DQ4];
+  {
+    const uint16_t* qrow = a.q + ((size_t)b * H + h) * DQK + kq * DQ4;
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+      const u32x4 w = ld16(qrow + 8 * c);
+      qv[8 * c + 0] = lo_bf16(w.x); qv[8 * c + 1] = hi_bf16(w.x);
+      qv[8 * c + 2] = lo_bf16(w.y); qv[8 * c + 3] = hi_bf16(w.y);
+      qv[8 * c + 4] = lo_bf16(w.z); qv[8 * c + 5] = hi_bf16(w.z);
+      qv[8 * c + 6] = lo_bf16(w.w); qv[8 * c + 7] = hi_bf16(w.w);
+    }
+  }
+  const uint16_t* kb = a.k + (size_t)bh * a.T_cap * DQK;
+  const uint16_t* vb = a.v + (size_t)bh * a.T_cap * DV;
+  const float sl2 = a.scale * 1.4426950408889634f;
+  float m_run = -INFINITY, l_run = 0.f, o0 = 0.f, o1 = 0.f;
+  u32x4 kf[2][KC];
+  uint32_t vf[2][16];
+  // keys past the last visible one re-read it (their scores are -inf, their values unused)
+  auto load = [&](int base, u32x4* k, uint32_t* v) __attribute__((always_inline)) {
+    const uint16_t* kr = kb + (size_t)min(base + kk, n - 1) * DQK + kq * DQ4;
+#pragma unroll
+    for (int c = 0; c < KC; ++c) k[c] = ld16(kr + 8 * c);
+#pragma unroll
+    for (int k2 = 0; k2 < 16; ++k2) v[k2] = *(const uint32_t*)(vb + (size_t)min(base + k2, n - 1) * DV + 2 * lane);
+  };
+  auto step = [&](int base, const u32x4* k, const uint32_t* v) __attribute__((always_inline)) {
+    float s = 0.f;
+#pragma unroll
+    for (int c = 0; c < KC; ++c)
+      s += qv[8 * c + 0] * lo_bf16(k[c].x) + qv[8 * c + 1] * hi_bf16(k[c].x) + qv[8 * c + 2] * lo_bf16(k[c].y) +
+           qv[8 * c + 3] * hi_bf16(k[c].y) + qv[8 * c + 4] * lo_bf16(k[c].z) + qv[8 * c + 5] * hi_bf16(k[c].z) +
+           qv[8 * c + 6] * lo_bf16(k[c].w) + qv[8 * c + 7] * hi_bf16(k[c].w);
+    s += __shfl_xor(s, 1, 64);
+    s += __shfl_xor(s, 2, 64);
+    s = (base + kk < n) ? s * sl2 : -INFINITY;
+    float mt = s;
+#pragma unroll
+    for (int off = 4; off < 64; off <<= 1) mt = fmaxf(mt, __shfl_xor(mt, off, 64));
+    const float m_new = fmaxf(m_run, mt);  // finite: key base is visible
+    const float alpha = fast_exp2(m_run - m_new);
+    const float p = fast_exp2(s - m_new);
+    const float ps = wave_sum(kq == 0 ? p : 0.f);
+    l_run = l_run * alpha + ps;
+    m_run = m_new;
+    o0 *= alpha;
+    o1 *= alpha;
+#pragma unroll
+    for (int k2 = 0; k2 < 16; ++k2) {
+      const float pj = __shfl(p, k2 * 4, 64);
+      if (base + k2 < n) {
+        o0 += pj * lo_bf16(v[k2]);
+        o1 += pj * hi_bf16(v[k2]);
+      }
+    }
+  };
+  int base = wave * 16;
+  if (base < n) load(base, kf[0], vf[0]);
+  for (; base < n; base += 128) {
+    if (base + 64 < n) load(base + 64, kf[1], vf[1]);
+    step(base, kf[0], vf[0]);
+    if (base + 64 >= n) break;
+    if (base + 128 < n) load(base + 128, kf[0], vf[0]);
+    step(base + 64, kf[1], vf[1]);
+  }
+  if (lane == 0) {
+    ms[wave] = m_run;
+    lsum[wave] = l_run;
+  }
+  os[wave][2 * lane] = o0;
+  os[wave][2 * lane + 1] = o1;
+  __syncthreads();
+  float M = -INFINITY;
+  for (int w = 0; w < 4; ++w) M = fmaxf(M, ms[w]);
+  float den = 0.f, f[4];
+  for (int w = 0; w < 4; ++w) {
+    f[w] = (ms[w] == -INFINITY) ? 0.f : fast_exp2(ms[w] - M);
+    den += f[w] * lsum[w];
+  }
+  for (int d = threadIdx.x; d < DV; d += 256) {
+    float acc = 0.f;
+    for (int w = 0; w < 4; ++w) acc += f[w] * os[w][d];
+    a.z[(size_t)bh * DV + d] = den > 0.f ? acc / den : 0.f;
+  }
+  if (threadIdx.x == 0 && a.lse) a.lse[bh] = (M + __log2f(den)) * 0.6931471805599453f;
+}
+
 __global__ void gate_mul_kernel(const float* z, const float* g_pre, int n, void* u, int u_f32) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= n) return;
@@ -1075,7 +1175,7 @@ hipError_t launch_index_topk(IndexScoreArgs sa, int max_visible, TopkArgs ta, in
 hipError_t launch_expanded_attention(Shape s, const ExpandedAttnArgs& a, hipStream_t st) {
   if (a.B <= 0) return hipSuccess;
   if (s == Shape::K3)
-    expanded_attn_kernel<ShapeK3><<<a.B * ShapeK3::H, 256, 0, st>>>(a);
+    expanded_attn_k3_kernel<<<a.B * ShapeK3::H, 256, 0, st>>>(a);
   else
     expanded_attn_kernel<ShapeTiny><<<a.B * ShapeTiny::H, 256, 0, st>>>(a);
   return hipGetLastError();
