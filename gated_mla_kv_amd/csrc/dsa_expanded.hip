@@ -1006,9 +1006,10 @@ __global__ __launch_bounds__(256) void expanded_attn_kernel(ExpandedAttnArgs a) 
 // The K3 shape (192-wide keys, 128-wide values) with the next 16-key step's K and V loaded while
 // the current one is scored: both loads of a step are issued together, a step ahead, into
 // registers (two buffers), so a step waits on neither. Lanes as in expanded_attn_kernel: key
-// base + lane/4, feature quarter lane%4 of the key; value features 2 lane, 2 lane + 1. At most
-// three workgroups per CU: the 3072 (b, h) workgroups of B = 32 then run in four full rounds.
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 3))) void expanded_attn_k3_kernel(ExpandedAttnArgs a) {
+// base + lane/4, feature quarter lane%4 of the key; value features 2 lane, 2 lane + 1. The two
+// buffers take the kernel to ~200 VGPRs, two workgroups per CU: the 3072 (b, h) workgroups of
+// B = 32 run in six whole rounds.
+__global__ __launch_bounds__(256) void expanded_attn_k3_kernel(ExpandedAttnArgs a) {
   constexpr int H = ShapeK3::H, DQK = 192, DV = 128, DQ4 = DQK / 4, KC = DQ4 / 8;
   __shared__ float ms[4], lsum[4];
   __shared__ float os[4][DV];
