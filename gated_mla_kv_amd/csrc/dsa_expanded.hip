@@ -5,14 +5,14 @@
 // The query q^I is fp32, as eq. (5) leaves it unrounded: each of its values enters the MFMA as a
 // bf16 pair hi + lo (split_bf16x8), so a key tile takes two MFMAs per k-step on the same keys and
 // the dot products carry the query to about 17 bits (fp32 accumulation, exact products).
-// The dot products are a [32 heads x 128] . [128 x 32 positions] bf16 MFMA per wave, with the
-// index keys loaded from HBM straight into the B operand (one 16-byte load per lane and k-step,
-// 256 bytes per position, each read once; two 32-position tiles in flight per wave, eight waves
-// per workgroup, chunks sized to fill the CUs once). Lane l ends with position l%32 and 16 heads, so the
-// head-weighted ReLU sum is in-lane plus one xor-32 shuffle. 1/sqrt(32*128) = 1/64 is folded
-// into a exactly. FP8 index keys (128 E4M3 codes and one scale s >= 0 per position, the blog's
-// cache section) load 8 bytes per lane and k-step, widen exactly to bf16, and the position's
-// score is multiplied by s (ReLU(s z) = s ReLU(z) for s >= 0).
+// The dot products are a [32 heads x 128] . [128 x 32 positions] bf16 MFMA per wave, with each
+// 32-position tile of index keys (256 bytes per position, each read once) copied whole into the
+// wave's LDS ring and the B operand read from there; eight waves per workgroup, one workgroup
+// per CU. Lane l ends with position l%32 and 16 heads, so the head-weighted ReLU sum is in-lane
+// plus one xor-32 shuffle. 1/sqrt(32*128) = 1/64 is folded into a exactly. FP8 index keys (128
+// E4M3 codes and one scale s >= 0 per position, the blog's cache section) are copied the same
+// way, widened exactly to bf16 when read, and the position's score is multiplied by s
+// (ReLU(s z) = s ReLU(z) for s >= 0).
 //
 // Top-k (eq. (6)): S = the min(k, t) largest I, ties to the lower position, -0 == +0, written
 // in ascending position order, over order-preserving 32-bit keys of the fp32 scores.
@@ -39,110 +39,163 @@
 
 namespace gmla {
 
+// As lds_dma16_sbase with 4 bytes per lane (global_load_lds_dword): lane L's word lands at
+// lds_byte_addr + 4*L.
+__device__ __forceinline__ void lds_dma4_sbase(uint32_t voff, const void* sbase, uint32_t lds_byte_addr) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dword %1, %2"
+      :
+      : "s"(__builtin_amdgcn_readfirstlane(lds_byte_addr)), "v"(voff), "s"(sbase)
+      : "memory", "m0");
+}
+
 // ------------------------------------------------------------------------------------------
 // Index scores (K3 indexer: 32 heads x 128)
 // ------------------------------------------------------------------------------------------
 __device__ __forceinline__ uint32_t order_key(float f);
 constexpr int kHistBins = 4096;      // first radix digit: the top 12 bits of the order key
-constexpr int kScoreChunkMin = 512;  // fewest positions per workgroup
+constexpr int kScoreTilesMin = 16;   // fewest 32-position tiles per workgroup
 constexpr int kScoreWaves = 8;
-constexpr int kScoreBufs = 2;  // key tiles in flight per wave (3 and 4 measured slower)
 
-// One workgroup per (chunk of a.chunk positions, row); wave w scores the 32-position tiles w,
-// w+8, ... of the chunk with the keys of the next tile already in flight, and every score's top
-// digit goes into an LDS histogram that is added to the row's histogram at the end. The launcher
-// sizes the chunks so that all rows' workgroups fill the CUs once (one per CU): with a fixed
-// chunk, B = 8 rows of 65,537 positions made 264 workgroups, and the 8 past the 256 CUs ran as
-// a second round.
-// FP8 (codes + per-key scale) and PAGED are template parameters so that the tile loop has no
-// branches: the wait counts for the keys in flight then stay exact (at a runtime branch the
-// compiler waits for every outstanding load), and a paged tile's table entry is read through the
-// scalar cache, leaving the key loads in flight.
+// One workgroup per (chunk, row); a row's chunks split the 32-position tiles of the longest row
+// as evenly as whole tiles allow, and wave w scores the tiles w, w+8, ... of its chunk. A tile's
+// keys are contiguous (32 consecutive cache rows; a tile never crosses a page), so the wave
+// copies each tile whole into its own two-slot LDS ring with wave-wide 1 KB DMA loads, the next
+// tile in flight while it scores the current one, and reads the MFMA's B operand from there. Loaded straight into the operand registers, each load took
+// 16 or 8 bytes from each of 32 rows: 31 against 26 us for 134 MB in a probe of the two forms.
+// Every score's top digit goes into an LDS histogram that is added to the row's histogram at
+// the end. The launcher picks the chunks per row so that all rows' workgroups fill the CUs once
+// (one per CU). A workgroup takes as long as its busiest wave: B = 8 rows of 65,537 positions
+// (2,049 tiles) in 32 chunks of 64 or 65 tiles leave one wave per row a ninth tile that holds a
+// single position, where chunks of 65 whole tiles gave one wave in every workgroup a ninth full
+// tile (and fixed chunks of 64 tiles made 264 workgroups, the 8 past the 256 CUs a second
+// round).
+// Tile layouts in LDS (conflict-free 16-byte reads of one chunk from 16 rows):
+// * bf16: row r (256 B) holds its 16-byte chunk c at r*256 + ((c ^ (r & 15)) << 4);
+// * FP8: row r (128 B of codes) holds chunk c at r*128 + ((c ^ ((r >> 1) & 7)) << 4), and the
+//   tile's 32 scales follow the codes.
+// FP8 and PAGED are template parameters so that the tile loop has no branches; a paged tile's
+// table entry is read through the scalar cache, leaving the DMA in flight.
 template <bool FP8, bool PAGED>
 __global__ __launch_bounds__(kScoreWaves * 64) void index_scores_kernel(IndexScoreArgs a) {
   constexpr int NIH = 32, DI = 128, KS = DI / 16;
+  constexpr int RB = FP8 ? DI : 2 * DI;        // bytes per key row
+  constexpr int NDMA = 32 * RB / 1024;         // wave-wide 1 KB loads per tile (8 or 4)
+  constexpr int SLOT = 32 * RB + (FP8 ? 256 : 0);
+  constexpr int VPT = NDMA + (FP8 ? 1 : 0);    // vector memory operations per tile
+  static_assert(VPT == 8 || VPT == 5, "vmcnt immediates");
   __shared__ int lhist[kHistBins];
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[kScoreWaves][2][SLOT];
+  // the row's q^I (32 heads x 128 fp32), head h's 16-byte chunk c at h*512 + ((c ^ h) << 4)
+  __shared__ __attribute__((aligned(1024))) uint8_t q_s[NIH * DI * 4];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g2 = lane >> 5, l32 = lane & 31;
   const int b = blockIdx.y;
   const RowMap rm = row_map(a.row0, a.rows_per_seq, b);
   const int t = min(min(a.n_vis[rm.seq] + a.vis_offset + rm.extra, a.T_cap), a.score_stride);
-  const int base = blockIdx.x * a.chunk;
+  const int tile0 = (int)((long long)blockIdx.x * a.row_tiles / a.n_chunks);
+  const int tile1 = (int)((long long)(blockIdx.x + 1) * a.row_tiles / a.n_chunks);
+  const int base = tile0 * 32;
   if (base >= t) return;
-  const int end = min(base + a.chunk, t);
+  const int end = min(tile1 * 32, t);
   for (int i = threadIdx.x; i < kHistBins; i += kScoreWaves * 64) lhist[i] = 0;
-  const uint16_t* kb = a.idx_k;
-  const uint8_t* kb8 = (const uint8_t*)a.idx_k;
   const int n_tiles = cdiv(end - base, 32);
   const int nt_w = wave < n_tiles ? cdiv(n_tiles - wave, kScoreWaves) : 0;  // this wave's tiles
-  // cache row of this lane's position in the wave's j-th tile (a 32-position tile lies in one
-  // page); tiles past the chunk's last re-read it and positions past the end repeat the last one
-  // (their scores are not stored), so that the tile loop needs no branches
-  auto key_row = [&](int j) __attribute__((always_inline)) {
-    const int p0 = base + min(wave + kScoreWaves * j, n_tiles - 1) * 32;
-    const int pos = min(p0 + l32, end - 1);
-    if constexpr (PAGED)
-      return cache_row_uniform(a.pages, a.T_cap, rm.seq, p0) + (size_t)(pos - p0);
-    else
-      return (size_t)rm.seq * a.T_cap + pos;
-  };
-  // keys of this wave's j-th tile (positions p0 + l32): the B operand, one 16-byte (bf16) or
-  // 8-byte (FP8, widened when used) load per k-step, and the FP8 key's scale with them
-  auto load_keys = [&](int j, u32x4* kf, float& ks) __attribute__((always_inline)) {
-    const size_t row = key_row(j);
-    if constexpr (FP8) {
+  // The wave's j-th tile into ring slot j & 1. Tiles past the chunk's last re-read it, and rows
+  // past the end repeat the last valid one (their scores are not stored), so the loop needs no
+  // branches.
+  auto issue = [&](int j) __attribute__((always_inline)) {
+    const int p0 = __builtin_amdgcn_readfirstlane(base + min(wave + kScoreWaves * j, n_tiles - 1) * 32);
+    const int nval = min(32, end - p0);
+    const size_t row0 = PAGED ? cache_row_uniform(a.pages, a.T_cap, rm.seq, p0) : (size_t)rm.seq * a.T_cap + p0;
+    const uint8_t* src = (const uint8_t*)a.idx_k + row0 * RB;
+    const uint32_t dst = lds_addr(ring[wave][j & 1]);
 #pragma unroll
-      for (int s = 0; s < KS; s += 2) {
-        const u32x2 w0 = ld8(kb8 + row * DI + s * 16 + g2 * 8);
-        const u32x2 w1 = ld8(kb8 + row * DI + (s + 1) * 16 + g2 * 8);
-        kf[s] = u32x4{w0.x, w0.y, w1.x, w1.y};  // raw codes, widened in score()
-      }
-      ks = a.idx_scale[row];
-    } else {
-#pragma unroll
-      for (int s = 0; s < KS; ++s) kf[s] = ld16(kb + row * DI + s * 16 + g2 * 8);
-      ks = 1.f;
+    for (int i = 0; i < NDMA; ++i) {
+      const int P = i * 64 + lane;  // 16-byte chunk of the slot this lane fills
+      const int r = FP8 ? P >> 3 : P >> 4;
+      const int c = FP8 ? ((P & 7) ^ ((r >> 1) & 7)) : ((P & 15) ^ (r & 15));
+      lds_dma16_sbase((uint32_t)(min(r, nval - 1) * RB + c * 16), src, dst + i * 1024);
     }
+    if constexpr (FP8)  // 32 scales; lanes 32-63 repeat them into the next 128 bytes
+      lds_dma4_sbase((uint32_t)(min(l32, nval - 1) * 4), a.idx_scale + row0, dst + 32 * RB);
   };
-  // A operand (loaded before the keys, whose loads then stay in flight past its wait): q^I of
-  // this lane's head l32 as bf16 hi + lo pairs
-  u32x4 qa[KS], ql[KS];
+  // The query is copied once per workgroup (each wave 2 KB of it), ahead of the first two tiles:
+  // loaded by every lane straight from memory, it took 16 scattered 16-byte loads per lane, as
+  // many bytes of L2 traffic as the keys, and the first tile waited for it.
   {
-    const float* qrow = a.q_idx + ((size_t)b * NIH + l32) * DI;
+    const float* qbase = a.q_idx + (size_t)__builtin_amdgcn_readfirstlane(b) * NIH * DI;
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      float f[8];
-      *(u32x4*)&f[0] = ld16(qrow + s * 16 + g2 * 8);
-      *(u32x4*)&f[4] = ld16(qrow + s * 16 + g2 * 8 + 4);
-      uint32_t h[4], l[4];
-      split_bf16x8(f, h, l);
-      qa[s] = u32x4{h[0], h[1], h[2], h[3]};
-      ql[s] = u32x4{l[0], l[1], l[2], l[3]};
+    for (int i = 0; i < 2; ++i) {
+      const int G = wave * 128 + i * 64 + lane, h = G >> 5, c = (G & 31) ^ h;
+      lds_dma16_sbase((uint32_t)(h * 512 + c * 16), qbase, lds_addr(q_s) + wave * 2048 + i * 1024);
     }
   }
-  // head weights of the 16 heads this lane's accumulators hold: (r/4)*8 + g2*4 + r%4
+  issue(0);
+  issue(1);
+  // head weights of the 16 heads this lane's accumulators hold, (r/4)*8 + g2*4 + r%4, read through
+  // the scalar cache (its wait leaves the copies in flight)
   float wgt[16];
+  {
+    f32x16 w0, w1;
+    const float* wrow = a.w_idx + (size_t)__builtin_amdgcn_readfirstlane(b) * NIH;
+    asm volatile("s_load_dwordx16 %0, %2, 0x0\n\ts_load_dwordx16 %1, %2, 0x40\n\ts_waitcnt lgkmcnt(0)"
+                 : "=s"(w0), "=s"(w1) : "s"(wrow) : "memory");
 #pragma unroll
-  for (int r = 0; r < 16; ++r) wgt[r] = a.w_idx[(size_t)b * NIH + (r >> 2) * 8 + g2 * 4 + (r & 3)] * a.scale;
-  u32x4 kf[kScoreBufs][KS];  // keys of this wave's next kScoreBufs tiles, in flight together
-  float kscale[kScoreBufs];
+    for (int r = 0; r < 16; ++r) {
+      const int i = (r >> 2) * 8 + (r & 3);  // head for g2 = 0; g2 = 1 takes i + 4
+      const float lo = i < 16 ? w0[i] : w1[i - 16], hi = i + 4 < 16 ? w0[i + 4] : w1[i - 12];
+      wgt[r] = (g2 ? hi : lo) * a.scale;
+    }
+  }
+  // this wave's part of the query has landed (its two tiles stay in flight); the barrier then
+  // covers every wave's part and the cleared histogram
+  if constexpr (VPT == 8)
+    asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
+  __syncthreads();
+  // A operand: q^I of this lane's head l32 as bf16 hi + lo pairs. k-step s takes, in lane group
+  // g2, the features the B operand holds there: bf16 keys 16 s + 8 g2 + (0..7); FP8 keys, whose
+  // 16-byte chunk 2 (s / 2) + g2 serves k-steps s and s + 1, 16 (2 (s / 2) + g2) + 8 (s % 2) + (0..7).
+  u32x4 qa[KS], ql[KS];
 #pragma unroll
-  for (int i = 0; i < kScoreBufs; ++i) load_keys(i, kf[i], kscale[i]);
-  __syncthreads();  // histogram cleared
-  auto score = [&](int j, const u32x4* kf, float ks) __attribute__((always_inline)) {
+  for (int s = 0; s < KS; ++s) {
+    const int c0 = (FP8 ? 16 * (2 * (s >> 1) + g2) + 8 * (s & 1) : 16 * s + 8 * g2) >> 2;
+    float f[8];
+    *(u32x4*)&f[0] = *(const u32x4*)(q_s + l32 * 512 + ((c0 ^ l32) << 4));
+    *(u32x4*)&f[4] = *(const u32x4*)(q_s + l32 * 512 + (((c0 + 1) ^ l32) << 4));
+    uint32_t h[4], l[4];
+    split_bf16x8(f, h, l);
+    qa[s] = u32x4{h[0], h[1], h[2], h[3]};
+    ql[s] = u32x4{l[0], l[1], l[2], l[3]};
+  }
+  auto score = [&](int j, int slot) __attribute__((always_inline)) {
+    const uint8_t* tile = ring[wave][slot];
     f32x16 acc = f32x16{};
     if constexpr (FP8) {
+      const uint8_t* row = tile + l32 * RB;
+      const int sw = (l32 >> 1) & 7;
+      u32x4 kr[KS / 2];
 #pragma unroll
-      for (int s = 0; s < KS; s += 2) {
-        const u32x2 a0 = e4m3x4_to_bf16(kf[s].x), a1 = e4m3x4_to_bf16(kf[s].y);
-        const u32x2 b0 = e4m3x4_to_bf16(kf[s].z), b1 = e4m3x4_to_bf16(kf[s].w);
+      for (int s2 = 0; s2 < KS / 2; ++s2) kr[s2] = *(const u32x4*)(row + (((2 * s2 + g2) ^ sw) << 4));
+#pragma unroll
+      for (int s2 = 0; s2 < KS / 2; ++s2) {
+        const u32x2 a0 = e4m3x4_to_bf16(kr[s2].x), a1 = e4m3x4_to_bf16(kr[s2].y);
+        const u32x2 b0 = e4m3x4_to_bf16(kr[s2].z), b1 = e4m3x4_to_bf16(kr[s2].w);
         const u32x4 k0 = u32x4{a0.x, a0.y, a1.x, a1.y}, k1 = u32x4{b0.x, b0.y, b1.x, b1.y};
-        acc = mfma32(qa[s], k0, acc);
-        acc = mfma32(ql[s], k0, acc);
-        acc = mfma32(qa[s + 1], k1, acc);
-        acc = mfma32(ql[s + 1], k1, acc);
+        acc = mfma32(qa[2 * s2], k0, acc);
+        acc = mfma32(ql[2 * s2], k0, acc);
+        acc = mfma32(qa[2 * s2 + 1], k1, acc);
+        acc = mfma32(ql[2 * s2 + 1], k1, acc);
       }
     } else {
+      const uint8_t* row = tile + l32 * RB;
+      u32x4 kf[KS];
+#pragma unroll
+      for (int s = 0; s < KS; ++s) kf[s] = *(const u32x4*)(row + (((2 * s + g2) ^ (l32 & 15)) << 4));
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
         acc = mfma32(qa[s], kf[s], acc);
@@ -153,22 +206,28 @@ __global__ __launch_bounds__(kScoreWaves * 64) void index_scores_kernel(IndexSco
 #pragma unroll
     for (int r = 0; r < 16; ++r) sc += wgt[r] * fmaxf(acc[r], 0.f);
     sc += __shfl_xor(sc, 32, 64);
-    if constexpr (FP8) sc *= ks;
+    if constexpr (FP8) sc *= *(const float*)(tile + 32 * RB + 4 * l32);
     const int pos = base + (wave + kScoreWaves * j) * 32 + l32;
     if (pos < end && g2 == 0) {
       a.scores[(size_t)b * a.score_stride + pos] = sc;
       atomicAdd(&lhist[order_key(sc) >> 20], 1);
     }
   };
-  // branch-free steady state: every step scores one tile and starts the loads kScoreBufs ahead
-  // (past the wave's last tile they re-read the chunk's last tile, unused)
-  for (int j = 0; j < nt_w; j += kScoreBufs) {
+  // steady state: wait for tile j (tile j + 1 stays in flight; a score store issued in between
+  // is waited for too), score it, and refill its slot with tile j + 2
+  for (int j = 0; j < nt_w; j += 2) {
 #pragma unroll
-    for (int i = 0; i < kScoreBufs; ++i) {
-      score(j + i, kf[i], kscale[i]);
-      load_keys(j + i + kScoreBufs, kf[i], kscale[i]);
+    for (int i = 0; i < 2; ++i) {
+      if constexpr (VPT == 8)
+        asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
+      score(j + i, i);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the slot's reads are done
+      issue(j + i + 2);
     }
   }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no copy into LDS outlives the loop
   __syncthreads();
   // the row's histogram gathers the workgroup's nonzero bins
   int* gh = a.hist + (size_t)b * kHistBins;
@@ -1145,8 +1204,9 @@ hipError_t launch_index_topk(IndexScoreArgs sa, int max_visible, TopkArgs ta, in
         hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n_cu < 1)
       n_cu = 256;
     const int cpr = max(1, n_cu * cdiv(B, n_cu) / B);
-    sa.chunk = max(kScoreChunkMin, cdiv(cdiv(max_visible, cpr), 32) * 32);
-    const dim3 grid(cdiv(max_visible, sa.chunk), B);
+    sa.row_tiles = cdiv(max_visible, 32);
+    sa.n_chunks = max(1, min(cpr, sa.row_tiles / kScoreTilesMin));
+    const dim3 grid(sa.n_chunks, B);
     const bool fp8 = sa.idx_scale != nullptr, paged = sa.pages.table != nullptr;
     if (fp8 && paged)
       index_scores_kernel<true, true><<<grid, kScoreWaves * 64, 0, st>>>(sa);

@@ -132,7 +132,7 @@ struct IndexScoreArgs {
   int score_stride;
   int32_t* hist;          // [B, 4096] counts of the scores' top-12-bit order-key digit (zeroed first)
   int row0, rows_per_seq; // see row_map
-  int chunk;              // positions per workgroup of index_scores_kernel (a multiple of 32)
+  int n_chunks, row_tiles; // index_scores_kernel: workgroups per row; 32-position tiles of the longest row
 };
 
 struct TopkArgs {
