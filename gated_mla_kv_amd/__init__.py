@@ -17,10 +17,12 @@ __all__ = [
     "mla_decode_noalloc", "NOALLOC_SCRATCH_BYTES", "kv_append", "dsa_index_topk", "dsa_index_topk_fp8", "mla_index_projections", "mla_gemm",
     "mla_rmsnorm", "mla_layernorm", "mla_prefill_attention", "mla_absorb_query",
     "mla_decode_attention", "mla_sparse_attention", "mla_expanded_attention", "mla_value_up_gate",
-    "mla_debug_scores", "DEBUG_SCORES_MAX", "LIB_PATH",
+    "mla_debug_scores", "DEBUG_SCORES_MAX", "mla_debug_flags", "LIB_PATH", "DEBUG_LIB_PATH",
 ]
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgmla.so")
+# GMLA_LIB selects another build of the library (the debug-checks or the host-ASan variant)
+LIB_PATH = os.environ.get("GMLA_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgmla.so")
+DEBUG_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgmla_debug.so")
 
 OUT_BF16, OUT_F32 = 0, 1
 PATH_ABSORBED, PATH_EXPANDED, PATH_SPARSE = 0, 1, 2
@@ -86,6 +88,7 @@ _SIGS = {
     "mla_expanded_attention": (ctypes.c_int, [_P, _P, _P, _P, _I, _I, _P, _P, _P]),
     "mla_value_up_gate": (ctypes.c_int, [_P, _P, _P, _P, _I, _P, _I, _P]),
     "mla_debug_scores": (ctypes.c_int, [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P]),
+    "mla_debug_flags": (ctypes.c_int, [_P, _P, _P]),
 }
 
 
@@ -280,3 +283,11 @@ def mla_value_up_gate(dims, o_latent, w_kv_b, g_pre, B, u, out_dtype=OUT_BF16, s
 def mla_debug_scores(dims, q, k, k_heads, B, Tq, Tk, D, logits, stream=None):
     _check(lib().mla_debug_scores(ctypes.byref(dims), _p(q), _p(k), k_heads, B, Tq, Tk, D, _p(logits),
                                   _stream(stream)), "mla_debug_scores")
+
+
+def mla_debug_flags(stream=None):
+    """(flags, checks_built): the device-side bound-check bits recorded since the last call
+    (cleared by this call), and whether this build of the library has the checks."""
+    flags, built = ctypes.c_uint32(0), ctypes.c_int32(0)
+    _check(lib().mla_debug_flags(ctypes.byref(flags), ctypes.byref(built), _stream(stream)), "mla_debug_flags")
+    return int(flags.value), bool(built.value)

@@ -2,6 +2,9 @@
 // whole-layer pipelines. Every public function validates all of its arguments before it
 // enqueues anything, so a call that returns an error has had no effect.
 #include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <mutex>
@@ -15,6 +18,26 @@ using namespace gmla;
 namespace {
 
 constexpr int kMaxTopk = 2048;
+
+// GMLA_LOG set to anything but "" or "0": every entry point that can launch work writes one line
+// to stderr on entry ("[gmla] <function> <sizes> stream=<stream>"), before it validates anything.
+bool log_enabled() {
+  static const bool on = [] {
+    const char* e = getenv("GMLA_LOG");
+    return e && *e && strcmp(e, "0") != 0;
+  }();
+  return on;
+}
+__attribute__((format(printf, 3, 4))) void trace(const char* fn, hipStream_t st, const char* fmt, ...) {
+  if (!log_enabled()) return;
+  char buf[320];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  fprintf(stderr, "[gmla] %s %s stream=%p\n", fn, buf, (void*)st);
+  fflush(stderr);
+}
 
 bool shape_of(const mla_dims* d, Shape* s) {
   if (!d) return false;
@@ -338,6 +361,7 @@ size_t mla_workspace_bytes(const mla_dims* d, int32_t B, int32_t T_new, int32_t 
 // ------------------------------------------------------------------------------------------
 int mla_gemm(const void* a, int32_t lda, const void* w, int32_t M, int32_t N, int32_t K, void* out,
              int32_t ldo, int32_t out_dtype, hipStream_t stream) {
+  trace(__func__, stream, "M=%d N=%d K=%d lda=%d ldo=%d out_dtype=%d", M, N, K, lda, ldo, out_dtype);
   if (M < 0 || N < 0 || K < 0) return MLA_ERR_SHAPE;
   if (M == 0 || N == 0) return MLA_OK;
   if (!a || !w || !out) return MLA_ERR_NULL;
@@ -352,6 +376,7 @@ int mla_gemm(const void* a, int32_t lda, const void* w, int32_t M, int32_t N, in
 
 int mla_rmsnorm(const float* x, int32_t ldx, const void* gain, int32_t M, int32_t N, float eps,
                 void* out, int32_t ldo, hipStream_t stream) {
+  trace(__func__, stream, "M=%d N=%d ldx=%d ldo=%d", M, N, ldx, ldo);
   if (M < 0 || N < 0) return MLA_ERR_SHAPE;
   if (M == 0 || N == 0) return MLA_OK;
   if (!x || !gain || !out) return MLA_ERR_NULL;
@@ -362,6 +387,7 @@ int mla_rmsnorm(const float* x, int32_t ldx, const void* gain, int32_t M, int32_
 
 int mla_layernorm(const float* x, int32_t ldx, const void* gain, const void* bias, int32_t M,
                   int32_t N, float eps, void* out, int32_t ldo, hipStream_t stream) {
+  trace(__func__, stream, "M=%d N=%d ldx=%d ldo=%d", M, N, ldx, ldo);
   if (M < 0 || N < 0) return MLA_ERR_SHAPE;
   if (M == 0 || N == 0) return MLA_OK;
   if (!x || !gain || !bias || !out) return MLA_ERR_NULL;
@@ -375,6 +401,7 @@ int mla_prefill_attention(const mla_dims* d, const void* q, const mla_cache* cac
                           const int32_t* start_pos, int32_t max_end, int32_t B, int32_t T,
                           const float* g_pre, void* u, int32_t out_dtype, float* lse,
                           hipStream_t stream) {
+  trace(__func__, stream, "B=%d T=%d max_end=%d out_dtype=%d", B, T, max_end, out_dtype);
   Shape s;
   if (!d) return MLA_ERR_NULL;
   if (!shape_of(d, &s)) return MLA_ERR_UNSUPPORTED;
@@ -404,6 +431,7 @@ int mla_prefill_attention(const mla_dims* d, const void* q, const mla_cache* cac
 
 int mla_absorb_query(const mla_dims* d, const void* q, int32_t ldq, const void* w_kv_b, int32_t B,
                      void* q_tilde, hipStream_t stream) {
+  trace(__func__, stream, "B=%d ldq=%d", B, ldq);
   Shape s;
   if (!d) return MLA_ERR_NULL;
   if (!shape_of(d, &s)) return MLA_ERR_UNSUPPORTED;
@@ -462,6 +490,7 @@ static int decode_attention_common(const mla_dims* d, const void* q_tilde, const
 int mla_decode_attention(const mla_dims* d, const void* q_tilde, const mla_cache* cache,
                          const int32_t* n_visible, int32_t max_visible, int32_t B, int32_t num_splits,
                          float* o_latent, float* lse, void* ws, size_t ws_bytes, hipStream_t stream) {
+  trace(__func__, stream, "B=%d max_visible=%d num_splits=%d ws_bytes=%zu", B, max_visible, num_splits, ws_bytes);
   return decode_attention_common(d, q_tilde, cache, n_visible, max_visible, nullptr, nullptr, B,
                                  num_splits, o_latent, lse, ws, ws_bytes, stream, false);
 }
@@ -469,6 +498,7 @@ int mla_decode_attention(const mla_dims* d, const void* q_tilde, const mla_cache
 int mla_sparse_attention(const mla_dims* d, const void* q_tilde, const mla_cache* cache,
                          const int32_t* sel_idx, const int32_t* sel_cnt, int32_t B, int32_t num_splits,
                          float* o_latent, float* lse, void* ws, size_t ws_bytes, hipStream_t stream) {
+  trace(__func__, stream, "B=%d num_splits=%d ws_bytes=%zu", B, num_splits, ws_bytes);
   return decode_attention_common(d, q_tilde, cache, nullptr, 0, sel_idx, sel_cnt, B, num_splits,
                                  o_latent, lse, ws, ws_bytes, stream, true);
 }
@@ -476,6 +506,7 @@ int mla_sparse_attention(const mla_dims* d, const void* q_tilde, const mla_cache
 int mla_expanded_attention(const mla_dims* d, const void* q, const mla_cache* cache,
                            const int32_t* n_visible, int32_t max_visible, int32_t B, float* z,
                            float* lse, hipStream_t stream) {
+  trace(__func__, stream, "B=%d max_visible=%d", B, max_visible);
   Shape s;
   if (!d) return MLA_ERR_NULL;
   if (!shape_of(d, &s)) return MLA_ERR_UNSUPPORTED;
@@ -501,6 +532,7 @@ int mla_expanded_attention(const mla_dims* d, const void* q, const mla_cache* ca
 
 int mla_debug_scores(const mla_dims* d, const void* q, const void* k, int32_t k_heads, int32_t B, int32_t Tq,
                      int32_t Tk, int32_t D, float* logits, hipStream_t stream) {
+  trace(__func__, stream, "B=%d Tq=%d Tk=%d D=%d k_heads=%d", B, Tq, Tk, D, k_heads);
   Shape s;
   if (!d) return MLA_ERR_NULL;
   if (!shape_of(d, &s)) return MLA_ERR_UNSUPPORTED;
@@ -528,6 +560,7 @@ int mla_debug_scores(const mla_dims* d, const void* q, const void* k, int32_t k_
 
 int mla_value_up_gate(const mla_dims* d, const float* o_latent, const void* w_kv_b, const float* g_pre,
                       int32_t B, void* u, int32_t out_dtype, hipStream_t stream) {
+  trace(__func__, stream, "B=%d out_dtype=%d", B, out_dtype);
   Shape s;
   if (!d) return MLA_ERR_NULL;
   if (!shape_of(d, &s)) return MLA_ERR_UNSUPPORTED;
@@ -542,6 +575,7 @@ int mla_value_up_gate(const mla_dims* d, const float* o_latent, const void* w_kv
 
 int mla_index_projections(const mla_dims* d, const mla_weights* w, const void* x, int32_t M, float* q_idx,
                           float* w_idx, void* k_idx, void* ws, size_t ws_bytes, hipStream_t stream) {
+  trace(__func__, stream, "M=%d ws_bytes=%zu", M, ws_bytes);
   Shape s;
   if (!d) return MLA_ERR_NULL;
   if (!shape_of(d, &s)) return MLA_ERR_UNSUPPORTED;
@@ -564,6 +598,7 @@ int mla_index_projections(const mla_dims* d, const mla_weights* w, const void* x
 int kv_append(const mla_dims* d, const mla_cache* cache, const int32_t* pos, int32_t max_end,
               int32_t B, int32_t T, const void* c, const void* r, const void* k_nope, const void* v,
               const void* idx_k, hipStream_t stream) {
+  trace(__func__, stream, "B=%d T=%d max_end=%d", B, T, max_end);
   Shape s;
   if (!d) return MLA_ERR_NULL;
   if (!shape_of(d, &s)) return MLA_ERR_UNSUPPORTED;
@@ -653,6 +688,7 @@ int dsa_index_topk(const mla_dims* d, const float* q_idx, const float* w_idx, co
                    int32_t T_cap, const int32_t* n_visible, int32_t max_visible, int32_t B,
                    int32_t* out_idx, int32_t* out_cnt, float* out_scores, void* ws, size_t ws_bytes,
                    hipStream_t stream) {
+  trace(__func__, stream, "B=%d T_cap=%d max_visible=%d ws_bytes=%zu", B, T_cap, max_visible, ws_bytes);
   return index_topk_common(d, q_idx, w_idx, idx_k_cache, nullptr, T_cap, n_visible, max_visible, B,
                            out_idx, out_cnt, out_scores, ws, ws_bytes, stream);
 }
@@ -661,6 +697,7 @@ int dsa_index_topk_fp8(const mla_dims* d, const float* q_idx, const float* w_idx
                        const float* idx_k_scales, int32_t T_cap, const int32_t* n_visible,
                        int32_t max_visible, int32_t B, int32_t* out_idx, int32_t* out_cnt,
                        float* out_scores, void* ws, size_t ws_bytes, hipStream_t stream) {
+  trace(__func__, stream, "B=%d T_cap=%d max_visible=%d ws_bytes=%zu", B, T_cap, max_visible, ws_bytes);
   if (!idx_k_scales) return MLA_ERR_NULL;
   if (d && d->d_idx != 128) return MLA_ERR_UNSUPPORTED;
   return index_topk_common(d, q_idx, w_idx, idx_k_codes, idx_k_scales, T_cap, n_visible, max_visible, B,
@@ -726,6 +763,7 @@ static int prefill_front(const mla_dims* d, const mla_weights* w, const mla_cach
 int mla_prefill(const mla_dims* d, const mla_weights* w, const mla_cache* cache, const int32_t* start_pos,
                 int32_t max_end, const void* x, int32_t B, int32_t T, void* y, int32_t out_dtype,
                 float* lse, void* ws, size_t ws_bytes, hipStream_t stream) {
+  trace(__func__, stream, "B=%d T=%d max_end=%d out_dtype=%d ws_bytes=%zu", B, T, max_end, out_dtype, ws_bytes);
   Shape s;
   if (!d) return MLA_ERR_NULL;
   if (!shape_of(d, &s)) return MLA_ERR_UNSUPPORTED;
@@ -824,6 +862,7 @@ int mla_prefill_sparse(const mla_dims* d, const mla_weights* w, const mla_cache*
                        int32_t max_end, const void* x, int32_t B, int32_t T, void* y, int32_t out_dtype,
                        int32_t* sel_idx, int32_t* sel_cnt, float* scores, void* ws, size_t ws_bytes,
                        hipStream_t stream) {
+  trace(__func__, stream, "B=%d T=%d max_end=%d out_dtype=%d ws_bytes=%zu", B, T, max_end, out_dtype, ws_bytes);
   Shape s;
   if (!d) return MLA_ERR_NULL;
   if (!shape_of(d, &s)) return MLA_ERR_UNSUPPORTED;
@@ -917,6 +956,7 @@ int mla_decode(const mla_dims* d, const mla_weights* w, const mla_cache* cache, 
                int32_t max_len, const void* x, int32_t B, int32_t path, int32_t num_splits,
                int32_t* sel_idx, int32_t* sel_cnt, void* y, int32_t out_dtype, void* ws, size_t ws_bytes,
                hipStream_t stream) {
+  trace(__func__, stream, "B=%d max_len=%d path=%d num_splits=%d out_dtype=%d ws_bytes=%zu", B, max_len, path, num_splits, out_dtype, ws_bytes);
   Shape s;
   if (!d) return MLA_ERR_NULL;
   if (!shape_of(d, &s)) return MLA_ERR_UNSUPPORTED;
@@ -1093,6 +1133,7 @@ extern "C" int mla_decode_noalloc(const mla_dims* d, const mla_weights* w, const
                                   const int32_t* seq_len, int32_t max_len, const void* x, int32_t B, int32_t path,
                                   int32_t num_splits, int32_t* sel_idx, int32_t* sel_cnt, void* y,
                                   int32_t out_dtype, hipStream_t stream) {
+  trace(__func__, stream, "B=%d max_len=%d path=%d num_splits=%d out_dtype=%d", B, max_len, path, num_splits, out_dtype);
   // the size check comes first and touches no device
   if (d && B > 0) {
     const size_t need = mla_workspace_bytes_ex(d, B, 1, max_len, path, num_splits);
@@ -1103,4 +1144,18 @@ extern "C" int mla_decode_noalloc(const mla_dims* d, const mla_weights* w, const
   if (!ws) return MLA_ERR_HIP;
   return mla_decode(d, w, cache, seq_len, max_len, x, B, path, num_splits, sel_idx, sel_cnt, y, out_dtype, ws,
                     (size_t)MLA_NOALLOC_SCRATCH_BYTES, stream);
+}
+
+extern "C" int mla_debug_flags(uint32_t* flags, int32_t* checks_built, hipStream_t stream) {
+  if (!flags || !checks_built) return MLA_ERR_NULL;
+  static_assert(kDbgAppendPos == MLA_DBG_APPEND_POS && kDbgAppendPage == MLA_DBG_APPEND_PAGE &&
+                    kDbgTopkOffset == MLA_DBG_TOPK_OFFSET,
+                "debug flag bits");
+  *flags = 0;
+  *checks_built = kDebugChecks ? 1 : 0;
+  uint32_t fa = 0, ft = 0;
+  if (read_debug_flags_append(&fa, stream) != hipSuccess || read_debug_flags_topk(&ft, stream) != hipSuccess)
+    return MLA_ERR_HIP;
+  *flags = fa | ft;
+  return MLA_OK;
 }

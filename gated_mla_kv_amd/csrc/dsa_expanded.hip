@@ -41,6 +41,10 @@ namespace gmla {
 
 // As lds_dma16_sbase with 4 bytes per lane (global_load_lds_dword): lane L's word lands at
 // lds_byte_addr + 4*L.
+#ifdef GMLA_DEBUG_CHECKS
+__device__ uint32_t g_debug_flags_topk;  // kDbgTopkOffset, set by the top-k compactions
+#endif
+
 __device__ __forceinline__ void lds_dma4_sbase(uint32_t voff, const void* sbase, uint32_t lds_byte_addr) {
   asm volatile(
       "s_mov_b32 m0, %0\n\t"
@@ -590,6 +594,9 @@ __device__ __forceinline__ void topk_full_row(const TopkArgs& a, const int b, in
       const uint64_t km = __ballot(keep);
       const int w = wpos + lanes_below(km);
       if (keep && w < a.k) out[w] = base + u * 64 + lane;
+#ifdef GMLA_DEBUG_CHECKS
+      if (keep && w >= k) atomicOr(&g_debug_flags_topk, kDbgTopkOffset);
+#endif
       wpos += (int)__popcll(km);
       eq_seen += (int)__popcll(em);
     }
@@ -952,6 +959,9 @@ __global__ __launch_bounds__(256) void topk_compact_kernel(TopkArgs a) {
   for (int r = 0; r < R; ++r) {
     const int o = w + lanes_below(km[r]);
     if (((km[r] >> lane) & 1) && o < kk) out[o] = base + r * 64 + lane;
+#ifdef GMLA_DEBUG_CHECKS
+    if (((km[r] >> lane) & 1) && o >= kk) atomicOr(&g_debug_flags_topk, kDbgTopkOffset);
+#endif
     w += (int)__popcll(km[r]);
   }
 }
@@ -1231,6 +1241,23 @@ hipError_t launch_index_topk(IndexScoreArgs sa, int max_visible, TopkArgs ta, in
     topk_compact_kernel<<<dim3(S, B), 256, 0, st>>>(ta);
   }
   return hipGetLastError();
+}
+
+hipError_t read_debug_flags_topk(uint32_t* flags, hipStream_t st) {
+  *flags = 0;
+#ifdef GMLA_DEBUG_CHECKS
+  hipError_t e = hipMemcpyFromSymbolAsync(flags, HIP_SYMBOL(g_debug_flags_topk), sizeof(uint32_t), 0,
+                                          hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  const uint32_t zero = 0;
+  if (e == hipSuccess)
+    e = hipMemcpyToSymbolAsync(HIP_SYMBOL(g_debug_flags_topk), &zero, sizeof(uint32_t), 0, hipMemcpyHostToDevice, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  return e;
+#else
+  (void)st;
+  return hipSuccess;
+#endif
 }
 
 hipError_t launch_expanded_attention(Shape s, const ExpandedAttnArgs& a, hipStream_t st) {

@@ -183,4 +183,21 @@ hipError_t launch_expanded_attention(Shape s, const ExpandedAttnArgs& a, hipStre
 hipError_t launch_gate_mul(const float* z, const float* g_pre, int n, void* u, int u_f32,
                            hipStream_t st);
 
+// Debug builds (GMLA_DEBUG_CHECKS): device-side bound checks in kv_append and the top-k
+// compaction. A failed check sets its bit in a device word of the kernel's source file; the
+// offending write is skipped in every build, so the checks change no result. read_debug_flags_*
+// return that word and clear it (0 and no device access in a normal build).
+enum : uint32_t {
+  kDbgAppendPos = 1u,   // kv_append: a token position outside [0, T_cap)
+  kDbgAppendPage = 2u,  // kv_append: a page-table entry outside [0, n_pages)
+  kDbgTopkOffset = 4u,  // top-k compaction: an output offset at or past the kept count
+};
+#ifdef GMLA_DEBUG_CHECKS
+constexpr bool kDebugChecks = true;
+#else
+constexpr bool kDebugChecks = false;
+#endif
+hipError_t read_debug_flags_append(uint32_t* flags, hipStream_t st);
+hipError_t read_debug_flags_topk(uint32_t* flags, hipStream_t st);
+
 }  // namespace gmla

@@ -264,11 +264,26 @@ __device__ __forceinline__ u32x2 fp8_group(const u32x4 v, float& scale) {
 // One workgroup per new token (b, t). Work items are 16-byte chunks:
 //   latent row: L/8 chunks of c then DS/8 of r; per head: DN/8 chunks of k_nope then DS/8 of r
 //   for K, DV/8 chunks for V; the index key: DI/8 chunks.
+#ifdef GMLA_DEBUG_CHECKS
+__device__ uint32_t g_debug_flags_append;
+#endif
+
 __global__ __launch_bounds__(256) void kv_append_kernel(KvAppendArgs a) {
   const int tok = blockIdx.x;
   const int b = tok / a.T, t = tok % a.T;
   const int p = a.pos[b] + t;
-  if (p < 0 || p >= a.T_cap) return;  // outside the cache: nothing is written
+  if (p < 0 || p >= a.T_cap) {  // outside the cache: nothing is written
+#ifdef GMLA_DEBUG_CHECKS
+    if (threadIdx.x == 0) atomicOr(&g_debug_flags_append, kDbgAppendPos);
+#endif
+    return;
+  }
+#ifdef GMLA_DEBUG_CHECKS
+  if (a.pages.table && threadIdx.x == 0) {  // cache_row clamps a bad entry to a valid page
+    const int e = a.pages.table[(size_t)b * a.pages.max_blocks + p / a.pages.page_size];
+    if (e < 0 || e >= a.pages.n_pages) atomicOr(&g_debug_flags_append, kDbgAppendPage);
+  }
+#endif
   const size_t bt = (size_t)b * a.T + t;
   const size_t crow = cache_row(a.pages, a.T_cap, b, p);  // latent / index-key row
   const int cL = a.L / 8, cS = a.DS / 8, cN = a.DN / 8, cV = a.DV / 8, cI = a.DI / 8;
@@ -346,6 +361,23 @@ hipError_t launch_kv_append(const KvAppendArgs& a, hipStream_t s) {
   if (a.B <= 0 || a.T <= 0) return hipSuccess;
   kv_append_kernel<<<a.B * a.T, 256, 0, s>>>(a);
   return hipGetLastError();
+}
+
+hipError_t read_debug_flags_append(uint32_t* flags, hipStream_t st) {
+  *flags = 0;
+#ifdef GMLA_DEBUG_CHECKS
+  hipError_t e = hipMemcpyFromSymbolAsync(flags, HIP_SYMBOL(g_debug_flags_append), sizeof(uint32_t), 0,
+                                          hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  const uint32_t zero = 0;
+  if (e == hipSuccess)
+    e = hipMemcpyToSymbolAsync(HIP_SYMBOL(g_debug_flags_append), &zero, sizeof(uint32_t), 0, hipMemcpyHostToDevice, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  return e;
+#else
+  (void)st;
+  return hipSuccess;
+#endif
 }
 
 }  // namespace gmla

@@ -352,6 +352,22 @@ int mla_value_up_gate(const mla_dims* dims, const float* o_latent, const void* w
 int mla_debug_scores(const mla_dims* dims, const void* q, const void* k, int32_t k_heads, int32_t B,
                      int32_t Tq, int32_t Tk, int32_t D, float* logits, hipStream_t stream);
 
+/* Device-side bound checks (for debugging callers' indices and the library itself; not a
+ * passage of the pages). In the debug build of the library (libgmla_debug.so, compiled with
+ * GMLA_DEBUG_CHECKS), kv_append checks every token position against [0, T_cap) and every
+ * page-table entry it uses against [0, n_pages), and the top-k compactions check every output
+ * offset against the kept count. A failed check sets a bit in *flags:
+ *   MLA_DBG_APPEND_POS, MLA_DBG_APPEND_PAGE, MLA_DBG_TOPK_OFFSET.
+ * Every build skips such writes (a position outside the cache is not written, a bad page entry
+ * is clamped to a valid page), so the checks change no result; the normal build only does not
+ * record them. This call synchronises `stream`, returns the bits set since the last call and
+ * clears them (for the current device). *checks_built = 1 in the debug build, 0 otherwise (then
+ * *flags is always 0). MLA_ERR_NULL if flags or checks_built is NULL; MLA_ERR_HIP on a HIP error. */
+#define MLA_DBG_APPEND_POS 1u
+#define MLA_DBG_APPEND_PAGE 2u
+#define MLA_DBG_TOPK_OFFSET 4u
+int mla_debug_flags(uint32_t* flags, int32_t* checks_built, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

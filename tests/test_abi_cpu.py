@@ -234,3 +234,39 @@ def test_debug_scores_validation():
     assert call(FAKE, FAKE, 96, 1, 4, 4, 192, None) == ERR_NULL
     assert call(FAKE + 2, FAKE, 1, 1, 4, 4, 576, FAKE) == ERR_SHAPE     # q not 16-byte aligned
     assert call(None, None, 96, 0, 4, 4, 192, None) == 0                # empty: nothing launched
+
+
+def test_debug_flags_entry():
+    """mla_debug_flags: NULL outputs are refused; the build under test reports whether it has the
+    device-side checks (the normal build: no, and no bits; it touches no device to say so)."""
+    L = gm.lib()
+    flags, built = ctypes.c_uint32(7), ctypes.c_int32(7)
+    assert L.mla_debug_flags(None, ctypes.byref(built), None) == ERR_NULL
+    assert L.mla_debug_flags(ctypes.byref(flags), None, None) == ERR_NULL
+    if os.path.basename(gm.LIB_PATH) == "libgmla_debug.so":
+        pytest.skip("the debug build reads its flags from the device")
+    assert L.mla_debug_flags(ctypes.byref(flags), ctypes.byref(built), None) == OK
+    assert (flags.value, built.value) == (0, 0)
+
+
+def test_launch_logging():
+    """GMLA_LOG=1: an entry point writes one line naming itself, its sizes and the stream to
+    stderr on entry, before validation (so a refused call is logged too); unset, nothing."""
+    import subprocess
+    import sys
+    code = ("import ctypes, gated_mla_kv_amd as gm; L = gm.lib(); "
+            "print(L.mla_gemm(None, 8, None, -1, 16, 8, None, 16, 0, None)); "
+            "print(L.kv_append(None, None, None, 5, 2, 3, None, None, None, None, None, None))")
+    env = dict(os.environ, PYTHONPATH=ROOT)
+    for on in (True, False):
+        env["GMLA_LOG"] = "1" if on else "0"
+        r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, timeout=120)
+        assert r.returncode == 0, r.stderr
+        assert r.stdout.split() == [str(ERR_SHAPE), str(ERR_NULL)]
+        lines = [ln for ln in r.stderr.splitlines() if ln.startswith("[gmla]")]
+        if on:
+            assert len(lines) == 2, r.stderr
+            assert lines[0].startswith("[gmla] mla_gemm M=-1 N=16 K=8 lda=8 ldo=16 out_dtype=0 stream=")
+            assert lines[1].startswith("[gmla] kv_append B=2 T=3 max_end=5 stream=")
+        else:
+            assert lines == [], r.stderr
