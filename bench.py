@@ -180,7 +180,19 @@ def decode_benches(args, d, lw, log):
     step()
     torch.cuda.synchronize()
     out["mla_decode_step_us"] = round(median(time_events(step, it, flush=flush)) * 1e3, 2)
-    log(f"[bench] whole mla_decode step (absorbed): {out['mla_decode_step_us']:.1f} us")
+    # the step's algorithmic bytes: every weight matrix read once (x-projection W_qa | W_kva | W_g,
+    # q_b, kv_b for the absorb and the value-up, o_proj), the latent cache read once, the new
+    # latent rows written, x read and y written
+    H = d.n_heads
+    w_bytes = 2 * (d.hidden * (d.q_lora + d.kv_lora + d.d_shared + H * d.d_v) + d.q_lora * H * d.d_qk
+                   + d.kv_lora * H * (d.d_nope + d.d_v) + H * d.d_v * d.hidden)
+    step_bytes = w_bytes + kv_bytes + B * d.d_latent * 2 + 2 * B * d.hidden * 2
+    out["mla_decode_step_roofline"] = roof_hbm("mla_decode (all kernels of the step)", step_bytes,
+                                               out["mla_decode_step_us"])
+    out["mla_decode_step_roofline"]["weight_bytes"] = w_bytes
+    log(f"[bench] whole mla_decode step (absorbed): {out['mla_decode_step_us']:.1f} us, "
+        f"{step_bytes / 1e6:.1f} MB ({w_bytes / 1e6:.1f} MB weights), "
+        f"{out['mla_decode_step_roofline']['achieved']:.0f} GB/s")
     # the same step captured once in a HIP graph and replayed (no launch gaps between its kernels)
     gs = torch.cuda.Stream()
     gs.wait_stream(torch.cuda.current_stream())

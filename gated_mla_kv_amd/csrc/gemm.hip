@@ -9,7 +9,7 @@
 //   double-buffered LDS tiles with a 144-byte row stride (conflict-free 16-byte reads over 16
 //   consecutive rows), workgroup ids remapped so that each XCD walks a contiguous, M-grouped
 //   range of tiles (operands reused from that XCD's L2).
-// * gemm_nt_skinny_lds: M <= 32 with K % 256 == 0 (decode at the K3 shape), see below.
+// * gemm_nt_skinny_dma: M <= 32 with K % 256 == 0 (decode at the K3 shape), see below.
 // * gemm_nt_skinny: other M <= 32 (decode). Weight-bandwidth bound: each wave computes
 //   W[32 rows] . X^T for all tokens, streaming weights straight from HBM into MFMA operands
 //   with eight 16-byte loads in flight per lane; four waves split K inside the workgroup and
@@ -512,82 +512,127 @@ __global__ __launch_bounds__(256) void gemm_nt_skinny(GemmArgs g, float* partial
   }
 }
 
-// M <= 32 with K % 256 == 0: the decode projections at the K3 shape. Wave w of a workgroup takes
-// weight rows [128 x + 32 w, +32) over the k range [kr y, kr y + kr) (x, y = workgroup ids). The
-// activations are the MFMA B operand staged through LDS in 256-wide k chunks (double-buffered,
-// one barrier per chunk), so the global loads are weight rows only: with every wave loading its
-// own activation fragments too (the same rows in every workgroup) the weight stream ran at half
-// the rate. The next chunk's weight fragments (16 per lane) are in flight during the current
-// chunk's MFMAs.
-constexpr int kSkChunk = 256, kSkXPitch = kSkChunk + 8;  // LDS row pitch (bf16): no bank-aligned rows
+// M <= 32 with K % 256 == 0: the decode projections at the K3 shape, bound by the weight stream.
+// Wave w of a workgroup computes out[0:32, n0 + 32 w, +32) (n0 = 128 x) over the 128-wide k chunks
+// [nch y / ks, nch (y + 1) / ks) of split y (x, y = workgroup ids), with the weight rows as the
+// MFMA A operand and the activations as B. Each chunk's operand tiles (32 rows x 256 bytes: a
+// wave's weight rows, and the workgroup's activation rows) are copied whole into LDS by
+// wave-wide 1 KB DMA loads, four rows per load, into a three-slot ring: two chunks are in flight
+// while one is multiplied, with one barrier per chunk (the activation tile is shared). A fourth
+// slot, or 256-wide chunks in a two-slot ring (512-byte row segments), measured no faster. Loaded
+// straight into the operand registers, each load took 16 bytes from each of 32 weight rows and
+// the stream ran at ~4.3 TB/s. Row r of a tile holds its 16-byte chunk c at r*256 + ((c ^ (r & 15)) << 4),
+// so the operand reads (one chunk of 16 consecutive rows per 16 lanes) are free of bank conflicts.
+// One workgroup per CU (120 KB of LDS; 144 KB with the split operand).
+constexpr int kSkChunk = 128;  // k values per chunk
+
+// wait until at most n chunks' copies (VPC loads each) of this wave are still in flight
+template <int VPC>
+__device__ __forceinline__ void sk_wait_chunks(int n) {
+  if (n >= 2)
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * VPC) : "memory");
+  else if (n == 1)
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(VPC) : "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
 
 // SPLIT: the split operand (GemmArgs::a_split): each chunk stages the hi and the lo activations
 // and every weight fragment feeds two MFMAs, so the weights are still read once.
 template <bool SPLIT>
-__global__ __launch_bounds__(256) void gemm_nt_skinny_lds(GemmArgs g, float* partial, int kr) {
+__global__ __launch_bounds__(256) void gemm_nt_skinny_dma(GemmArgs g, float* partial, int ks) {
   constexpr int NX = SPLIT ? 2 : 1;
-  __shared__ __attribute__((aligned(16))) uint16_t xs[2][NX][32 * kSkXPitch];
+  constexpr int RB = kSkChunk * 2;         // bytes of a row per chunk
+  constexpr int TB = 32 * RB;              // one 32-row tile, 8 KB
+  constexpr int XL = NX * TB / 1024 / 4;   // activation loads per wave per chunk (2 or 4)
+  constexpr int VPC = TB / 1024 + XL;      // DMA loads per wave per chunk (10 or 12)
+  constexpr int NS = 3;                     // ring slots (four measured no faster)
+  __shared__ __attribute__((aligned(1024))) uint8_t wring[4][NS][TB];
+  __shared__ __attribute__((aligned(1024))) uint8_t xring[NS][NX][TB];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5;
   const int n0 = blockIdx.x * 128 + wave * 32;
-  const int k1 = blockIdx.y * kr;
-  // rows past N re-read the last row (computed, never stored)
-  const uint16_t* wr = wrow_ptr(g, min(n0 + (lane & 31), g.N - 1)) + k1 + half * 8;
-  // activation staging: thread t copies token t / 8, k [32 (t % 8), +32) of each chunk; tokens
-  // past M copy token 0 (their outputs are computed, never stored)
-  const int tt = tid >> 3, part = tid & 7;
-  const uint16_t* xg = g.a + (size_t)(tt < g.M ? tt : 0) * g.lda + k1 + part * 32;
-  const int nch = kr / kSkChunk;
-  u32x4 xr[NX][4], wa[16], wb[16];
-  auto load_x = [&](int ch) __attribute__((always_inline)) {
+  const int nch_all = g.K / kSkChunk;
+  const int c0 = (int)((long long)blockIdx.y * nch_all / ks), c1 = (int)((long long)(blockIdx.y + 1) * nch_all / ks);
+  const int nch = c1 - c0;
+  // load i of a tile fills its rows 4i .. 4i+3: lane L copies row 4i + L/16's source chunk
+  // (L % 16) ^ (row & 15) into position L % 16. Weight rows past N re-read row N - 1 and
+  // activation rows past M row M - 1 (computed, never stored).
+  const int lrow = lane >> 4, lpos = lane & 15;
+  const uint16_t* wsrc[8];
 #pragma unroll
-    for (int h = 0; h < NX; ++h)
+  for (int i = 0; i < 8; ++i) {
+    const int row = 4 * i + lrow;
+    wsrc[i] = wrow_ptr(g, min(n0 + row, g.N - 1)) + (size_t)c0 * kSkChunk + ((lpos ^ (row & 15)) << 3);
+  }
+  const uint16_t* xsrc[XL];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) xr[h][i] = ld16(xg + h * g.K + ch * kSkChunk + i * 8);
-  };
-  auto load_w = [&](int ch, u32x4* v) __attribute__((always_inline)) {
+  for (int q = 0; q < XL; ++q) {
+    const int j = wave * XL + q, row = 4 * (j & 7) + lrow;  // load j: half j / 8, rows 4 (j % 8) ..
+    xsrc[q] = g.a + (size_t)min(row, g.M - 1) * g.lda + (j >> 3) * g.K + (size_t)c0 * kSkChunk +
+              ((lpos ^ (row & 15)) << 3);
+  }
+  auto issue = [&](int ch) __attribute__((always_inline)) {
+    const int sl = ch % NS;
+    const uint32_t wd = lds_addr(wring[wave][sl]);
 #pragma unroll
-    for (int u = 0; u < 16; ++u) v[u] = ld16(wr + ch * kSkChunk + u * 16);
-  };
-  f32x16 acc = f32x16{};
-  auto step = [&](int ch, const u32x4* wcur, u32x4* wnext) __attribute__((always_inline)) {
+    for (int i = 0; i < 8; ++i) lds_dma16(wsrc[i] + ch * kSkChunk, wd + i * 1024);
 #pragma unroll
-    for (int h = 0; h < NX; ++h)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) st16(&xs[ch & 1][h][tt * kSkXPitch + part * 32 + i * 8], xr[h][i]);
-    // the next chunk (the last one again after the last: unused), with no branch, so that the
-    // MFMAs below wait only for this chunk's weights (at a branch the compiler waits for all loads)
-    const int cn = min(ch + 1, nch - 1);
-    load_x(cn);
-    load_w(cn, wnext);
-    __syncthreads();
-#pragma unroll
-    for (int u = 0; u < 16; ++u) {
-#pragma unroll
-      for (int h = 0; h < NX; ++h) {
-        const u32x4 xv = *(const u32x4*)(&xs[ch & 1][h][(lane & 31) * kSkXPitch + u * 16 + half * 8]);
-        acc = mfma32(wcur[u], xv, acc);
-      }
+    for (int q = 0; q < XL; ++q) {
+      const int j = wave * XL + q;
+      lds_dma16(xsrc[q] + ch * kSkChunk, lds_addr(xring[sl][j >> 3]) + (j & 7) * 1024);
     }
   };
-  load_x(0);
-  load_w(0, wa);
-  int ch = 0;
-  for (; ch + 1 < nch; ch += 2) {
-    step(ch, wa, wb);
-    step(ch + 1, wb, wa);
+  const int r = lane & 31;
+  const uint32_t roff = r * RB, rsw = r & 15;
+  f32x16 acc = f32x16{};
+  auto compute = [&](int ch) __attribute__((always_inline)) {
+    const int sl = ch % NS;
+    const uint8_t* wt = wring[wave][sl] + roff;
+    u32x4 wf[8], xf[NX][8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const uint32_t co = ((2 * u + half) ^ rsw) << 4;
+      wf[u] = *(const u32x4*)(wt + co);
+#pragma unroll
+      for (int h = 0; h < NX; ++h) xf[h][u] = *(const u32x4*)(xring[sl][h] + roff + co);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int h = 0; h < NX; ++h) acc = mfma32(wf[u], xf[h][u], acc);
+  };
+  static_assert(NS - 2 <= 2, "sk_wait_chunks covers two chunks");
+  // the source addresses (their segment lookups read the kernel arguments with vector loads) are
+  // complete before the first copy, so that no wait for them lands between copies
+#pragma unroll
+  for (int i = 0; i < 8; ++i) asm volatile("" ::"v"(wsrc[i]));
+#pragma unroll
+  for (int q = 0; q < XL; ++q) asm volatile("" ::"v"(xsrc[q]));
+  if (nch > 0) {
+    for (int c = 0; c < NS - 1 && c < nch; ++c) issue(c);
+    sk_wait_chunks<VPC>(min(NS - 2, nch - 1));  // chunk 0 has landed
+    __syncthreads();
+    for (int ch = 0; ch < nch; ++ch) {
+      // chunk ch + NS - 1 goes to the slot of chunk ch - 1, which every wave finished before the
+      // barrier that ended the previous step
+      if (ch + NS - 1 < nch) issue(ch + NS - 1);
+      compute(ch);
+      sk_wait_chunks<VPC>(min(NS - 2, nch - 2 - ch));  // chunk ch + 1 has landed
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      __syncthreads();
+    }
   }
-  if (ch < nch) step(ch, wa, wb);
   // acc[r] = out(m = lane % 32, n = n0 + 8 (r / 4) + 4 half + r % 4)
   const int m = lane & 31;
   if (m >= g.M) return;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int n = n0 + (r >> 2) * 8 + half * 4 + (r & 3);
+  for (int e = 0; e < 16; ++e) {
+    const int n = n0 + (e >> 2) * 8 + half * 4 + (e & 3);
     if (n >= g.N) continue;
     if (partial)
-      partial[((size_t)blockIdx.y * g.M + m) * g.N + n] = acc[r];
+      partial[((size_t)blockIdx.y * g.M + m) * g.N + n] = acc[e];
     else
-      store_out(out_col(g, n), m, acc[r]);
+      store_out(out_col(g, n), m, acc[e]);
   }
 }
 
@@ -603,14 +648,15 @@ __global__ void gemm_reduce(GemmArgs g, const float* partial, int ksplit) {
 // ----------------------------------------------------------------------------------------
 // Host launchers
 // ----------------------------------------------------------------------------------------
-static bool skinny_lds_ok(int M, int K) { return M <= 32 && K % kSkChunk == 0; }
+static bool skinny_lds_ok(int M, int K) { return M <= 32 && K % 256 == 0; }
 
 static int skinny_ksplit(int M, int N, int K) {
   if (skinny_lds_ok(M, K)) {
-    // about two 128-row workgroups per CU, each k range a whole number of chunks
+    // one 128-row workgroup per CU: the most k splits (at least two chunks each) that keep the
+    // grid within 256 workgroups
     const int groups = cdiv(N, 128), nch = K / kSkChunk;
     int ks = 1;
-    while (groups * ks * 2 <= 512 && nch % (ks * 2) == 0) ks *= 2;
+    while (groups * (ks + 1) <= 256 && 2 * (ks + 1) <= nch) ++ks;
     return ks;
   }
   const int ntiles = cdiv(N, 32);
@@ -649,9 +695,9 @@ hipError_t launch_gemm(const GemmArgs& g, void* ws, size_t ws_bytes, hipStream_t
       partial = (float*)ws;
     }
     if (skinny_lds_ok(g.M, g.K) && g.a_split)
-      gemm_nt_skinny_lds<true><<<dim3(cdiv(g.N, 128), ks), 256, 0, stream>>>(g, partial, g.K / ks);
+      gemm_nt_skinny_dma<true><<<dim3(cdiv(g.N, 128), ks), 256, 0, stream>>>(g, partial, ks);
     else if (skinny_lds_ok(g.M, g.K))
-      gemm_nt_skinny_lds<false><<<dim3(cdiv(g.N, 128), ks), 256, 0, stream>>>(g, partial, g.K / ks);
+      gemm_nt_skinny_dma<false><<<dim3(cdiv(g.N, 128), ks), 256, 0, stream>>>(g, partial, ks);
     else
       gemm_nt_skinny<<<dim3(cdiv(g.N, 32), ks), 256, 0, stream>>>(g, partial, spw);
     if (ks > 1) {
