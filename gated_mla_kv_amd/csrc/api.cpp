@@ -220,10 +220,12 @@ int run_projections(const mla_dims* d, const mla_weights* w, const void* x, int 
   const int H = d->n_heads, dqk = d->d_nope + d->d_shared;
   int rc = run_x_gemm(d, w, x, M, wsp, with_idx, st);
   if (rc) return rc;
-  CHECK_HIP(launch_rmsnorm(wsp.xq, d->q_lora, (const uint16_t*)w->g_q_a, M, d->q_lora, d->rms_eps, wsp.cq,
-                           wsp.ldcq, idx_query ? wsp.cq + d->q_lora : nullptr, st));
-  CHECK_HIP(launch_rmsnorm(wsp.xc, d->kv_lora, (const uint16_t*)w->g_kv_a, M, d->kv_lora, d->rms_eps, wsp.c,
-                           d->kv_lora, nullptr, st));
+  // the two RMSNorms (c^Q, and the latent c) in one launch
+  CHECK_HIP(launch_rmsnorm2(
+      RmsNormJob{wsp.xq, d->q_lora, (const uint16_t*)w->g_q_a, M, d->q_lora, wsp.cq, wsp.ldcq,
+                 idx_query ? wsp.cq + d->q_lora : nullptr},
+      RmsNormJob{wsp.xc, d->kv_lora, (const uint16_t*)w->g_kv_a, M, d->kv_lora, wsp.c, d->kv_lora, nullptr},
+      d->rms_eps, st));
   {
     GemmArgs g = gemm_args(wsp.cq, wsp.ldcq, M, d->q_lora);
     int n = 0;

@@ -10,6 +10,19 @@ namespace gmla {
 enum class Shape { K3, Tiny };
 
 // out_lo (or null): the bf16 residual f - hi of every output, at the same ldo
+// RMSNorm of M rows of N fp32 values (N % 4 == 0): out = bf16(x * rsqrt(mean(x^2) + eps) * gain),
+// and out_lo (if set) the remainder x*... - out in bf16.
+struct RmsNormJob {
+  const float* x;
+  int ldx;
+  const uint16_t* gain;
+  int M, N;
+  uint16_t* out;
+  int ldo;
+  uint16_t* out_lo;
+};
+// both jobs in one launch (b.M = 0: job a only)
+hipError_t launch_rmsnorm2(const RmsNormJob& a, const RmsNormJob& b, float eps, hipStream_t s);
 hipError_t launch_rmsnorm(const float* x, int ldx, const uint16_t* gain, int M, int N, float eps,
                           uint16_t* out, int ldo, uint16_t* out_lo, hipStream_t s);
 hipError_t launch_layernorm(const float* x, int ldx, const uint16_t* gain, const uint16_t* bias,

@@ -19,38 +19,46 @@
 
 namespace gmla {
 
-__global__ __launch_bounds__(256) void rmsnorm_rows(const float* __restrict__ x, int ldx,
-                                                    const uint16_t* __restrict__ gain, int M, int N,
-                                                    float eps, uint16_t* __restrict__ out, int ldo,
-                                                    uint16_t* __restrict__ out_lo) {
-  const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= M) return;
-  const float* xr = x + (size_t)row * ldx;
+// One wave normalises row `row` of job j: out = bf16(x * rsqrt(mean(x^2) + eps) * gain), and with
+// out_lo the bf16 rounding remainder of each value (the split operand's lo half).
+__device__ __forceinline__ void rmsnorm_row(const RmsNormJob& j, int row, int lane, float eps) {
+  const float* xr = j.x + (size_t)row * j.ldx;
   float ss = 0.f;
-  for (int i = lane * 4; i < N; i += 256) {
+  for (int i = lane * 4; i < j.N; i += 256) {
     const float4 v = *(const float4*)(xr + i);
     ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
   }
   ss = wave_sum(ss);
-  const float inv = rsqrtf(ss / (float)N + eps);
-  uint16_t* orow = out + (size_t)row * ldo;
-  for (int i = lane * 4; i < N; i += 256) {
+  const float inv = rsqrtf(ss / (float)j.N + eps);
+  uint16_t* orow = j.out + (size_t)row * j.ldo;
+  for (int i = lane * 4; i < j.N; i += 256) {
     const float4 v = *(const float4*)(xr + i);
-    const uint2 gw = *(const uint2*)(gain + i);
+    const uint2 gw = *(const uint2*)(j.gain + i);
     const float f0 = v.x * inv * lo_bf16(gw.x), f1 = v.y * inv * hi_bf16(gw.x);
     const float f2 = v.z * inv * lo_bf16(gw.y), f3 = v.w * inv * hi_bf16(gw.y);
     uint2 o;
     o.x = pack_bf16x2(f0, f1);
     o.y = pack_bf16x2(f2, f3);
     *(uint2*)(orow + i) = o;
-    if (out_lo) {  // f - hi is exact in fp32; its bf16 rounding leaves at most 2^-17 |f|
+    if (j.out_lo) {  // f - hi is exact in fp32; its bf16 rounding leaves at most 2^-17 |f|
       uint2 r;
       r.x = pack_bf16x2(f0 - lo_bf16(o.x), f1 - hi_bf16(o.x));
       r.y = pack_bf16x2(f2 - lo_bf16(o.y), f3 - hi_bf16(o.y));
-      *(uint2*)(out_lo + (size_t)row * ldo + i) = r;
+      *(uint2*)(j.out_lo + (size_t)row * j.ldo + i) = r;
     }
   }
+}
+
+// Four rows per workgroup: the first cdiv(a.M, 4) workgroups take job a, the rest job b (two
+// normalisations of one step in one launch).
+__global__ __launch_bounds__(256) void rmsnorm_rows(RmsNormJob a, RmsNormJob b, float eps) {
+  const int lane = threadIdx.x & 63;
+  const int na = cdiv(a.M, 4);
+  const bool first = (int)blockIdx.x < na;
+  const RmsNormJob& j = first ? a : b;
+  const int row = ((int)blockIdx.x - (first ? 0 : na)) * 4 + (threadIdx.x >> 6);
+  if (row >= j.M) return;
+  rmsnorm_row(j, row, lane, eps);
 }
 
 __global__ __launch_bounds__(256) void layernorm_rows(const float* __restrict__ x, int ldx,
@@ -345,8 +353,13 @@ __global__ __launch_bounds__(256) void kv_append_kernel(KvAppendArgs a) {
 
 hipError_t launch_rmsnorm(const float* x, int ldx, const uint16_t* gain, int M, int N, float eps,
                           uint16_t* out, int ldo, uint16_t* out_lo, hipStream_t s) {
-  if (M <= 0) return hipSuccess;
-  rmsnorm_rows<<<cdiv(M, 4), 256, 0, s>>>(x, ldx, gain, M, N, eps, out, ldo, out_lo);
+  return launch_rmsnorm2(RmsNormJob{x, ldx, gain, M, N, out, ldo, out_lo}, RmsNormJob{}, eps, s);
+}
+
+hipError_t launch_rmsnorm2(const RmsNormJob& a, const RmsNormJob& b, float eps, hipStream_t s) {
+  const int blocks = cdiv(max(a.M, 0), 4) + cdiv(max(b.M, 0), 4);
+  if (blocks == 0) return hipSuccess;
+  rmsnorm_rows<<<blocks, 256, 0, s>>>(a, b, eps);
   return hipGetLastError();
 }
 
