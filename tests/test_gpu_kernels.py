@@ -24,8 +24,8 @@ def _sync():
 @pytest.mark.parametrize("M,N,K", [(1, 14400, 7168), (7, 300, 1536), (32, 7168, 12288), (33, 200, 256),
                                    (64, 2112, 512), (300, 1000, 64), (513, 2112, 7168), (256, 24576, 32),
                                    (1000, 2120, 1536), (768, 520, 128),
-                                   # decode kernel with activations in LDS: one, three and five 256-wide
-                                   # k chunks (the odd counts end on the loop's single-chunk tail)
+                                   # decode kernel (operand tiles copied into a three-slot LDS ring): two,
+                                   # six and ten 128-wide k chunks (fewer chunks than slots, and ring wraps)
                                    (5, 640, 256), (17, 1000, 768), (32, 2056, 1280)])
 def test_gemm(M, N, K):
     print(f"gemm M={M} N={N} K={K}", flush=True)
