@@ -221,8 +221,8 @@ int mla_index_projections(const mla_dims* dims, const mla_weights* w, const void
  * (hipGetSymbolAddress, with that device current); MLA_ERR_HIP if that fails.
  *   Returns MLA_ERR_WORKSPACE, before touching the device, when the call would need more than
  *   that (mla_workspace_bytes_ex(dims, B, 1, max_len, path, num_splits) > the buffer): e.g.
- *   B = 32 at max_len 8193 needs 47 MiB, B = 4 at 131073 27 MiB, the DSA path at B = 8,
- *   65537 25 MiB. Other errors as mla_decode.
+ *   B = 32 at max_len 8193 needs 44 MiB, B = 4 at 131073 27 MiB, the DSA path at B = 8,
+ *   65537 24 MiB. Other errors as mla_decode.
  *   Every call on one GPU shares the buffer: calls that overlap in time on one GPU (other
  *   streams, other threads) race and must be serialised by the caller. Nothing in the buffer
  *   needs to start at zero; the kernels clear what they count into. */
