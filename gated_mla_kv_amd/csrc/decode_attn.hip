@@ -486,6 +486,71 @@ __global__ __launch_bounds__(256) void absorb_q_k3_kernel(const uint16_t* __rest
   }
 }
 
+// absorb for at most 32 tokens (decode): one wave per (head h, block c of 128 latent features),
+// four times the workgroups of absorb_q_k3_kernel, so that the 12.6 MB of W^K reach all CUs (with
+// one workgroup per head, 96 CUs staged 128 KB each). The wave copies W^K_h[:, 128 c, +128)
+// (128 rows x 256 bytes) into LDS by 32 wave-wide DMA loads (four rows each), 16-byte piece p of
+// row r at r*256 + ((p ^ 2 (r & 7)) << 4): the transposed reads of four rows x 32 bytes per 16
+// lanes then fall on distinct banks, as with the padded rows of the wide kernel.
+__global__ __launch_bounds__(64) void absorb_q_k3_small_kernel(const uint16_t* __restrict__ q, int ldq,
+                                                               const uint16_t* __restrict__ wkvb, int B,
+                                                               uint16_t* __restrict__ qt) {
+  using S = ShapeK3;
+  constexpr int H = S::H, DN = S::DN, DS = S::DS, DV = S::DV, L = S::L, DQK = DN + DS;
+  __shared__ __attribute__((aligned(1024))) uint8_t wk_s[DN * 256];
+  const int h = blockIdx.x, c = blockIdx.y;
+  const int lane = threadIdx.x;
+  const uint16_t* wsrc = wkvb + (size_t)h * (DN + DV) * L + c * 128;
+  {
+    const uint32_t base = lds_addr(wk_s);
+    const int lr = lane >> 4, pos = lane & 15;
+#pragma unroll 8
+    for (int i = 0; i < DN / 4; ++i) {
+      const int row = 4 * i + lr;
+      lds_dma16(wsrc + (size_t)row * L + ((pos ^ (2 * (row & 7))) << 3), base + i * 1024);
+    }
+  }
+  const int G = lane >> 4, jj = lane & 15, g2 = lane >> 5, l32 = lane & 31;
+  const int tok = min(l32, B - 1);  // tokens past B repeat the last (computed, not stored)
+  u32x4 qb[DN / 16];
+  const uint16_t* qrow = q + (size_t)tok * ldq + h * DQK + g2 * 8;
+#pragma unroll
+  for (int ks = 0; ks < DN / 16; ++ks) qb[ks] = ld16(qrow + ks * 16);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // W^K block and q (loaded after it) are in
+  f32x16 acc[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};
+  auto rd = [&](int r, int col) __attribute__((always_inline)) {
+    return lds_read_tr16(wk_s + r * 256 + (((col >> 3) ^ (2 * (r & 7))) << 4) + (col & 7) * 2);
+  };
+#pragma unroll
+  for (int ks = 0; ks < DN / 16; ++ks) {
+    const int r0 = ks * 16 + 8 * (G >> 1) + (jj >> 2);
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      const int col = dt * 32 + 16 * (G & 1) + 4 * (jj & 3);
+      const u32x2 lo = rd(r0, col), hi = rd(r0 + 4, col);
+      acc[dt] = mfma32(u32x4{lo.x, lo.y, hi.x, hi.y}, qb[ks], acc[dt]);
+    }
+  }
+  if (l32 < B) {
+    uint16_t* dst = qt + ((size_t)l32 * H + h) * (L + DS) + c * 128;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int jg = 0; jg < 4; ++jg) {
+        const int n = dt * 32 + jg * 8 + g2 * 4;
+        *(u32x2*)(dst + n) = u32x2{pack_bf16x2(acc[dt][jg * 4], acc[dt][jg * 4 + 1]),
+                                   pack_bf16x2(acc[dt][jg * 4 + 2], acc[dt][jg * 4 + 3])};
+      }
+  }
+  if (c == 0) {  // q_shared passes through to q~[.., L:]: 32 tokens x 8 chunks of 16 bytes
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int idx = i * 64 + lane, t = idx >> 3, ch = idx & 7;
+      if (t < B) st16(qt + ((size_t)t * H + h) * (L + DS) + L + ch * 8, ld16(q + (size_t)t * ldq + h * DQK + DN + ch * 8));
+    }
+  }
+}
+
 // value up-projection and gate: Z^T[d, tok] = W^V_h[d, c] O~^T[c, tok]. W^V_h rows (c contiguous)
 // are the A operand straight from memory; o~ is fp32, split into bf16 hi + lo parts (two MFMAs,
 // products exact to ~2^-17 relative) as the B operand. Workgroup (h, y) takes head h and the
@@ -639,7 +704,9 @@ __global__ __launch_bounds__(256) void vup_gate_k3_lds_kernel(const float* __res
 hipError_t launch_absorb_q(Shape s, const uint16_t* q, int ldq, const uint16_t* wkvb, int B,
                            uint16_t* qt, hipStream_t st) {
   if (B <= 0) return hipSuccess;
-  if (s == Shape::K3)  // up to eight token blocks per workgroup (W^K_h is staged once per workgroup)
+  if (s == Shape::K3 && B <= 32)  // one wave per (head, 128-feature block)
+    absorb_q_k3_small_kernel<<<dim3(ShapeK3::H, 4), 64, 0, st>>>(q, ldq, wkvb, B, qt);
+  else if (s == Shape::K3)  // up to eight token blocks per workgroup (W^K_h is staged once per workgroup)
     absorb_q_k3_kernel<<<dim3(ShapeK3::H, cdiv(B, 256)), 256, 0, st>>>(q, ldq, wkvb, B, qt);
   else
     absorb_q_kernel<ShapeTiny><<<ShapeTiny::H, 256, 0, st>>>(q, ldq, wkvb, B, qt);
