@@ -158,12 +158,14 @@ struct TopkArgs {
   int out_stride;
   int32_t* out_cnt;  // [B]
   int32_t* hist;     // [B, 4096] from the score kernel
+  int32_t* info;     // [B, 4]: boundary bin, keys above it, keys in it
   int32_t* sel;      // [B, 4]: path, threshold key, last kept tie position, chunk count
   int32_t* off;      // [B, off_stride]: output offset of each 2048-position chunk
   int32_t* above;    // [B, off_stride]: per chunk, keys above the boundary bin
   int32_t* ncand;    // [B, off_stride]: per chunk, keys inside the boundary bin
   uint32_t* cand;    // [B, off_stride, 2, 2048]: per chunk, those keys, then their positions
-  int off_stride;
+  int off_stride;    // chunk slots per row
+  int cpw;           // chunks per workgroup of the fused select + compaction
   int row0, rows_per_seq;  // see row_map
 };
 // int32 scratch words of the index-score + top-k launches for B rows of score_stride scores

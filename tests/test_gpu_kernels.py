@@ -390,6 +390,44 @@ def test_topk_many_equal_scores(t, n_pos):
         assert n_zero_kept >= 2048 - n_pos
 
 
+@pytest.mark.parametrize("B,t", [(64, 9000), (128, 20000), (1, 300000)])
+def test_topk_row_counts(B, t):
+    """The chunked top-k in both launch forms: few rows per call spread each row's select over
+    several workgroups that each compact a few chunks (64 rows of 9,000: two chunks per
+    workgroup; one row of 300,000: one chunk each), many long rows take one select workgroup per
+    row and one compaction workgroup per chunk (128 rows of 20,000: ten chunks per row over two
+    workgroups would be five each). Selection exact against the oracle's rule on the GPU's own
+    scores; ragged lengths (every row shorter than the longest by a different amount)."""
+    d = K3.replace(topk=2048)
+    print(f"topk rows B={B} t={t}", flush=True)
+    rng = np.random.default_rng(100 + B)
+    t_vis = [t - (37 * b) % 1500 for b in range(B)]
+    T_cap = t + 3
+    qi = rand_f32((B, d.n_idx_heads, d.d_idx), 101, std=0.1)
+    a = rng.standard_normal((B, d.n_idx_heads)).astype(np.float32)
+    keys = rand_bf16((B, T_cap, d.d_idx), 102)
+    dims_c = gm.make_dims(d)
+    out_idx = torch.empty((B, 2048), dtype=torch.int32, device="cuda")
+    out_cnt = torch.empty((B,), dtype=torch.int32, device="cuda")
+    scores = torch.full((B, T_cap), float("nan"), dtype=torch.float32, device="cuda")
+    ws = torch.empty(gm.workspace_bytes(dims_c, B, 1, T_cap, gm.PATH_SPARSE), dtype=torch.uint8, device="cuda")
+    gm.dsa_index_topk(dims_c, dev_f32(qi), dev_f32(a), dev_bf16(keys), T_cap, i32(t_vis),
+                      max(t_vis), B, out_idx, out_cnt, scores, ws)
+    _sync()
+    sel = out_idx.cpu().numpy()
+    cnt = out_cnt.cpu().numpy()
+    sc_gpu = scores.cpu().numpy()
+    for b in range(B):
+        tb = t_vis[b]
+        assert cnt[b] == 2048
+        np.testing.assert_array_equal(sel[b], O.select_topk(sc_gpu[b, :tb].astype(np.float64), 2048),
+                                      err_msg=f"row {b}")
+    # the scores themselves against the oracle on a few rows
+    for b in (0, B - 1):
+        ref = O.index_scores(qi[b].astype(np.float64), a[b].astype(np.float64), f64(keys[b]), t_vis[b])
+        assert np.max(np.abs(sc_gpu[b, :t_vis[b]] - ref)) < 2e-5
+
+
 # ---------------------------------------------------------------------------------------------
 # Raw logits (stage entry point)
 # ---------------------------------------------------------------------------------------------
