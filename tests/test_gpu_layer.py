@@ -194,14 +194,15 @@ def test_dsa_sparse_prefill_equal_prefix_keys():
         assert np.array_equal(pre, np.arange(len(pre))), f"row {i}: tied prefix keys not taken lowest first"
 
 
-@pytest.mark.parametrize("starts,T", [([100, 37], 150), ([0], 90), ([210], 160)])
+@pytest.mark.parametrize("starts,T", [([100, 37], 150), ([0], 90), ([210], 160), ([5000], 16), ([5000, 4400], 12)])
 def test_dsa_sparse_prefill(starts, T):
     """mla_prefill_sparse against the oracle's dsa_prefill, per sequence (ragged starts, P > 0,
-    rows seeing up to three 128-position key blocks): every row's index scores (the row-blocked
-    scorer for a one-sequence call, the per-row scorer otherwise) against eq. (5) within the
-    score rule, the selections equal to the oracle's except swaps across its k-th score within
-    1e-4 (rows with a swap are compared with the oracle's output for the GPU's set), the output
-    rows within the tolerance, and the appended index keys equal to the oracle's bit for bit."""
+    rows seeing up to three 128-position key blocks, or more than 4096 positions so that the
+    top-k takes its chunked path): every row's index scores (the row-blocked scorer for a
+    one-sequence call, the per-row scorer otherwise) against eq. (5) within the score rule, the
+    selections equal to the oracle's except swaps across its k-th score within 1e-4 (rows with a
+    swap are compared with the oracle's output for the GPU's set), the output rows within the
+    tolerance, and the appended index keys equal to the oracle's bit for bit."""
     d = K3_SMALL_TOPK
     print(f"dsa prefill starts={starts} T={T} k={d.topk}", flush=True)
     lw, L = _layer(d, 94, "k3")
