@@ -54,8 +54,10 @@ def _pair(d, seed, B, T, path):
 
 @pytest.mark.gpu
 def test_noalloc_decode_matches_decode_twice():
-    # first the larger call (DSA path: index scores, top-k with its counters, sparse attention),
-    # then a smaller one (absorbed path, fewer sequences and positions) over the same buffer
+    # largest first (DSA path with rows past 4096 positions: index scores, the chunked top-k with
+    # its histograms, candidate lists and chunk counts, sparse attention), then smaller calls over
+    # the same buffer (DSA with one-workgroup top-k rows, then the absorbed path)
+    _pair(K3, 212, 2, 9000, gm.PATH_SPARSE)
     _pair(K3_SMALL_TOPK, 210, 6, 700, gm.PATH_SPARSE)
     _pair(K3.replace(n_idx_heads=0), 211, 2, 300, gm.PATH_ABSORBED)
 
