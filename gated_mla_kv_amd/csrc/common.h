@@ -146,13 +146,11 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // OCP E4M3 (FP8 caches). Decoding uses the hardware conversion (exact); encoding is written
 // out: round to nearest, ties to even, sign copied, magnitudes from 448 up saturate to 448.
 // ---------------------------------------------------------------------------------------
-// four E4M3 bytes -> four bf16 (exact: every E4M3 value is a bf16 value), as two packed words
+// four E4M3 bytes -> four bf16 (exact: every E4M3 value is a bf16 value), as two packed words,
+// one v_cvt_scalef32_pk_bf16_fp8 per pair (scale 1: the exponent adjustment is zero)
 __device__ __forceinline__ u32x2 e4m3x4_to_bf16(uint32_t w) {
-  typedef float f32x2_ __attribute__((ext_vector_type(2)));
-  const f32x2_ lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
-  const f32x2_ hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
-  return u32x2{(__float_as_uint(lo.x) >> 16) | (__float_as_uint(lo.y) & 0xFFFF0000u),
-               (__float_as_uint(hi.x) >> 16) | (__float_as_uint(hi.y) & 0xFFFF0000u)};
+  return u32x2{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, false)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, true))};
 }
 __device__ __forceinline__ uint32_t e4m3_encode(float x) {
   const uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
