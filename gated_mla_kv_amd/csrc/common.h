@@ -171,7 +171,9 @@ __device__ __forceinline__ uint32_t e4m3_encode(float x) {
   return sign | mag;
 }
 
-__device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + __expf(-x)); }
+// logistic function; the reciprocal is v_rcp_f32 (within 1 ulp) rather than an IEEE division,
+// whose scale/fixup sequence was ten instructions per call in the gate epilogues
+__device__ __forceinline__ float sigmoidf_(float x) { return __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
 
 // ---------------------------------------------------------------------------------------
 // Compile-time layer shapes (the dims a kernel is instantiated for)
