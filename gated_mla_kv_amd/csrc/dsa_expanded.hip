@@ -254,6 +254,8 @@ __global__ __launch_bounds__(kScoreWaves * 64) void index_scores_kernel(IndexSco
 constexpr int kRowsPerWg = 8, kRowBlock = 128;
 
 // at most 128 VGPRs, so that two 8-wave workgroups share a CU (four waves per SIMD)
+// FP8 is a template parameter so that each form's registers fit the 128 without spills.
+template <bool FP8>
 __global__ __launch_bounds__(kRowsPerWg * 64) __attribute__((amdgpu_waves_per_eu(4))) void index_scores_rows_kernel(IndexScoreArgs a) {
   constexpr int NIH = 32, DI = 128, KS = DI / 16;
   __shared__ __attribute__((aligned(16))) uint8_t keys_s[kRowBlock * DI * 2];
@@ -276,11 +278,11 @@ __global__ __launch_bounds__(kRowsPerWg * 64) __attribute__((amdgpu_waves_per_eu
   const int t_last = visible(b_last);  // the block's longest row
   if (p0 >= t_last) return;
   const int t = b < a.B ? visible(b) : 0;
-  const bool fp8 = a.idx_scale != nullptr;
+  constexpr bool fp8 = FP8;
   for (int i = tid; i < kRowsPerWg * kHistBins / 4; i += kRowsPerWg * 64) hist4[i] = 0;
   // the block's keys (positions past t_last repeat its last one; never scored)
   constexpr int NT = kRowsPerWg * 64;
-  if (!fp8) {
+  if constexpr (!fp8) {
     // two passes of two 16-byte loads each (fewer registers live next to the query below)
 #pragma unroll
     for (int h = 0; h < kRowBlock * 16 / NT; h += 2) {
@@ -330,7 +332,7 @@ __global__ __launch_bounds__(kRowsPerWg * 64) __attribute__((amdgpu_waves_per_eu
   for (int j = 0; j < kRowBlock / 32 && p0 + 32 * j < t; ++j) {
     const int r = 32 * j + l32;  // key row of this lane
     f32x16 acc = f32x16{};
-    if (fp8) {
+    if constexpr (fp8) {
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
         const u32x2 w = ld8(keys_s + r * 128 + ((s ^ (r & 7)) << 4) + g2 * 8);
@@ -356,7 +358,7 @@ __global__ __launch_bounds__(kRowsPerWg * 64) __attribute__((amdgpu_waves_per_eu
       for (int e = 0; e < 4; ++e) sc += wv[e] * fmaxf(acc[4 * qq + e], 0.f);
     }
     sc += __shfl_xor(sc, 32, 64);
-    if (fp8) sc *= kscale_s[r];
+    if constexpr (fp8) sc *= kscale_s[r];
     const int pos = p0 + r;
     if (pos < t && g2 == 0) {
       a.scores[(size_t)b * a.score_stride + pos] = sc;
@@ -1334,9 +1336,13 @@ hipError_t launch_index_topk(IndexScoreArgs sa, int max_visible, TopkArgs ta, in
     n_cu = 256;
   // rows of one sequence (a prefill's tokens) share each key block among eight rows
   const bool one_seq = sa.rows_per_seq > 1 && sa.row0 / sa.rows_per_seq == (sa.row0 + B - 1) / sa.rows_per_seq;
-  if (max_visible > 0 && one_seq)
-    index_scores_rows_kernel<<<dim3(cdiv(max_visible, kRowBlock), cdiv(B, kRowsPerWg)), kRowsPerWg * 64, 0, st>>>(sa);
-  else if (max_visible > 0) {
+  if (max_visible > 0 && one_seq) {
+    const dim3 grid(cdiv(max_visible, kRowBlock), cdiv(B, kRowsPerWg));
+    if (sa.idx_scale)
+      index_scores_rows_kernel<true><<<grid, kRowsPerWg * 64, 0, st>>>(sa);
+    else
+      index_scores_rows_kernel<false><<<grid, kRowsPerWg * 64, 0, st>>>(sa);
+  } else if (max_visible > 0) {
     // chunks per row such that the B rows' workgroups fill the CUs a whole number of times
     const int cpr = max(1, n_cu * cdiv(B, n_cu) / B);
     sa.row_tiles = cdiv(max_visible, 32);
