@@ -236,15 +236,16 @@ __global__ __launch_bounds__(k3dec::NTHREADS) void decode_attn_k3_kernel(DecodeA
       }
       f32x16 sacc = sacc2[0] + sacc2[1];
       const int jbase = t * BT;
+      if (jbase + BT > n_pos) {  // the split's last, partial tile: positions past it get -inf
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (jbase + 16 * (r >> 3) + 8 * g2 + (r & 7) >= n_pos) sacc[r] = -INFINITY;
+      }
+      // the raw scores' max, scaled once (sl2 > 0); the exponent arguments below are one FMA each
       float mt = -INFINITY;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int j = jbase + 16 * (r >> 3) + 8 * g2 + (r & 7);
-        const float x = (j < n_pos) ? sacc[r] * sl2 : -INFINITY;
-        sacc[r] = x;
-        mt = fmaxf(mt, x);
-      }
-      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+      for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[r]);
+      mt = fmaxf(mt, __shfl_xor(mt, 32, 64)) * sl2;
       float alpha = 1.f;
       if (mt > m_run + RESCALE_SLACK || m_run == -INFINITY) {
         alpha = fast_exp2(m_run - mt);  // 0 on the first tile
@@ -257,7 +258,7 @@ __global__ __launch_bounds__(k3dec::NTHREADS) void decode_attn_k3_kernel(DecodeA
         float p[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          p[i] = fast_exp2(sacc[hh * 8 + i] - m_run);
+          p[i] = fast_exp2(fmaf(sacc[hh * 8 + i], sl2, -m_run));
           ls += p[i];
         }
         st16(prow + hh * 16, u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
