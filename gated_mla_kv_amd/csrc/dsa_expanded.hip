@@ -244,14 +244,16 @@ __global__ __launch_bounds__(kScoreWaves * 64) void index_scores_kernel(IndexSco
 }
 
 // Prefill rows of one sequence see nested prefixes of one index cache, so a workgroup takes 8
-// consecutive rows (one per wave) and a 128-position block of keys, staged once in LDS for all
-// of them (256-byte rows, 16-byte chunk c at c ^ (row & 15); FP8 codes: 128-byte rows, chunk c
-// at c ^ (row & 7), widened when read, and the block's scales). Each wave scores its row's
-// visible positions of the block as index_scores_kernel does; the top digits go to per-row LDS
-// histograms of 8-bit counters (four bins per word: at most 128 per bin), added to the rows'
-// histograms at the end. 66 KB of LDS: two workgroups per CU, so one's key loads and histogram
-// flush overlap the other's scoring.
+// consecutive rows (one per wave) and, in turn, four consecutive 128-position blocks of keys,
+// each staged once in LDS for all of them (256-byte rows, 16-byte chunk c at c ^ (row & 15); FP8
+// codes: 128-byte rows, chunk c at c ^ (row & 7), widened when read, and the block's scales);
+// the rows' q^I is loaded once for the four blocks. Each wave scores its row's visible positions
+// of a block as index_scores_kernel does; the top digits go to per-row LDS histograms of 8-bit
+// counters (four bins per word: at most 128 per bin), added to the rows' histograms after each
+// block. 66 KB of LDS: two workgroups per CU, so one's key loads and histogram flush overlap the
+// other's scoring.
 constexpr int kRowsPerWg = 8, kRowBlock = 128;
+constexpr int kRowBlocksPerWg = 4;  // key blocks a workgroup takes in turn (its rows' q^I loaded once)
 
 // at most 128 VGPRs, so that two 8-wave workgroups share a CU (four waves per SIMD)
 // FP8 is a template parameter so that each form's registers fit the 128 without spills.
@@ -267,7 +269,6 @@ __global__ __launch_bounds__(kRowsPerWg * 64) __attribute__((amdgpu_waves_per_eu
   __shared__ __attribute__((aligned(16))) float wgt_s[kRowsPerWg][32];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g2 = lane >> 5, l32 = lane & 31;
-  const int p0 = blockIdx.x * kRowBlock;
   auto visible = [&](int row) __attribute__((always_inline)) {
     const RowMap rm = row_map(a.row0, a.rows_per_seq, row);
     return min(min(a.n_vis[rm.seq] + a.vis_offset + rm.extra, a.T_cap), a.score_stride);
@@ -276,45 +277,13 @@ __global__ __launch_bounds__(kRowsPerWg * 64) __attribute__((amdgpu_waves_per_eu
   const int b_last = min((int)blockIdx.y * kRowsPerWg + kRowsPerWg, a.B) - 1;
   const int seq = row_map(a.row0, a.rows_per_seq, b_last).seq;
   const int t_last = visible(b_last);  // the block's longest row
-  if (p0 >= t_last) return;
+  const int base0 = blockIdx.x * kRowBlocksPerWg * kRowBlock;
+  if (base0 >= t_last) return;
   const int t = b < a.B ? visible(b) : 0;
   constexpr bool fp8 = FP8;
-  for (int i = tid; i < kRowsPerWg * kHistBins / 4; i += kRowsPerWg * 64) hist4[i] = 0;
-  // the block's keys (positions past t_last repeat its last one; never scored)
   constexpr int NT = kRowsPerWg * 64;
-  if constexpr (!fp8) {
-    // two passes of two 16-byte loads each (fewer registers live next to the query below)
-#pragma unroll
-    for (int h = 0; h < kRowBlock * 16 / NT; h += 2) {
-      u32x4 v[2];
-#pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        const int i = (h + k) * NT + tid, r = i >> 4, c = i & 15;
-        v[k] = ld16(a.idx_k + cache_row(a.pages, a.T_cap, seq, min(p0 + r, t_last - 1)) * DI + c * 8);
-      }
-#pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        const int i = (h + k) * NT + tid, r = i >> 4, c = i & 15;
-        st16(keys_s + r * 256 + ((c ^ (r & 15)) << 4), v[k]);
-      }
-    }
-  } else {
-    u32x4 v[kRowBlock * 8 / NT];
-#pragma unroll
-    for (int k = 0; k < kRowBlock * 8 / NT; ++k) {
-      const int i = k * NT + tid, r = i >> 3, c = i & 7;
-      v[k] = ld16((const uint8_t*)a.idx_k + cache_row(a.pages, a.T_cap, seq, min(p0 + r, t_last - 1)) * DI + c * 16);
-    }
-#pragma unroll
-    for (int k = 0; k < kRowBlock * 8 / NT; ++k) {
-      const int i = k * NT + tid, r = i >> 3, c = i & 7;
-      st16(keys_s + r * 128 + ((c ^ (r & 7)) << 4), v[k]);
-    }
-    for (int i = tid; i < kRowBlock; i += NT)
-      kscale_s[i] = a.idx_scale[cache_row(a.pages, a.T_cap, seq, min(p0 + i, t_last - 1))];
-  }
   if (b < a.B && lane < 32) wgt_s[wave][lane] = a.w_idx[(size_t)b * NIH + lane] * a.scale;
-  u32x4 qa[KS], ql[KS];  // q^I as bf16 hi + lo pairs, as in index_scores_kernel
+  u32x4 qa[KS], ql[KS];  // q^I as bf16 hi + lo pairs, as in index_scores_kernel (loaded once)
   if (b < a.B) {
     const float* qrow = a.q_idx + ((size_t)b * NIH + l32) * DI;
 #pragma unroll
@@ -328,54 +297,94 @@ __global__ __launch_bounds__(kRowsPerWg * 64) __attribute__((amdgpu_waves_per_eu
       ql[s] = u32x4{l[0], l[1], l[2], l[3]};
     }
   }
-  __syncthreads();  // keys staged, histograms cleared, head weights staged
-  for (int j = 0; j < kRowBlock / 32 && p0 + 32 * j < t; ++j) {
-    const int r = 32 * j + l32;  // key row of this lane
-    f32x16 acc = f32x16{};
-    if constexpr (fp8) {
+#pragma unroll 1
+  for (int blk = 0; blk < kRowBlocksPerWg; ++blk) {
+    const int p0 = base0 + blk * kRowBlock;
+    if (p0 >= t_last) break;
+    for (int i = tid; i < kRowsPerWg * kHistBins / 4; i += NT) hist4[i] = 0;
+    // the block's keys (positions past t_last repeat its last one; never scored)
+    if constexpr (!fp8) {
+      // copied straight into LDS (no registers next to the query): wave-wide 1 KB load i fills
+      // slots 64 i .. 64 i + 63, slot P holding row P / 16's chunk (P % 16) ^ (row & 15)
+      constexpr int LPW = kRowBlock * 256 / 1024 / kRowsPerWg;  // loads per wave
+      // (lane through an opaque move: the per-lane addresses are formed per block, not hoisted
+      // out of the block loop where they would hold registers next to the query)
+      int ln;
+      asm volatile("v_mov_b32 %0, %1" : "=v"(ln) : "v"(lane));
 #pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const u32x2 w = ld8(keys_s + r * 128 + ((s ^ (r & 7)) << 4) + g2 * 8);
-        const u32x2 lo = e4m3x4_to_bf16(w.x), hi = e4m3x4_to_bf16(w.y);
-        const u32x4 kv = u32x4{lo.x, lo.y, hi.x, hi.y};
-        acc = mfma32(qa[s], kv, acc);
-        acc = mfma32(ql[s], kv, acc);
+      for (int k = 0; k < LPW; ++k) {
+        const int i = wave * LPW + k, P = i * 64 + ln, r = P >> 4, c = (P & 15) ^ (r & 15);
+        lds_dma16(a.idx_k + cache_row(a.pages, a.T_cap, seq, min(p0 + r, t_last - 1)) * DI + c * 8,
+                  lds_addr(keys_s) + i * 1024);
       }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's copies have landed
     } else {
+      u32x4 v[kRowBlock * 8 / NT];
 #pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const u32x4 kv = ld16(keys_s + r * 256 + (((2 * s + g2) ^ (r & 15)) << 4));
-        acc = mfma32(qa[s], kv, acc);
-        acc = mfma32(ql[s], kv, acc);
+      for (int k = 0; k < kRowBlock * 8 / NT; ++k) {
+        const int i = k * NT + tid, r = i >> 3, c = i & 7;
+        v[k] = ld16((const uint8_t*)a.idx_k + cache_row(a.pages, a.T_cap, seq, min(p0 + r, t_last - 1)) * DI + c * 16);
+      }
+#pragma unroll
+      for (int k = 0; k < kRowBlock * 8 / NT; ++k) {
+        const int i = k * NT + tid, r = i >> 3, c = i & 7;
+        st16(keys_s + r * 128 + ((c ^ (r & 7)) << 4), v[k]);
+      }
+      for (int i = tid; i < kRowBlock; i += NT)
+        kscale_s[i] = a.idx_scale[cache_row(a.pages, a.T_cap, seq, min(p0 + i, t_last - 1))];
+    }
+    __syncthreads();  // keys staged, histograms cleared (and head weights staged)
+    int l32o;  // l32 through an opaque move, for the same reason as ln above
+    asm volatile("v_mov_b32 %0, %1" : "=v"(l32o) : "v"(l32));
+    for (int j = 0; j < kRowBlock / 32 && p0 + 32 * j < t; ++j) {
+      const int r = 32 * j + l32o;  // key row of this lane
+      f32x16 acc = f32x16{};
+      if constexpr (fp8) {
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          const u32x2 w = ld8(keys_s + r * 128 + ((s ^ (r & 7)) << 4) + g2 * 8);
+          const u32x2 lo = e4m3x4_to_bf16(w.x), hi = e4m3x4_to_bf16(w.y);
+          const u32x4 kv = u32x4{lo.x, lo.y, hi.x, hi.y};
+          acc = mfma32(qa[s], kv, acc);
+          acc = mfma32(ql[s], kv, acc);
+        }
+      } else {
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          const u32x4 kv = ld16(keys_s + r * 256 + (((2 * s + g2) ^ (r & 15)) << 4));
+          acc = mfma32(qa[s], kv, acc);
+          acc = mfma32(ql[s], kv, acc);
+        }
+      }
+      // acc[4 qq + e] holds head 8 qq + 4 g2 + e
+      float sc = 0.f;
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) {
+        const f32x4 wv = *(const f32x4*)&wgt_s[wave][8 * qq + 4 * g2];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sc += wv[e] * fmaxf(acc[4 * qq + e], 0.f);
+      }
+      sc += __shfl_xor(sc, 32, 64);
+      if constexpr (fp8) sc *= kscale_s[r];
+      const int pos = p0 + r;
+      if (pos < t && g2 == 0) {
+        a.scores[(size_t)b * a.score_stride + pos] = sc;
+        const uint32_t bin = order_key(sc) >> 20;
+        atomicAdd(&hist4[wave * (kHistBins / 4) + (bin >> 2)], 1u << (8 * (bin & 3)));
       }
     }
-    // acc[4 qq + e] holds head 8 qq + 4 g2 + e
-    float sc = 0.f;
+    __syncthreads();
+    for (int i = tid; i < kRowsPerWg * kHistBins / 4; i += NT) {
+      const uint32_t w = hist4[i];
+      const int row = blockIdx.y * kRowsPerWg + i / (kHistBins / 4), bin = 4 * (i % (kHistBins / 4));
+      if (w && row < a.B) {
+        int* gh = a.hist + (size_t)row * kHistBins + bin;
 #pragma unroll
-    for (int qq = 0; qq < 4; ++qq) {
-      const f32x4 wv = *(const f32x4*)&wgt_s[wave][8 * qq + 4 * g2];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) sc += wv[e] * fmaxf(acc[4 * qq + e], 0.f);
+        for (int e = 0; e < 4; ++e)
+          if ((w >> (8 * e)) & 0xFFu) atomicAdd(gh + e, (int)((w >> (8 * e)) & 0xFFu));
+      }
     }
-    sc += __shfl_xor(sc, 32, 64);
-    if constexpr (fp8) sc *= kscale_s[r];
-    const int pos = p0 + r;
-    if (pos < t && g2 == 0) {
-      a.scores[(size_t)b * a.score_stride + pos] = sc;
-      const uint32_t bin = order_key(sc) >> 20;
-      atomicAdd(&hist4[wave * (kHistBins / 4) + (bin >> 2)], 1u << (8 * (bin & 3)));
-    }
-  }
-  __syncthreads();
-  for (int i = tid; i < kRowsPerWg * kHistBins / 4; i += NT) {
-    const uint32_t w = hist4[i];
-    const int row = blockIdx.y * kRowsPerWg + i / (kHistBins / 4), bin = 4 * (i % (kHistBins / 4));
-    if (w && row < a.B) {
-      int* gh = a.hist + (size_t)row * kHistBins + bin;
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if ((w >> (8 * e)) & 0xFFu) atomicAdd(gh + e, (int)((w >> (8 * e)) & 0xFFu));
-    }
+    __syncthreads();  // the histograms and keys are reused by the next block
   }
 }
 
@@ -1337,7 +1346,7 @@ hipError_t launch_index_topk(IndexScoreArgs sa, int max_visible, TopkArgs ta, in
   // rows of one sequence (a prefill's tokens) share each key block among eight rows
   const bool one_seq = sa.rows_per_seq > 1 && sa.row0 / sa.rows_per_seq == (sa.row0 + B - 1) / sa.rows_per_seq;
   if (max_visible > 0 && one_seq) {
-    const dim3 grid(cdiv(max_visible, kRowBlock), cdiv(B, kRowsPerWg));
+    const dim3 grid(cdiv(max_visible, kRowBlock * kRowBlocksPerWg), cdiv(B, kRowsPerWg));
     if (sa.idx_scale)
       index_scores_rows_kernel<true><<<grid, kRowsPerWg * 64, 0, st>>>(sa);
     else
