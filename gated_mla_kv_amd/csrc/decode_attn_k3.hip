@@ -110,8 +110,10 @@ __global__ __launch_bounds__(k3dec::NTHREADS) void decode_attn_k3_kernel(DecodeA
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g2 = lane >> 5, l32 = lane & 31;
   // consecutive workgroups take different sequences, so that (with B a multiple of 8) all splits of
-  // a sequence run on one XCD and share its L2 for q~ and, in the merge, for the partials
-  const int b = blockIdx.x % a.B, split = blockIdx.x / a.B;
+  // a sequence run on one XCD and share its L2 for q~ and, in the merge, for the partials. Rows go
+  // out last first: in causal prefill the later rows of a chunk select the most positions, and
+  // dispatching them first keeps them out of the launch's tail.
+  const int b = a.B - 1 - (int)(blockIdx.x % a.B), split = blockIdx.x / a.B;
   const int n_vis = GATHER ? min(a.sel_cnt[b], a.sel_stride) : min(a.n_vis[b] + a.vis_offset, a.T_cap);
   const int p0 = split * a.chunk;
   const int p1 = min(p0 + a.chunk, n_vis);
