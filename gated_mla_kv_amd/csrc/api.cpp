@@ -848,8 +848,8 @@ static SparseWs carve_sparse(const mla_dims* d, int R, int max_end, char* base) 
 // Rows per chunk: the largest of 2048, 1024, 512, 256 whose per-chunk buffers fit in 1 GiB (256
 // at least), and never more than the call's rows.
 static int sparse_rows(const mla_dims* d, int M, int max_end) {
-  int R = 2048;
-  while (R > 256 && carve_sparse(d, R, max_end, nullptr).total > (size_t(1) << 30)) R /= 2;
+  int R = 4096;
+  while (R > 256 && carve_sparse(d, R, max_end, nullptr).total > (size_t(1) << 31)) R /= 2;
   return M < R ? M : R;
 }
 
