@@ -433,6 +433,9 @@ __global__ __launch_bounds__(256) void absorb_q_k3_kernel(const uint16_t* __rest
   using S = ShapeK3;
   constexpr int H = S::H, DN = S::DN, DS = S::DS, DV = S::DV, L = S::L, DQK = DN + DS;
   __shared__ __attribute__((aligned(16))) uint16_t wk_s[DN * kAbsPitch];
+  // per wave, 32 tokens x 64 latent features of output (half the wave's 128), 16-byte chunk c of
+  // token t at chunk position c ^ (t & 7), so that the stores are whole 128-byte runs per token
+  __shared__ __attribute__((aligned(16))) uint16_t st_s[4][32 * 64];
   const int h = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // token blocks of 32: this workgroup takes blocks blockIdx.y, + gridDim.y, ...
@@ -468,16 +471,28 @@ __global__ __launch_bounds__(256) void absorb_q_k3_kernel(const uint16_t* __rest
         acc[dt] = mfma32(u32x4{lo.x, lo.y, hi.x, hi.y}, qb[ks], acc[dt]);
       }
     }
-    if (t0 + l32 < B) {
-      uint16_t* dst = qt + ((size_t)(t0 + l32) * H + h) * (L + DS);
+    // acc[dt][4 jg + e] is latent feature wave*128 + dt*32 + jg*8 + g2*4 + e of token t0 + l32;
+    // each half (dt = 2 hf, 2 hf + 1) goes through the wave's LDS block, then out as 16-byte
+    // chunks, eight tokens' 128-byte runs per store
+    uint16_t* stg = st_s[wave];
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
+    for (int hf = 0; hf < 2; ++hf) {
+#pragma unroll
+      for (int d2 = 0; d2 < 2; ++d2)
 #pragma unroll
         for (int jg = 0; jg < 4; ++jg) {
-          const int n = wave * 128 + dt * 32 + jg * 8 + g2 * 4;
-          *(u32x2*)(dst + n) = u32x2{pack_bf16x2(acc[dt][jg * 4], acc[dt][jg * 4 + 1]),
-                                     pack_bf16x2(acc[dt][jg * 4 + 2], acc[dt][jg * 4 + 3])};
+          const int dt = 2 * hf + d2, c = d2 * 4 + jg;
+          *(u32x2*)(stg + l32 * 64 + ((c ^ (l32 & 7)) << 3) + g2 * 4) =
+              u32x2{pack_bf16x2(acc[dt][jg * 4], acc[dt][jg * 4 + 1]),
+                    pack_bf16x2(acc[dt][jg * 4 + 2], acc[dt][jg * 4 + 3])};
         }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // LDS ops of a wave complete in order
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tk = i * 8 + (lane >> 3), c = lane & 7;
+        const u32x4 v = *(const u32x4*)(stg + tk * 64 + ((c ^ (tk & 7)) << 3));
+        if (t0 + tk < B) st16(qt + ((size_t)(t0 + tk) * H + h) * (L + DS) + wave * 128 + hf * 64 + c * 8, v);
+      }
     }
     if (t0 + ctok < B) st16(qt + ((size_t)(t0 + ctok) * H + h) * (L + DS) + L + cch * 8, sh);
 #pragma unroll
