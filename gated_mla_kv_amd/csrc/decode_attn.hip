@@ -649,19 +649,33 @@ __global__ __launch_bounds__(256) void vup_gate_k3_lds_kernel(const float* __res
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g2 = lane >> 5, l32 = lane & 31;
   stage_rows_512(wv_s, kVupPitch, wkvb + ((size_t)h * (DN + DV) + DN) * L, DV, wave, lane);
-  // wave w takes the 32-token blocks 4 blockIdx.y + w, + 4 gridDim.y, ... (W^V_h staged once)
-  for (int t0 = (blockIdx.y * 4 + wave) * 32; t0 < B; t0 += gridDim.y * 128) {
-    const int tok = min(t0 + l32, B - 1);
-    const float* orow = o + ((size_t)tok * H + h) * L + g2 * 8;
-    const uint16_t* arow = wv_s + l32 * kVupPitch + g2 * 8;
-    f32x16 acc[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};
-    constexpr int U = 8;  // k-steps of o~ loaded together
-    f32x4 ov[U][2];
+  // wave w takes the 32-token blocks 4 blockIdx.y + w, + 4 gridDim.y, ... (W^V_h staged once). The
+  // loads run one k-slice ahead, across blocks too: the last slice of a block issues the block's
+  // gate pre-activations and the next block's first slice of o~, so neither waits a full memory
+  // latency at a block boundary.
+  const int tstep = gridDim.y * 128;
+  const uint16_t* arow = wv_s + l32 * kVupPitch + g2 * 8;
+  auto orow_of = [&](int t0) __attribute__((always_inline)) {  // this lane's o~ row (tokens past B: the last)
+    return o + ((size_t)min(t0 + l32, B - 1) * H + h) * L + g2 * 8;
+  };
+  constexpr int U = 8;  // k-steps of o~ loaded together
+  f32x4 ov[U][2];
+  int t0 = (blockIdx.y * 4 + wave) * 32;
+  if (t0 < B) {
+    const float* orow = orow_of(t0);
 #pragma unroll
     for (int i = 0; i < U; ++i) {
       ov[i][0] = *(const f32x4*)(orow + i * 16);
       ov[i][1] = *(const f32x4*)(orow + i * 16 + 4);
     }
+  }
+  for (; t0 < B; t0 += tstep) {
+    const float* orow = orow_of(t0);
+    const int tn = t0 + tstep;
+    const float* nrow = orow_of(min(tn, B - 1));
+    const size_t ubl = (size_t)min(t0 + l32, B - 1) * H * DV + (size_t)h * DV;
+    f32x16 acc[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};
+    f32x4 gv[4][4];
 #pragma unroll 1
     for (int k0 = 0; k0 < L / 16; k0 += U) {
       u32x4 bh[U], bl[U];
@@ -684,6 +698,20 @@ __global__ __launch_bounds__(256) void vup_gate_k3_lds_kernel(const float* __res
           ov[i][0] = *(const f32x4*)(orow + (k0 + U + i) * 16);
           ov[i][1] = *(const f32x4*)(orow + (k0 + U + i) * 16 + 4);
         }
+      } else {  // last slice: this block's gates, then the next block's first slice
+        if (g_pre) {
+#pragma unroll
+          for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+            for (int jg = 0; jg < 4; ++jg) gv[dt][jg] = *(const f32x4*)(g_pre + ubl + dt * 32 + jg * 8 + g2 * 4);
+        }
+        if (tn < B) {
+#pragma unroll
+          for (int i = 0; i < U; ++i) {
+            ov[i][0] = *(const f32x4*)(nrow + i * 16);
+            ov[i][1] = *(const f32x4*)(nrow + i * 16 + 4);
+          }
+        }
       }
 #pragma unroll
       for (int i = 0; i < U; ++i)
@@ -703,9 +731,8 @@ __global__ __launch_bounds__(256) void vup_gate_k3_lds_kernel(const float* __res
           const int d = dt * 32 + jg * 8 + g2 * 4;
           float z[4] = {acc[dt][jg * 4], acc[dt][jg * 4 + 1], acc[dt][jg * 4 + 2], acc[dt][jg * 4 + 3]};
           if (g_pre) {
-            const f32x4 gv = *(const f32x4*)(g_pre + ub + d);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) z[e] *= sigmoidf_(gv[e]);
+            for (int e = 0; e < 4; ++e) z[e] *= sigmoidf_(gv[dt][jg][e]);
           }
           if (u_f32)
             *(f32x4*)((float*)u + ub + d) = f32x4{z[0], z[1], z[2], z[3]};
