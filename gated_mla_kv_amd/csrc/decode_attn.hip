@@ -645,6 +645,9 @@ __global__ __launch_bounds__(256) void vup_gate_k3_lds_kernel(const float* __res
   using S = ShapeK3;
   constexpr int H = S::H, DN = S::DN, DV = S::DV, L = S::L;
   __shared__ __attribute__((aligned(16))) uint16_t wv_s[DV * kVupPitch];
+  // bf16 output staging, per wave 32 tokens x 64 value features (16-byte chunk c of token t at
+  // chunk position c ^ (t & 7)), so that the stores are whole 128-byte runs per token
+  __shared__ __attribute__((aligned(16))) uint16_t st_s[4][32 * 64];
   const int h = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g2 = lane >> 5, l32 = lane & 31;
@@ -722,23 +725,49 @@ __global__ __launch_bounds__(256) void vup_gate_k3_lds_kernel(const float* __res
           acc[dt] = mfma32(wa, bl[i], acc[dt]);
         }
     }
-    if (t0 + l32 < B) {
-      const size_t ub = (size_t)(t0 + l32) * H * DV + (size_t)h * DV;
+    // acc[dt][4 jg + e] is value feature dt*32 + jg*8 + g2*4 + e of token t0 + l32
+    auto gated = [&](int dt, int jg, float* z) __attribute__((always_inline)) {
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
+      for (int e = 0; e < 4; ++e) z[e] = acc[dt][jg * 4 + e];
+      if (g_pre) {
 #pragma unroll
-        for (int jg = 0; jg < 4; ++jg) {
-          const int d = dt * 32 + jg * 8 + g2 * 4;
-          float z[4] = {acc[dt][jg * 4], acc[dt][jg * 4 + 1], acc[dt][jg * 4 + 2], acc[dt][jg * 4 + 3]};
-          if (g_pre) {
+        for (int e = 0; e < 4; ++e) z[e] *= sigmoidf_(gv[dt][jg][e]);
+      }
+    };
+    if (u_f32) {
+      if (t0 + l32 < B) {
+        const size_t ub = (size_t)(t0 + l32) * H * DV + (size_t)h * DV;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) z[e] *= sigmoidf_(gv[dt][jg][e]);
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+          for (int jg = 0; jg < 4; ++jg) {
+            float z[4];
+            gated(dt, jg, z);
+            *(f32x4*)((float*)u + ub + dt * 32 + jg * 8 + g2 * 4) = f32x4{z[0], z[1], z[2], z[3]};
           }
-          if (u_f32)
-            *(f32x4*)((float*)u + ub + d) = f32x4{z[0], z[1], z[2], z[3]};
-          else
-            *(u32x2*)((uint16_t*)u + ub + d) = u32x2{pack_bf16x2(z[0], z[1]), pack_bf16x2(z[2], z[3])};
+      }
+    } else {  // bf16: each half (dt = 2 hf, 2 hf + 1) through the wave's LDS block, then 16-byte chunks
+      uint16_t* stg = st_s[wave];
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+#pragma unroll
+        for (int d2 = 0; d2 < 2; ++d2)
+#pragma unroll
+          for (int jg = 0; jg < 4; ++jg) {
+            const int c = d2 * 4 + jg;
+            float z[4];
+            gated(2 * hf + d2, jg, z);
+            *(u32x2*)(stg + l32 * 64 + ((c ^ (l32 & 7)) << 3) + g2 * 4) =
+                u32x2{pack_bf16x2(z[0], z[1]), pack_bf16x2(z[2], z[3])};
+          }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // LDS ops of a wave complete in order
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int tk = i * 8 + (lane >> 3), c = lane & 7;
+          const u32x4 v = *(const u32x4*)(stg + tk * 64 + ((c ^ (tk & 7)) << 3));
+          if (t0 + tk < B) st16((uint16_t*)u + (size_t)(t0 + tk) * H * DV + (size_t)h * DV + hf * 64 + c * 8, v);
         }
+      }
     }
   }
 }

@@ -292,10 +292,14 @@ def test_absorb_query_and_value_up(dims, B):
     u = torch.empty((B, H * d.d_v), dtype=torch.float32, device="cuda")
     gm.mla_value_up_gate(dims_c, torch.tensor(bf16_bits_to_f32(o), device="cuda"), Wd, torch.tensor(g, device="cuda"),
                          B, u, gm.OUT_F32)
+    ub = torch.empty((B, H * d.d_v), dtype=torch.bfloat16, device="cuda")  # the bf16 output's store path
+    gm.mla_value_up_gate(dims_c, torch.tensor(bf16_bits_to_f32(o), device="cuda"), Wd, torch.tensor(g, device="cuda"),
+                         B, ub, gm.OUT_BF16)
     _sync()
     check_rows(to_np(qt), qt_ref, "absorbed query", bf16_out=True)
     u_ref = O.value_up(f64(o), w64, d).reshape(B, H * d.d_v) * O.sigmoid(g.astype(np.float64))
     check_rows(to_np(u), u_ref, "value up + gate")
+    check_rows(to_np(ub), u_ref, "value up + gate (bf16 out)", bf16_out=True)
 
 
 # ---------------------------------------------------------------------------------------------
