@@ -393,6 +393,13 @@ __global__ void zero_words_kernel(int32_t* p, int n) {
   if (i < n) p[i] = 0;
 }
 
+// The same clear in 16-byte stores over a grid-stride loop (p 16-byte aligned, n4 = words / 4):
+// a decode's 8 row histograms take 32 workgroups instead of 128, a prefill chunk's 64 MB at most
+// 1024 workgroups of whole-line stores.
+__global__ void zero_words16_kernel(int4* p, int n4) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += gridDim.x * blockDim.x) p[i] = int4{0, 0, 0, 0};
+}
+
 // ------------------------------------------------------------------------------------------
 // Top-k
 // ------------------------------------------------------------------------------------------
@@ -1338,7 +1345,10 @@ hipError_t launch_index_topk(IndexScoreArgs sa, int max_visible, TopkArgs ta, in
   ta.cand = (uint32_t*)(ta.ncand + (size_t)B * S);
   ta.off_stride = S;
   const int nz = B * kHistBins;
-  zero_words_kernel<<<cdiv(nz, 256), 256, 0, st>>>(scratch, nz);
+  if (((uintptr_t)scratch & 15) == 0 && nz % 4 == 0)
+    zero_words16_kernel<<<min(cdiv(nz / 4, 256), 1024), 256, 0, st>>>((int4*)scratch, nz / 4);
+  else
+    zero_words_kernel<<<cdiv(nz, 256), 256, 0, st>>>(scratch, nz);
   int dev = 0, n_cu = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n_cu < 1)
